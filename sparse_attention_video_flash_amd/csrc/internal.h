@@ -1,0 +1,156 @@
+// internal.h -- shared definitions of the svgear HIP library (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "svgear.h"
+
+#define SVG_HIDDEN __attribute__((visibility("hidden")))
+
+namespace svg {
+
+using bf16 = uint16_t;
+
+// ----------------------------------------------------------------------------- element types
+
+__host__ __device__ __forceinline__ float bf16_to_f32(bf16 b)
+{
+    union { uint32_t u; float f; } v;
+    v.u = (uint32_t)b << 16;
+    return v.f;
+}
+
+// Round to nearest even; inputs are finite.
+__host__ __device__ __forceinline__ bf16 f32_to_bf16(float f)
+{
+    union { uint32_t u; float f; } v;
+    v.f = f;
+    uint32_t u = v.u;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (bf16)(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float to_f32(T x);
+template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ float to_f32<bf16>(bf16 x) { return bf16_to_f32(x); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return f32_to_bf16(x); }
+
+// ----------------------------------------------------------------------------- sizes
+
+constexpr int kTile = 256;          // tokens per counting-sort / run-length tile
+constexpr int kMaxC = 4096;         // largest cluster count
+constexpr int kMaxN = 1 << 20;      // largest token count
+
+// Fixed-point scale 2^S of the exact centroid sums: |x| < 2^8 and N < 2^lgN give
+// |sum| < 2^(8 + lgN + S) <= 2^62.
+inline int fixed_point_shift(int N)
+{
+    int lg = 0;
+    while ((1 << lg) <= N) ++lg;   // N < 2^lg
+    return 62 - 8 - lg;
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Device-detected invalid data (reported under SVGEAR_DEBUG_SYNC).
+enum : int { ERR_INIT_INDEX = 1, ERR_LABEL = 2, ERR_RANGE = 4 };
+
+// Workspace map.  [ intermediates of svgear_forward | stage scratch (union) ].
+struct Layout {
+    // forward intermediates
+    size_t labels_q, qbar, counts_q, offsets_q, perm_q, inv_perm_q, Qp;
+    size_t labels_k, kbar, vbar, counts_k, offsets_k, perm_k, inv_perm_k, Kp, Vp;
+    size_t log_ratio, mask, sel_cost;
+    size_t scratch;  // start of the per-stage scratch
+    // cluster scratch (relative to scratch)
+    size_t cl_err, cl_cent64, cl_sums, cl_cnt, cl_hi, cl_lo, cl_cnorm, cl_stats, cl_flag, cl_nflag,
+        cl_hist;
+    size_t cl_end;
+    // probe scratch (relative to scratch)
+    size_t pr_err, pr_qplanes, pr_sbar, pr_keys, pr_pg;
+    size_t pr_end;
+    // attention scratch (relative to scratch)
+    size_t at_err, at_kvplanes, at_logm, at_tiles;
+    size_t at_end;
+    size_t total;
+};
+
+SVG_HIDDEN Layout make_layout(const svgear_shape& s);
+SVG_HIDDEN size_t elem_bytes(int dtype);
+
+// ----------------------------------------------------------------------------- launchers
+
+struct ClusterArgs {
+    int H, N, d, C, iters, dtype, side, flags, shift;
+    const void* X;
+    const void* V;
+    const int32_t* init;
+    int32_t* labels;
+    float* cent;
+    float* vbar;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* perm;
+    int32_t* inv_perm;
+    void* Xp;
+    void* Vp;
+    char* scratch;      // cluster scratch base
+    const Layout* L;
+};
+SVG_HIDDEN hipError_t launch_cluster(const ClusterArgs& a, hipStream_t st);
+
+struct ProbeArgs {
+    int H, Nk, d, Cq, Ck, dtype, flags;
+    const float* qbar;
+    const int32_t* counts_q;
+    const void* Kp;
+    const void* Vp;
+    const float* kbar;
+    const float* vbar;
+    const int32_t* counts_k;
+    const int32_t* offsets_k;
+    float* log_ratio;
+    float* log_eps2;
+    char* scratch;
+    const Layout* L;
+};
+SVG_HIDDEN hipError_t launch_probe(const ProbeArgs& a, hipStream_t st);
+
+struct RouteArgs {
+    int H, Cq, Ck;
+    int64_t budget;
+    const float* log_ratio;
+    const int32_t* counts_q;
+    const int32_t* counts_k;
+    uint8_t* mask;
+    int64_t* sel_cost;
+};
+SVG_HIDDEN hipError_t launch_route(const RouteArgs& a, hipStream_t st);
+
+struct AttnArgs {
+    int H, Nq, Nk, d, Cq, Ck, dtype;
+    const void* Qp;
+    const int32_t* offsets_q;
+    const int32_t* perm_q;
+    const void* Kp;
+    const void* Vp;
+    const float* kbar;
+    const float* vbar;
+    const int32_t* counts_k;
+    const int32_t* offsets_k;
+    const uint8_t* mask;
+    void* O;
+    char* scratch;
+    const Layout* L;
+};
+SVG_HIDDEN hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
+
+// Reads and clears the device error word of a stage scratch (synchronous).
+SVG_HIDDEN int read_device_error(const int* err, hipStream_t st);
+
+}  // namespace svg

@@ -1,0 +1,178 @@
+// probe.hip -- steps 2 and 3 of the SVG-EAR pipeline (review page, inference-
+// pipeline paragraph; German summary 2B): the value-aware centroid probe and the
+// block error-to-cost ratio, streamed without writing logits to device memory.
+//
+// For query cluster c and key j of key cluster g, with s = tau qbar_c.k_j,
+// sbar = tau qbar_c.kbar_g, D = sbar - s and delta_j = vbar_g - v_j,
+//     e[c,j] = || e^sbar vbar_g - e^s v_j ||^2
+//            = e^{2s} [ expm1(D)^2 ||vbar_g||^2 + 2 expm1(D) vbar_g.delta_j + ||delta_j||^2 ].
+// The bracket is a norm, hence >= 0, and does not cancel when the compensation
+// is accurate (small D, small delta).  The block sum over j is accumulated as a
+// running log-sum-exp in the exponent 2s, so the ratio is produced as ln r
+// without overflow: ln r = ln sum_j e[c,j] - ln m_g.
+#include "internal.h"
+
+namespace svg {
+
+// Per key (reordered order): (vbar_g.delta_j, ||delta_j||^2), and per key
+// cluster ||vbar_g||^2.  One block per key cluster; 16 lanes per key row.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_key_scalars(const T* __restrict__ Vp,
+                                                     const float* __restrict__ vbar,
+                                                     const int32_t* __restrict__ offsets_k, int Nk,
+                                                     int Ck, float2* __restrict__ keys,
+                                                     float* __restrict__ pg)
+{
+    constexpr int EPT = D / 16;  // elements per thread
+    const int g = blockIdx.x, h = blockIdx.y;
+    const int sub = threadIdx.x & 15, row = threadIdx.x >> 4;
+    const float* vb = vbar + ((size_t)h * Ck + g) * D + sub * EPT;
+    float vbr[EPT];
+    float p = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        vbr[e] = vb[e];
+        p = fmaf(vbr[e], vbr[e], p);
+    }
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) p += __shfl_xor(p, o, 16);
+    if (threadIdx.x == 0) pg[(size_t)h * Ck + g] = p;
+    const int j0 = offsets_k[(size_t)h * (Ck + 1) + g], j1 = offsets_k[(size_t)h * (Ck + 1) + g + 1];
+    for (int j = j0 + row; j < j1; j += 16) {
+        const T* v = Vp + ((size_t)h * Nk + j) * D + sub * EPT;
+        float qd = 0.f, r = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            float dl = vbr[e] - to_f32<T>(v[e]);
+            qd = fmaf(vbr[e], dl, qd);
+            r = fmaf(dl, dl, r);
+        }
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) {
+            qd += __shfl_xor(qd, o, 16);
+            r += __shfl_xor(r, o, 16);
+        }
+        if (sub == 0) keys[(size_t)h * Nk + j] = make_float2(qd, r);
+    }
+}
+
+// sbar[c, g] = tau qbar_c . kbar_g, accumulated in fp64 and rounded once to fp32.
+template <int D>
+__global__ __launch_bounds__(256) void k_sbar(const float* __restrict__ qbar,
+                                              const float* __restrict__ kbar, int Cq, int Ck,
+                                              double tau, float* __restrict__ sbar)
+{
+    __shared__ double s_q[D];
+    const int c = blockIdx.x, h = blockIdx.z;
+    for (int t = threadIdx.x; t < D; t += 256) s_q[t] = qbar[((size_t)h * Cq + c) * D + t];
+    __syncthreads();
+    const int g = blockIdx.y * 256 + threadIdx.x;
+    if (g >= Ck) return;
+    const float* kb = kbar + ((size_t)h * Ck + g) * D;
+    double s = 0.0;
+#pragma unroll 8
+    for (int t = 0; t < D; ++t) s = fma(s_q[t], (double)kb[t], s);
+    sbar[((size_t)h * Cq + c) * Ck + g] = (float)(tau * s);
+}
+
+// Generic probe: one block per key cluster g, one thread per query cluster c.
+// The differences kbar_g - k_j of the cluster's keys are staged in LDS 32 at a
+// time, so D = tau qbar.(kbar_g - k_j) is formed directly: it is exactly zero
+// when a key equals its centroid, and small differences keep their accuracy.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_probe_generic(
+    const float* __restrict__ qbar, const int32_t* __restrict__ counts_q, const T* __restrict__ Kp,
+    const float* __restrict__ kbar, const float* __restrict__ sbar, const float2* __restrict__ keys,
+    const float* __restrict__ pg,
+    const int32_t* __restrict__ offsets_k, int Nk, int Cq, int Ck, float tau,
+    float* __restrict__ log_ratio, float* __restrict__ log_eps2)
+{
+    constexpr int KB = 32;
+    __shared__ float s_k[KB][D + 1];
+    __shared__ float2 s_ks[KB];
+    const int g = blockIdx.x, h = blockIdx.y;
+    const int j0 = offsets_k[(size_t)h * (Ck + 1) + g], j1 = offsets_k[(size_t)h * (Ck + 1) + g + 1];
+    const float P = pg[(size_t)h * Ck + g];
+    const float* kb = kbar + ((size_t)h * Ck + g) * D;
+    for (int c0 = 0; c0 < Cq; c0 += 256) {
+        const int c = c0 + threadIdx.x;
+        const bool act = c < Cq;
+        float q[D];
+        float sb = 0.f;
+        if (act) {
+#pragma unroll
+            for (int t = 0; t < D; ++t) q[t] = qbar[((size_t)h * Cq + c) * D + t];
+            sb = sbar[((size_t)h * Cq + c) * Ck + g];
+        }
+        float M = -__builtin_inff(), S = 0.f;
+        for (int jb = j0; jb < j1; jb += KB) {
+            const int kn = min(KB, j1 - jb);
+            __syncthreads();
+            for (int k = threadIdx.x; k < kn * D; k += 256)
+                s_k[k / D][k % D] = kb[k % D] - to_f32<T>(Kp[((size_t)h * Nk + jb) * D + k]);
+            if (threadIdx.x < kn) s_ks[threadIdx.x] = keys[(size_t)h * Nk + jb + threadIdx.x];
+            __syncthreads();
+            if (!act) continue;
+            for (int jj = 0; jj < kn; ++jj) {
+                float dot = 0.f;
+#pragma unroll 16
+                for (int t = 0; t < D; ++t) dot = fmaf(q[t], s_k[jj][t], dot);
+                const float dlt = tau * dot;   // sbar - s
+                const float s = sb - dlt;
+                const float em = expm1f(dlt);
+                const float2 kq = s_ks[jj];
+                const float f = fmaxf(fmaf(em, fmaf(em, P, 2.f * kq.x), kq.y), 0.f);
+                const float x = 2.f * s;
+                if (log_eps2)
+                    log_eps2[((size_t)h * Cq + c) * Nk + jb + jj] =
+                        f > 0.f ? x + logf(f) : -__builtin_inff();
+                if (f > 0.f) {
+                    if (x > M) {
+                        S = S * expf(M - x) + f;
+                        M = x;
+                    } else {
+                        S += f * expf(x - M);
+                    }
+                }
+            }
+        }
+        if (act) {
+            const int nq = counts_q[(size_t)h * Cq + c];
+            const int mg = j1 - j0;
+            float lr = -__builtin_inff();
+            if (nq > 0 && mg > 0 && S > 0.f) lr = M + logf(S) - logf((float)mg);
+            log_ratio[((size_t)h * Cq + c) * Ck + g] = lr;
+        }
+    }
+}
+
+SVG_HIDDEN hipError_t launch_probe_mfma(const ProbeArgs& a, const float* sbar, const float2* keys,
+                                        const float* pg, hipStream_t st);
+SVG_HIDDEN bool probe_mfma_supported(const ProbeArgs& a);
+
+template <typename T, int D>
+static hipError_t run_probe(const ProbeArgs& a, hipStream_t st)
+{
+    const Layout& L = *a.L;
+    float* sbar = (float*)(a.scratch + L.pr_sbar);
+    float2* keys = (float2*)(a.scratch + L.pr_keys);
+    float* pg = (float*)(a.scratch + L.pr_pg);
+    const float tau = 1.0f / sqrtf((float)D);
+    hipLaunchKernelGGL((k_key_scalars<T, D>), dim3(a.Ck, a.H), dim3(256), 0, st, (const T*)a.Vp,
+                       a.vbar, a.offsets_k, a.Nk, a.Ck, keys, pg);
+    hipLaunchKernelGGL((k_sbar<D>), dim3(a.Cq, (a.Ck + 255) / 256, a.H), dim3(256), 0, st, a.qbar,
+                       a.kbar, a.Cq, a.Ck, 1.0 / sqrt((double)D), sbar);
+    if (probe_mfma_supported(a)) return launch_probe_mfma(a, sbar, keys, pg, st);
+    hipLaunchKernelGGL((k_probe_generic<T, D>), dim3(a.Ck, a.H), dim3(256), 0, st, a.qbar,
+                       a.counts_q, (const T*)a.Kp, a.kbar, sbar, keys, pg, a.offsets_k, a.Nk, a.Cq, a.Ck,
+                       tau, a.log_ratio, (a.flags & SVGEAR_DEBUG_EPS) ? a.log_eps2 : nullptr);
+    return hipGetLastError();
+}
+
+SVG_HIDDEN hipError_t launch_probe(const ProbeArgs& a, hipStream_t st)
+{
+    if (a.dtype == SVGEAR_BF16) return a.d == 128 ? run_probe<bf16, 128>(a, st) : run_probe<bf16, 64>(a, st);
+    return a.d == 128 ? run_probe<float, 128>(a, st) : run_probe<float, 64>(a, st);
+}
+
+}  // namespace svg

@@ -1,0 +1,152 @@
+// route.hip -- step 3 of the SVG-EAR pipeline (review page, inference-pipeline
+// paragraph, step 3, and the weaknesses paragraph that names greedy selection as
+// an approximate 0-1 knapsack): per head, take blocks in descending ratio order
+// (equal ratios: lower block index first) while their summed cost
+// counts_q[c] * counts_k[g] stays within the budget; stop at the first block that
+// does not fit.
+//
+// No sort is materialised.  The selected set is "every block before the first
+// block whose inclusive prefix cost exceeds the budget", so it is enough to find
+// that block: a radix select over the 32-bit order key, one byte per pass, with
+// cost-weighted (int64) LDS histograms, then an in-order prefix scan over the
+// blocks that share the final key (the tie group, ordered by block index).  One
+// workgroup per head; the ratio array stays in L2 between passes.
+#include "internal.h"
+
+namespace svg {
+
+// Order-preserving map of a float to uint32 (NaN goes below -inf).
+__device__ __forceinline__ uint32_t order_key(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if (f != f) return 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+constexpr int kRouteThreads = 1024;
+
+__device__ long long block_sum_i64(long long v, long long* s_red)
+{
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) s_red[w] = v;
+    __syncthreads();
+    long long t = 0;
+    for (int k = 0; k < kRouteThreads / 64; ++k) t += s_red[k];
+    return t;
+}
+
+__global__ __launch_bounds__(kRouteThreads) void k_route(const float* __restrict__ log_ratio,
+                                                         const int32_t* __restrict__ counts_q,
+                                                         const int32_t* __restrict__ counts_k,
+                                                         int Cq, int Ck, long long budget,
+                                                         uint8_t* __restrict__ mask,
+                                                         long long* __restrict__ sel_cost)
+{
+    __shared__ long long s_hist[256];
+    __shared__ long long s_red[kRouteThreads / 64];
+    __shared__ long long s_scan[kRouteThreads];
+    __shared__ int s_stop;
+    __shared__ uint32_t s_prefix;
+    __shared__ long long s_base;
+    __shared__ int s_found;
+
+    const int h = blockIdx.x;
+    const int nb = Cq * Ck;
+    const float* lr = log_ratio + (size_t)h * nb;
+    const int32_t* cq = counts_q + (size_t)h * Cq;
+    const int32_t* ck = counts_k + (size_t)h * Ck;
+
+    // Radix select of the key of the first block that does not fit.
+    uint32_t prefix = 0;     // determined high bits of the crossing key
+    long long base = 0;      // cost of all blocks with a larger key
+    bool crosses = true;
+    for (int pass = 0; pass < 4 && crosses; ++pass) {
+        const int shift = 24 - 8 * pass;
+        for (int b = threadIdx.x; b < 256; b += kRouteThreads) s_hist[b] = 0;
+        __syncthreads();
+        for (int b = threadIdx.x; b < nb; b += kRouteThreads) {
+            const uint32_t key = order_key(lr[b]);
+            const bool match = pass == 0 || (key >> (shift + 8)) == prefix;
+            if (match) {
+                const long long w = (long long)cq[b / Ck] * (long long)ck[b % Ck];
+                if (w) atomicAdd((unsigned long long*)&s_hist[(key >> shift) & 255u],
+                                 (unsigned long long)w);
+            }
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            long long acc = base;
+            int found = 0;
+            for (int bk = 255; bk >= 0; --bk) {
+                if (acc + s_hist[bk] > budget) {
+                    s_prefix = (prefix << 8) | (uint32_t)bk;
+                    found = 1;
+                    break;
+                }
+                acc += s_hist[bk];
+            }
+            s_found = found;
+            s_base = acc;
+        }
+        __syncthreads();
+        crosses = s_found != 0;
+        if (crosses) {
+            prefix = s_prefix;
+            base = s_base;
+        }
+        __syncthreads();
+    }
+
+    // Tie group (key == prefix) in block-index order: the first block whose
+    // inclusive prefix cost exceeds the budget stops the walk.
+    int stop = nb;
+    if (crosses) {
+        if (threadIdx.x == 0) s_stop = nb;
+        __syncthreads();
+        long long run = base;
+        for (int b0 = 0; b0 < nb; b0 += kRouteThreads) {
+            const int b = b0 + threadIdx.x;
+            long long w = 0;
+            if (b < nb && order_key(lr[b]) == prefix) w = (long long)cq[b / Ck] * (long long)ck[b % Ck];
+            s_scan[threadIdx.x] = w;
+            __syncthreads();
+            for (int off = 1; off < kRouteThreads; off <<= 1) {
+                long long v = threadIdx.x >= off ? s_scan[threadIdx.x - off] : 0;
+                __syncthreads();
+                s_scan[threadIdx.x] += v;
+                __syncthreads();
+            }
+            if (w > 0 && run + s_scan[threadIdx.x] > budget) atomicMin(&s_stop, b);
+            run += s_scan[kRouteThreads - 1];
+            __syncthreads();
+            if (s_stop < nb) break;
+        }
+        stop = s_stop;
+    }
+
+    long long used = 0;
+    uint8_t* mk = mask + (size_t)h * nb;
+    for (int b = threadIdx.x; b < nb; b += kRouteThreads) {
+        bool sel = true;
+        if (crosses) {
+            const uint32_t key = order_key(lr[b]);
+            sel = key > prefix || (key == prefix && b < stop);
+        }
+        mk[b] = sel ? 1 : 0;
+        if (sel) used += (long long)cq[b / Ck] * (long long)ck[b % Ck];
+    }
+    used = block_sum_i64(used, s_red);
+    if (threadIdx.x == 0) sel_cost[h] = used;
+}
+
+SVG_HIDDEN hipError_t launch_route(const RouteArgs& a, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_route, dim3(a.H), dim3(kRouteThreads), 0, st, a.log_ratio, a.counts_q,
+                       a.counts_k, a.Cq, a.Ck, (long long)a.budget, a.mask,
+                       (long long*)a.sel_cost);
+    return hipGetLastError();
+}
+
+}  // namespace svg

@@ -1,0 +1,89 @@
+"""Shared helpers of the GPU parity tests: device upload of seeded inputs, one
+library forward with every intermediate kept, and oracle references."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from sparse_attention_video_flash_amd import svgear as sv
+from sparse_attention_video_flash_amd.inputs import WORKLOADS, Mixture, Workload, generate_head
+
+# A shape that spans several tiles and leaves ragged tails everywhere:
+# 1380 tokens (not a multiple of 32, 64 or 256), odd cluster counts.
+RAGGED = Workload("ragged", 3, (3, 20, 23), 128, "bf16", 13, 37, 10, (0.3,), 5,
+                  (Mixture((0, 3), 24, (2, 3, 4), 0.25, "normal", 0.08, 2.0, "add"),))
+
+TOL = {"fp32": dict(rel_l2=1e-5, max_abs=1e-4), "bf16": dict(rel_l2=5e-3, max_abs=2e-2)}
+
+
+def torch_gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    sv.load()  # a GPU run must have the library: raises if it is missing
+    return torch
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def upload(w: Workload, heads=None):
+    """Seeded inputs of ``heads`` as device tensors (+ the host float32 copies)."""
+    torch = torch_gpu()
+    heads = list(range(w.H)) if heads is None else list(heads)
+    parts = [generate_head(w, h) for h in heads]
+    q, k, v, iq, ik = (np.stack([p[i] for p in parts]) for i in range(5))
+    et = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(dt)  # noqa: E731
+    return dict(Q=dev(q, et), K=dev(k, et), V=dev(v, et), init_q=dev(iq, torch.int32),
+                init_k=dev(ik, torch.int32), host=(q, k, v, iq, ik), heads=heads)
+
+
+def shape_of(w: Workload, H: int, iters=None):
+    return sv.make_shape(H, w.N, w.N, w.d, w.Cq, w.Ck, w.iters if iters is None else iters,
+                         sv.BF16 if w.dtype == "bf16" else sv.F32)
+
+
+def gpu_forward(w: Workload, rho: float, data=None, heads=None):
+    """One svgear_forward call with every intermediate in its own tensor."""
+    torch = torch_gpu()
+    data = data or upload(w, heads)
+    H = len(data["heads"])
+    shape = shape_of(w, H)
+    ws = sv.alloc_workspace(shape)
+    im = sv.alloc_intermediates(shape)
+    O = torch.empty_like(data["Q"])
+    sv.forward(shape, rho, data["Q"], data["K"], data["V"], data["init_q"], data["init_k"], O, ws, im)
+    torch.cuda.synchronize()
+    out = {k: v.cpu() for k, v in im.items()}
+    out["O"] = O.float().cpu().numpy()
+    return out, data
+
+
+def oracle_head(w: Workload, data, hi: int, rho: float, rows=None, want_eps=False):
+    q, k, v, iq, ik = (a[hi] for a in data["host"])
+    return oracle.forward_head(q, k, v, iq, ik, w.Cq, w.Ck, rho, iters=w.iters, rows=rows, want_eps=want_eps)
+
+
+def rel_l2(a, b) -> float:
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def check_output(got, ref, dtype: str, what=""):
+    t = TOL[dtype]
+    r = rel_l2(got, ref)
+    m = float(np.abs(np.asarray(got, np.float64) - ref).max()) if np.size(ref) else 0.0
+    log("  %s rel_l2=%.3e max_abs=%.3e (tol %.0e / %.0e)" % (what, r, m, t["rel_l2"], t["max_abs"]))
+    assert r <= t["rel_l2"], (what, r)
+    assert m <= t["max_abs"], (what, m)
+
+
+__all__ = ["RAGGED", "WORKLOADS", "torch_gpu", "upload", "shape_of", "gpu_forward", "oracle_head", "rel_l2",
+           "check_output", "log", "TOL"]

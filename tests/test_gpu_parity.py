@@ -1,0 +1,342 @@
+"""GPU parity: every stage of libsvgear against the fp64 oracle on the same
+seeded inputs, stage by stage (oracle results injected as inputs) and end to
+end.  Bars: integer outputs bit-exact; ratios within 1e-3 relative; route mask
+bit-exact given the same ratios; output rel-L2 <= 1e-5 (fp32) or <= 5e-3 with
+max-abs <= 2e-2 (bf16)."""
+import numpy as np
+import pytest
+
+import oracle
+from sparse_attention_video_flash_amd import svgear as sv
+
+from gpu_common import (RAGGED, WORKLOADS, check_output, gpu_forward, log, oracle_head, shape_of,
+                        torch_gpu, upload)
+
+pytestmark = pytest.mark.gpu
+
+CASES = {"tiny": WORKLOADS["tiny"], "ragged": RAGGED, "small": WORKLOADS["small"]}
+
+
+def _dev(a, dt):
+    torch = torch_gpu()
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(dt)
+
+
+def _et(w):
+    torch = torch_gpu()
+    return torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+
+def _oracle_all(w, data, rho, want_eps=False):
+    return [oracle_head(w, data, hi, rho, want_eps=want_eps) for hi in range(len(data["heads"]))]
+
+
+# ----------------------------------------------------------------------------- step 1
+
+@pytest.mark.parametrize("case", ["tiny", "ragged", "small"])
+def test_cluster_with_oracle_labels_is_bit_exact(case):
+    torch = torch_gpu()
+    w = CASES[case]
+    log("cluster labels-given %s" % case)
+    data = upload(w)
+    H = len(data["heads"])
+    shape = shape_of(w, H)
+    ws = sv.alloc_workspace(shape)
+    q, k, v, iq, ik = data["host"]
+    for side, X, Xh, C in ((0, data["Q"], q, w.Cq), (1, data["K"], k, w.Ck)):
+        labels = []
+        for hi in range(H):
+            init = (iq if side == 0 else ik)[hi]
+            labels.append(oracle.kmeans(Xh[hi], C, init, iters=w.iters)[0])
+        labels = np.stack(labels)
+        out = dict(labels=_dev(labels, torch.int32), cent=torch.empty(H, C, w.d, device="cuda"),
+                   counts=torch.empty(H, C, dtype=torch.int32, device="cuda"),
+                   offsets=torch.empty(H, C + 1, dtype=torch.int32, device="cuda"),
+                   perm=torch.empty(H, X.shape[1], dtype=torch.int32, device="cuda"),
+                   inv_perm=torch.empty(H, X.shape[1], dtype=torch.int32, device="cuda"),
+                   Xp=torch.empty_like(X))
+        V = None
+        if side == 1:
+            out["vbar"] = torch.empty(H, C, w.d, device="cuda")
+            out["Vp"] = torch.empty_like(data["V"])
+            V = data["V"]
+        sv.cluster(shape, side, X, None, out, ws, V=V, flags=sv.LABELS_GIVEN | sv.DEBUG_SYNC)
+        for hi in range(H):
+            counts, offsets, perm, inv = oracle.permutation(labels[hi], C)
+            np.testing.assert_array_equal(out["counts"][hi].cpu().numpy(), counts)
+            np.testing.assert_array_equal(out["offsets"][hi].cpu().numpy(), offsets)
+            np.testing.assert_array_equal(out["perm"][hi].cpu().numpy(), perm)
+            np.testing.assert_array_equal(out["inv_perm"][hi].cpu().numpy(), inv)
+            np.testing.assert_array_equal(out["Xp"][hi].float().cpu().numpy(), Xh[hi][perm])
+            means = oracle.group_means(Xh[hi], labels[hi], C)
+            np.testing.assert_array_equal(out["cent"][hi].cpu().numpy(), means.astype(np.float32))
+            if side == 1:
+                vmeans = oracle.group_means(v[hi], labels[hi], C)
+                np.testing.assert_array_equal(out["vbar"][hi].cpu().numpy(), vmeans.astype(np.float32))
+                np.testing.assert_array_equal(out["Vp"][hi].float().cpu().numpy(), v[hi][perm])
+
+
+@pytest.mark.parametrize("case", ["tiny", "ragged", "small"])
+def test_kmeans_labels_and_centroids_match_oracle(case):
+    torch = torch_gpu()
+    w = CASES[case]
+    log("kmeans %s" % case)
+    data = upload(w)
+    H = len(data["heads"])
+    shape = shape_of(w, H)
+    ws = sv.alloc_workspace(shape)
+    q, k, v, iq, ik = data["host"]
+    for side, X, Xh, C, init in ((0, data["Q"], q, w.Cq, iq), (1, data["K"], k, w.Ck, ik)):
+        out = dict(labels=torch.empty(H, X.shape[1], dtype=torch.int32, device="cuda"),
+                   cent=torch.empty(H, C, w.d, device="cuda"),
+                   counts=torch.empty(H, C, dtype=torch.int32, device="cuda"),
+                   offsets=torch.empty(H, C + 1, dtype=torch.int32, device="cuda"),
+                   perm=torch.empty(H, X.shape[1], dtype=torch.int32, device="cuda"),
+                   inv_perm=torch.empty(H, X.shape[1], dtype=torch.int32, device="cuda"),
+                   Xp=torch.empty_like(X))
+        V = None
+        if side == 1:
+            out["vbar"] = torch.empty(H, C, w.d, device="cuda")
+            out["Vp"] = torch.empty_like(data["V"])
+            V = data["V"]
+        sv.cluster(shape, side, X, _dev(init, torch.int32), out, ws, V=V, flags=sv.DEBUG_SYNC)
+        for hi in range(H):
+            lab, cent, counts = oracle.kmeans(Xh[hi], C, init[hi], iters=w.iters)
+            np.testing.assert_array_equal(out["labels"][hi].cpu().numpy(), lab)
+            np.testing.assert_array_equal(out["counts"][hi].cpu().numpy(), counts)
+            np.testing.assert_array_equal(out["cent"][hi].cpu().numpy(), cent.astype(np.float32))
+
+
+# ----------------------------------------------------------------------------- steps 2-3
+
+def _probe_inputs(w, data, refs):
+    """Oracle clustering as device tensors (centroids rounded to fp32 as the ABI takes them)."""
+    torch = torch_gpu()
+    q, k, v, iq, ik = data["host"]
+    H = len(refs)
+    f32 = lambda key: np.stack([r[key] for r in refs]).astype(np.float32)  # noqa: E731
+    Kp = np.stack([k[h][refs[h]["perm_k"]] for h in range(H)])
+    Vp = np.stack([v[h][refs[h]["perm_k"]] for h in range(H)])
+    return dict(qbar=_dev(f32("qbar"), torch.float32), counts_q=_dev(np.stack([r["counts_q"] for r in refs]), torch.int32),
+                Kp=_dev(Kp, _et(w)), Vp=_dev(Vp, _et(w)), kbar=_dev(f32("kbar"), torch.float32),
+                vbar=_dev(f32("vbar"), torch.float32),
+                counts_k=_dev(np.stack([r["counts_k"] for r in refs]), torch.int32),
+                offsets_k=_dev(np.stack([r["offsets_k"] for r in refs]), torch.int32),
+                Kp_h=Kp, Vp_h=Vp)
+
+
+def _ratio_close(lr_gpu, r_ref, floor):
+    """|r_gpu - r_ref| <= 1e-3 * max(r_ref, floor), evaluated in the log domain."""
+    lr_gpu = np.asarray(lr_gpu, np.float64)
+    with np.errstate(divide="ignore"):
+        lref = np.log(r_ref)
+        lf = np.log(np.maximum(r_ref, floor))
+    ok_zero = (r_ref == 0) & (lr_gpu == -np.inf)
+    with np.errstate(over="ignore", invalid="ignore"):
+        dev = np.abs(np.exp(lr_gpu - lf) - np.exp(lref - lf))
+    bad = ~(ok_zero | (dev <= 1e-3))
+    return bad, dev
+
+
+@pytest.mark.parametrize("case", ["tiny", "ragged", "small"])
+def test_probe_ratios_and_eps_match_oracle(case):
+    torch = torch_gpu()
+    w = CASES[case]
+    log("probe %s" % case)
+    data = upload(w)
+    refs = _oracle_all(w, data, w.rhos[0])
+    H = len(refs)
+    shape = shape_of(w, H)
+    ws = sv.alloc_workspace(shape)
+    P = _probe_inputs(w, data, refs)
+    lr = torch.empty(H, w.Cq, w.Ck, device="cuda")
+    le = torch.empty(H, w.Cq, w.N, device="cuda")
+    sv.probe(shape, P["qbar"], P["counts_q"], P["Kp"], P["Vp"], P["kbar"], P["vbar"], P["counts_k"],
+             P["offsets_k"], lr, ws, log_eps2=le, flags=sv.DEBUG_SYNC)
+    tau = 1.0 / np.sqrt(w.d)
+    for h in range(H):
+        r = refs[h]
+        qbar32, kbar32, vbar32 = (r[x].astype(np.float32).astype(np.float64) for x in ("qbar", "kbar", "vbar"))
+        k64 = data["host"][1][h].astype(np.float64)
+        v64 = data["host"][2][h].astype(np.float64)
+        ratio, eps = oracle.probe(qbar32, r["counts_q"], k64, v64, r["labels_k"], kbar32, vbar32,
+                                  r["counts_k"], want_eps=True)
+        # floor: scale of the two terms whose difference is e, averaged over each block
+        lk = r["labels_k"]
+        a2 = np.exp(2 * tau * qbar32 @ kbar32.T)[:, lk] * (vbar32[lk] ** 2).sum(1)[None, :]
+        b2 = np.exp(2 * tau * qbar32 @ k64.T) * (v64 ** 2).sum(1)[None, :]
+        S = np.zeros_like(ratio)
+        for g in range(w.Ck):
+            sel = lk == g
+            if sel.any():
+                S[:, g] = (a2[:, sel] + b2[:, sel]).mean(1)
+        bad, dev = _ratio_close(lr[h].cpu().numpy(), ratio, 1e-4 * S)
+        assert not bad.any(), (h, int(bad.sum()), float(dev[bad].max()))
+        # per-key estimate, reordered key order
+        eps_p = eps[:, r["perm_k"]]
+        Sj = (a2 + b2)[:, r["perm_k"]]
+        badj, devj = _ratio_close(le[h].cpu().numpy(), eps_p, 1e-4 * Sj)
+        assert not badj.any(), (h, int(badj.sum()), float(devj[badj].max()))
+        log("  head %d: max ratio dev %.2e, max eps dev %.2e" % (h, float(np.nanmax(dev)), float(np.nanmax(devj))))
+
+
+def _route_gpu(w, H, lr, cq, ck, rho):
+    torch = torch_gpu()
+    shape = shape_of(w, H)
+    ws = sv.alloc_workspace(shape)
+    mask = torch.empty(H, w.Cq, w.Ck, dtype=torch.uint8, device="cuda")
+    sel = torch.empty(H, dtype=torch.int64, device="cuda")
+    sv.route(shape, rho, lr, cq, ck, mask, sel, ws)
+    torch.cuda.synchronize()
+    return mask.cpu().numpy(), sel.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", ["tiny", "ragged", "small"])
+def test_route_mask_bit_exact_given_ratios(case):
+    torch = torch_gpu()
+    w = CASES[case]
+    log("route %s" % case)
+    rng = np.random.default_rng(7)
+    H = 4
+    cq = rng.integers(0, 2 * w.N // w.Cq, (H, w.Cq)).astype(np.int32)
+    ck = rng.integers(0, 2 * w.N // w.Ck, (H, w.Ck)).astype(np.int32)
+    cq[:, 0] = 0   # an empty query cluster
+    ck[:, 1] = 0   # an empty key cluster
+    variants = {
+        "continuous": rng.standard_normal((H, w.Cq, w.Ck)).astype(np.float32) * 5,
+        "ties": rng.integers(-3, 3, (H, w.Cq, w.Ck)).astype(np.float32),
+        "with_-inf": np.where(rng.random((H, w.Cq, w.Ck)) < 0.2, -np.inf,
+                              rng.standard_normal((H, w.Cq, w.Ck))).astype(np.float32),
+    }
+    Nq, Nk = int(cq[0].sum()), int(ck[0].sum())
+    for name, lr in variants.items():
+        for rho in (0.0, 0.05, w.rhos[0], 0.5, 1.0):
+            # the budget uses the shape's Nq, Nk
+            m, s = _route_gpu(w, H, _dev(lr, torch.float32), _dev(cq, torch.int32), _dev(ck, torch.int32), rho)
+            for h in range(H):
+                ref, used = oracle.route(lr[h].astype(np.float64), cq[h], ck[h], rho, w.N, w.N)
+                np.testing.assert_array_equal(m[h], ref, err_msg="%s rho=%s head %d" % (name, rho, h))
+                assert s[h] == used
+    del Nq, Nk
+
+
+# ----------------------------------------------------------------------------- step 4
+
+@pytest.mark.parametrize("case", ["tiny", "ragged", "small"])
+@pytest.mark.parametrize("rho", [None, 0.0, 1.0])
+def test_attention_matches_oracle_given_routing(case, rho):
+    torch = torch_gpu()
+    w = CASES[case]
+    rho = w.rhos[0] if rho is None else rho
+    log("attention %s rho=%s" % (case, rho))
+    data = upload(w)
+    refs = _oracle_all(w, data, rho)
+    H = len(refs)
+    shape = shape_of(w, H)
+    ws = sv.alloc_workspace(shape)
+    q, k, v = data["host"][:3]
+    P = _probe_inputs(w, data, refs)
+    Qp = np.stack([q[h][refs[h]["perm_q"]] for h in range(H)])
+    O = torch.empty_like(data["Q"])
+    sv.attention(shape, _dev(Qp, _et(w)), _dev(np.stack([r["offsets_q"] for r in refs]), torch.int32),
+                 _dev(np.stack([r["perm_q"] for r in refs]), torch.int32), P["Kp"], P["Vp"], P["kbar"],
+                 P["vbar"], P["counts_k"], P["offsets_k"], _dev(np.stack([r["mask"] for r in refs]), torch.uint8),
+                 O, ws)
+    torch.cuda.synchronize()
+    O = O.float().cpu().numpy()
+    for h in range(H):
+        r = refs[h]
+        ref = oracle.hybrid(q[h], k[h], v[h], r["labels_q"], r["labels_k"], r["kbar"].astype(np.float32),
+                            r["vbar"].astype(np.float32), r["counts_k"], r["mask"])
+        check_output(O[h], ref, w.dtype, "head %d" % h)
+
+
+# ----------------------------------------------------------------------------- end to end
+
+def _near_threshold_ok(mask_gpu, r, lr_gpu):
+    """Mask mismatches are allowed only for blocks within 1e-5 relative of the
+    oracle's selection threshold (the ratio of the first unselected block)."""
+    diff = mask_gpu != r["mask"]
+    if not diff.any():
+        return True, 0
+    ratio = r["ratio"]
+    order = sorted(range(ratio.size), key=lambda b: (-ratio.reshape(-1)[b], b))
+    nsel = int(r["mask"].sum())
+    if nsel >= ratio.size:
+        return False, int(diff.sum())
+    thr = ratio.reshape(-1)[order[nsel]]
+    near = np.abs(ratio - thr) <= 1e-5 * abs(thr)
+    return bool((~diff | near).all()), int(diff.sum())
+
+
+@pytest.mark.parametrize("case,rho", [("tiny", 0.25), ("tiny", 1.0), ("ragged", 0.3), ("small", 0.2)])
+def test_forward_end_to_end(case, rho):
+    w = CASES[case]
+    log("forward %s rho=%s" % (case, rho))
+    out, data = gpu_forward(w, rho)
+    H = len(data["heads"])
+    for h in range(H):
+        r = oracle_head(w, data, h, rho)
+        for key in ("labels_q", "counts_q", "offsets_q", "perm_q", "inv_perm_q", "labels_k", "counts_k",
+                    "offsets_k", "perm_k", "inv_perm_k"):
+            np.testing.assert_array_equal(out[key][h].numpy(), r[key], err_msg="%s head %d" % (key, h))
+        ok, nd = _near_threshold_ok(out["mask"][h].numpy(), r, out["log_ratio"][h].numpy())
+        assert ok, ("mask mismatch away from the threshold", h, nd)
+        if nd == 0:
+            assert int(out["sel_cost"][h]) == int(r["sel_cost"])
+        assert int(out["sel_cost"][h]) <= int(r["budget"])
+        check_output(out["O"][h], r["O"], w.dtype, "head %d O" % h)
+
+
+def _cluster_given(w, shape, X, labels, C, ws, V=None):
+    torch = torch_gpu()
+    H, N = labels.shape
+    out = dict(labels=_dev(labels, torch.int32), cent=torch.empty(H, C, w.d, device="cuda"),
+               counts=torch.empty(H, C, dtype=torch.int32, device="cuda"),
+               offsets=torch.empty(H, C + 1, dtype=torch.int32, device="cuda"),
+               perm=torch.empty(H, N, dtype=torch.int32, device="cuda"),
+               inv_perm=torch.empty(H, N, dtype=torch.int32, device="cuda"), Xp=torch.empty_like(X))
+    if V is not None:
+        out["vbar"] = torch.empty(H, C, w.d, device="cuda")
+        out["Vp"] = torch.empty_like(V)
+    sv.cluster(shape, 1 if V is not None else 0, X, None, out, ws, V=V, flags=sv.LABELS_GIVEN | sv.DEBUG_SYNC)
+    return out
+
+
+@pytest.mark.parametrize("case", ["tiny", "ragged"])
+def test_probe_exact_special_cases(case):
+    """Keys equal to their centroid: the estimate is exactly zero when the values
+    are equal too (singleton clusters), and a^2 ||vbar - v||^2 otherwise."""
+    torch = torch_gpu()
+    w = CASES[case]
+    log("probe special cases %s" % case)
+    rng = np.random.default_rng(3)
+    H, N, G = 2, 640, 40
+    shape = sv.make_shape(H, N, N, w.d, 8, G, 2, sv.BF16 if w.dtype == "bf16" else sv.F32)
+    ws = sv.alloc_workspace(shape)
+    from sparse_attention_video_flash_amd.inputs import round_to_bf16
+    rnd = round_to_bf16 if w.dtype == "bf16" else (lambda a: a.astype(np.float32))
+    lab_k = rng.integers(0, G, (H, N)).astype(np.int32)
+    lab_k[:, :G] = np.arange(G)                           # every cluster non-empty
+    kc = rnd(rng.standard_normal((H, G, w.d)).astype(np.float32))
+    K = np.stack([kc[h][lab_k[h]] for h in range(H)])    # keys identical within clusters
+    V = rnd(rng.standard_normal((H, N, w.d)).astype(np.float32))
+    qbar = rng.standard_normal((H, 8, w.d)).astype(np.float32)
+    cq = np.full((H, 8), N // 8, np.int32)
+    o = _cluster_given(w, shape, _dev(K, _et(w)), lab_k, G, ws, V=_dev(V, _et(w)))
+    lr = torch.empty(H, 8, G, device="cuda")
+    sv.probe(shape, _dev(qbar, torch.float32), _dev(cq, torch.int32), o["Xp"], o["Vp"], o["cent"], o["vbar"],
+             o["counts"], o["offsets"], lr, ws, flags=sv.DEBUG_SYNC)
+    lr = lr.cpu().numpy()
+    for h in range(H):
+        kbar = o["cent"][h].cpu().numpy().astype(np.float64)
+        vbar = o["vbar"][h].cpu().numpy().astype(np.float64)
+        ratio = oracle.probe(qbar[h], cq[h], K[h], V[h], lab_k[h], kbar, vbar, o["counts"][h].cpu().numpy())
+        np.testing.assert_allclose(lr[h], np.log(ratio), rtol=0, atol=1e-4)
+    # now values identical within clusters too: every estimate is exactly zero
+    V2 = np.stack([V[h][:G][lab_k[h]] for h in range(H)])
+    o = _cluster_given(w, shape, _dev(K, _et(w)), lab_k, G, ws, V=_dev(V2, _et(w)))
+    lr2 = torch.empty(H, 8, G, device="cuda")
+    sv.probe(shape, _dev(qbar, torch.float32), _dev(cq, torch.int32), o["Xp"], o["Vp"], o["cent"], o["vbar"],
+             o["counts"], o["offsets"], lr2, ws, flags=sv.DEBUG_SYNC)
+    assert (lr2.cpu().numpy() == -np.inf).all()
