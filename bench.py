@@ -1,0 +1,238 @@
+"""Benchmark: one SVG-EAR routed attention call (cluster -> probe -> route ->
+hybrid attention) per step, on the Wan2.2-shaped workload (40 heads x 75,600
+tokens, d = 128, bf16, Cq = 100, Ck = 500, rho = 0.15) by default.
+
+Prints ONE JSON line: ms per call (the headline), per-stage ms, executed and
+dense-equivalent TFLOP/s, the roofline of the dominant kernel (hybrid
+attention, MFMA-bound) measured live with HIP events on the stream the library
+runs on, and the fp64 oracle timed on this host's cores on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from sparse_attention_video_flash_amd import svgear as sv  # noqa: E402
+from sparse_attention_video_flash_amd.inputs import WORKLOADS, generate_head  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "ms per routed attention call @40h×75.6K tok; executed TFLOP/s vs MFMA peak"
+STAGES = ("cluster_q", "cluster_k", "probe", "route", "attention")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def upload(w, torch, device):
+    """Seeded inputs for every head, drawn on host threads, stored bf16/fp32 on the GPU."""
+    et = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    N, d, H = w.N, w.d, w.H
+    Q = torch.empty(H, N, d, dtype=et, device=device)
+    K = torch.empty_like(Q)
+    V = torch.empty_like(Q)
+    iq = torch.empty(H, w.Cq, dtype=torch.int32, device=device)
+    ik = torch.empty(H, w.Ck, dtype=torch.int32, device=device)
+    workers = min(16, os.cpu_count() or 4)
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        for h, (q, k, v, a, b) in enumerate(ex.map(lambda h: generate_head(w, h), range(H))):
+            Q[h].copy_(torch.from_numpy(q).to(et))
+            K[h].copy_(torch.from_numpy(k).to(et))
+            V[h].copy_(torch.from_numpy(v).to(et))
+            iq[h].copy_(torch.from_numpy(a))
+            ik[h].copy_(torch.from_numpy(b))
+    return Q, K, V, iq, ik
+
+
+def staged_call(shape, rho, Q, K, V, iq, ik, O, im, ws, ev):
+    """The five stages of svgear_forward through the per-stage entry points,
+    with an event after each stage (ev[0] before the first)."""
+    ev[0].record()
+    sv.cluster(shape, 0, Q, iq, dict(labels=im["labels_q"], cent=im["qbar"], counts=im["counts_q"],
+                                     offsets=im["offsets_q"], perm=im["perm_q"], inv_perm=im["inv_perm_q"],
+                                     Xp=im["Qp"]), ws)
+    ev[1].record()
+    sv.cluster(shape, 1, K, ik, dict(labels=im["labels_k"], cent=im["kbar"], vbar=im["vbar"],
+                                     counts=im["counts_k"], offsets=im["offsets_k"], perm=im["perm_k"],
+                                     inv_perm=im["inv_perm_k"], Xp=im["Kp"], Vp=im["Vp"]), ws, V=V)
+    ev[2].record()
+    sv.probe(shape, im["qbar"], im["counts_q"], im["Kp"], im["Vp"], im["kbar"], im["vbar"], im["counts_k"],
+             im["offsets_k"], im["log_ratio"], ws)
+    ev[3].record()
+    sv.route(shape, rho, im["log_ratio"], im["counts_q"], im["counts_k"], im["mask"], im["sel_cost"], ws)
+    ev[4].record()
+    sv.attention(shape, im["Qp"], im["offsets_q"], im["perm_q"], im["Kp"], im["Vp"], im["kbar"], im["vbar"],
+                 im["counts_k"], im["offsets_k"], im["mask"], O, ws)
+    ev[5].record()
+
+
+def work_counts(w, im):
+    """Algorithmic flops of the call (from the routing that was actually taken)."""
+    d, H = w.d, w.H
+    cq = im["counts_q"].cpu().numpy().astype(np.int64)
+    ck = im["counts_k"].cpu().numpy().astype(np.int64)
+    mask = im["mask"].cpu().numpy().astype(bool)
+    sel = im["sel_cost"].cpu().numpy().astype(np.int64)
+    exact_pairs = int(sel.sum())
+    # compensation: one centroid term per (query, skipped non-empty key cluster)
+    comp_pairs = int(sum(((~mask[h]) & (ck[h] > 0)[None, :]).sum(axis=1) @ cq[h] for h in range(H)))
+    f_exact = 4.0 * d * exact_pairs
+    f_comp = 4.0 * d * comp_pairs
+    f_kmeans = w.iters * 2.0 * d * (w.N * w.Cq + w.N * w.Ck) * H
+    f_probe = 2.0 * d * w.Cq * (w.N + w.Ck) * H
+    dense = 4.0 * w.N * w.N * d * H
+    return dict(exact=f_exact, comp=f_comp, kmeans=f_kmeans, probe=f_probe, dense=dense,
+                density=exact_pairs / float(w.N * w.N * H))
+
+
+def cpu_baseline(w, rho, rows_stride=16):
+    """The fp64 oracle on head 0: full k-means (Q and K), probe and route, and the
+    hybrid output on every rows_stride-th query; scaled to a whole call."""
+    import oracle
+    q, k, v, iq, ik = generate_head(w, 0)
+    threads = oracle.num_threads()
+    t0 = time.perf_counter()
+    lq, qbar, cq = oracle.kmeans(q, w.Cq, iq, w.iters)
+    lk, kbar, ck = oracle.kmeans(k, w.Ck, ik, w.iters)
+    oracle.permutation(lq, w.Cq)
+    oracle.permutation(lk, w.Ck)
+    vbar = oracle.group_means(v, lk, w.Ck)
+    ratio = oracle.probe(qbar, cq, k, v, lk, kbar, vbar, ck)
+    mask, _ = oracle.route(ratio, cq, ck, rho, w.N, w.N)
+    t1 = time.perf_counter()
+    rows = np.arange(0, w.N, rows_stride, dtype=np.int32)
+    oracle.hybrid(q, k, v, lq, lk, kbar, vbar, ck, mask, rows)
+    t2 = time.perf_counter()
+    per_head_s = (t1 - t0) + (t2 - t1) * (w.N / float(len(rows)))
+    return dict(value=per_head_s * w.H * 1e3, unit="ms/call", cores=threads, kind="oracle",
+                sample="head 0 of %d: full k-means, probe, route; hybrid output on every %dth query row "
+                       "(%d rows), scaled by rows and heads; %.1f s of CPU work"
+                       % (w.H, rows_stride, len(rows), t2 - t0))
+
+
+def traffic_entry(kernel_file):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "attention_counters.json")
+    src = os.path.join(ROOT, "sparse_attention_video_flash_amd", "csrc", kernel_file)
+    if not (os.path.exists(path) and os.path.exists(src)):
+        return None
+    rec = json.load(open(path))
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if rec.get("source_sha256") != digest:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="wan", choices=sorted(WORKLOADS))
+    ap.add_argument("--rho", type=float, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows-stride", type=int, default=16)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (heads shard across GPUs "
+              "without communication; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    sv.load()
+    dev = torch.device("cuda:0")
+    w = WORKLOADS[args.workload]
+    rho = w.rhos[0] if args.rho is None else args.rho
+    t = time.perf_counter()
+    Q, K, V, iq, ik = upload(w, torch, dev)
+    torch.cuda.synchronize()
+    log("inputs ready in %.1f s" % (time.perf_counter() - t))
+    shape = sv.make_shape(w.H, w.N, w.N, w.d, w.Cq, w.Ck, w.iters, sv.BF16 if w.dtype == "bf16" else sv.F32)
+    ws = sv.alloc_workspace(shape, dev)
+    im = sv.alloc_intermediates(shape, dev)
+    O = torch.empty_like(Q)
+
+    for i in range(args.warmup):
+        sv.forward(shape, rho, Q, K, V, iq, ik, O, ws, im)
+        torch.cuda.synchronize()
+        log("warmup %d done" % i)
+
+    # Timed region: K calls, each stage bracketed by events on the library's stream.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        staged_call(shape, rho, Q, K, V, iq, ik, O, im, ws, evs[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    stage_ms = {st: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
+                for i, st in enumerate(STAGES)}
+    log("timed %d steps: %.3f ms/call; stages %s" % (args.steps, ms_per_step,
+                                                     {k: round(v, 3) for k, v in stage_ms.items()}))
+
+    # One-call forward, for reference (same kernels through svgear_forward).
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    sv.forward(shape, rho, Q, K, V, iq, ik, O, ws, im)
+    e1.record()
+    torch.cuda.synchronize()
+    forward_ms = e0.elapsed_time(e1)
+
+    wk = work_counts(w, im)
+    t_att = stage_ms["attention"] * 1e-3
+    att_flops = wk["exact"] + wk["comp"]
+    achieved = att_flops / t_att / 1e12
+    routing_ms = stage_ms["cluster_q"] + stage_ms["cluster_k"] + stage_ms["probe"] + stage_ms["route"]
+    executed = wk["exact"] + wk["comp"] + wk["kmeans"] + wk["probe"]
+    result = {
+        "metric": METRIC,
+        "value": round(ms_per_step, 4),
+        "unit": "ms/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded Gaussian-mixture Q/K/V on the latent grid)",
+        "config": {"workload": "%s: %d heads x %d tokens (%dx%dx%d), d=%d, Cq=%d, Ck=%d, %d k-means iters, rho=%g"
+                   % (w.name, w.H, w.N, *w.grid, w.d, w.Cq, w.Ck, w.iters, rho),
+                   "heads": w.H, "tokens": w.N, "d": w.d, "Cq": w.Cq, "Ck": w.Ck, "rho": rho,
+                   "parallelism": "single GPU"},
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "forward_ms": round(forward_ms, 4),
+        "routing_share": round(routing_ms / sum(stage_ms.values()), 4),
+        "realised_density": round(wk["density"], 5),
+        "executed_tflops": round(executed / (ms_per_step * 1e-3) / 1e12, 2),
+        "dense_equiv_tflops": round(wk["dense"] / (ms_per_step * 1e-3) / 1e12, 2),
+        "roofline": {"kernel": "hybrid attention (svgear_attention)", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_entry("attn_mfma.hip")},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on a bounded sample ...")
+        result["cpu_baseline"] = cpu_baseline(w, rho, args.cpu_rows_stride)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -75,6 +75,8 @@ SVG_HIDDEN Layout make_layout(const svgear_shape& s)
     L.at_kvplanes = take(4 * H * Ck * d * 2);
     L.at_logm = take(H * Ck * 4);
     L.at_tiles = take(H * (Cq + 1) * 4 + 256);
+    L.at_segs = take(H * Cq * Ck * 8);
+    L.at_nsegs = take(H * Cq * 4);
     L.at_end = off;
 
     size_t sc = L.cl_end;

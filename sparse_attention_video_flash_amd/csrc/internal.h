@@ -75,7 +75,7 @@ struct Layout {
     size_t pr_err, pr_qplanes, pr_sbar, pr_keys, pr_pg;
     size_t pr_end;
     // attention scratch (relative to scratch)
-    size_t at_err, at_kvplanes, at_logm, at_tiles;
+    size_t at_err, at_kvplanes, at_logm, at_tiles, at_segs, at_nsegs;
     size_t at_end;
     size_t total;
 };

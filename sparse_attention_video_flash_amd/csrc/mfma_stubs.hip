@@ -5,6 +5,4 @@ SVG_HIDDEN bool assign_mfma_supported(const ClusterArgs&) { return false; }
 SVG_HIDDEN hipError_t launch_assign_mfma(const ClusterArgs&, const double*, int*, hipStream_t) { return hipErrorInvalidValue; }
 SVG_HIDDEN bool probe_mfma_supported(const ProbeArgs&) { return false; }
 SVG_HIDDEN hipError_t launch_probe_mfma(const ProbeArgs&, const float*, const float2*, const float*, hipStream_t) { return hipErrorInvalidValue; }
-SVG_HIDDEN bool attention_mfma_supported(const AttnArgs&) { return false; }
-SVG_HIDDEN hipError_t launch_attention_mfma(const AttnArgs&, hipStream_t) { return hipErrorInvalidValue; }
 }
