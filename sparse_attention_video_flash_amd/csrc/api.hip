@@ -56,6 +56,7 @@ SVG_HIDDEN Layout make_layout(const svgear_shape& s)
     L.cl_hi = take(H * C * d * 2);
     L.cl_lo = take(H * C * d * 2);
     L.cl_cnorm = take(H * C * 4);
+    L.cl_cn64 = take(H * C * 8);
     L.cl_stats = take(H * 16);
     L.cl_flag = take(H * N * 4);
     L.cl_nflag = take(H * 4);

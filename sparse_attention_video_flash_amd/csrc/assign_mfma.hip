@@ -1,0 +1,352 @@
+// assign_mfma.hip -- k-means assignment on bf16 MFMA for d = 128 (step 1 of the
+// SVG-EAR pipeline: Flash k-means; review page inference-pipeline paragraph).
+//
+// The nearest centroid minimises d_m = ||c_m||^2 - 2 x.c_m (||x||^2 is common to
+// all m).  Tokens x are bf16 (exact as MFMA operands); each fp64 centroid is
+// split into bf16 hi + lo planes, so the screen evaluates
+//     d~_m = fl(cn_m - 2 * acc_m),   acc_m = sum_t x_t hi_mt + x_t lo_mt  (fp32 MFMA)
+// with |d~_m - d_m| <= E(x), a bound built from:
+//   the split residual      2 ||x|| R,       R = max_m ||c_m - hi_m - lo_m||,
+//   the MFMA accumulation   2 * 16 instructions, each rounding its result once
+//                           (the products of an instruction are summed before
+//                           one rounding), counted twice for margin: 64 u
+//                           ||x|| ||c||max, u = 2^-24, plus a 1% margin,
+//   cn_m and the final fma  u (||c||max^2 + 2 ||x|| ||c||max) each.
+// The true nearest centroid is then within 2E of the screen's best, so a token
+// whose second-best screen distance is more than 2E above its best keeps the
+// screen's label; otherwise it is queued and k_recheck settles it in fp64 with
+// the oracle's exact arithmetic (sum of (x_t - c_t)^2 in coordinate order,
+// lowest index on ties).  The labels therefore equal those of a direct fp64
+// evaluation.
+#include "internal.h"
+
+namespace svg {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int KM_D = 128;
+constexpr int KM_CB = 64;                       // centroids per LDS chunk
+constexpr int KM_PITCH = KM_D * 2 + 16;         // bytes per centroid row of a plane
+constexpr int KM_PLANE = KM_CB * KM_PITCH;      // 17408
+constexpr int KM_BUF = 2 * KM_PLANE + KM_CB * 4;  // hi, lo, ||c||^2
+constexpr int KM_LDS = 2 * KM_BUF;
+constexpr int KM_TOK = 256;                     // tokens per workgroup (4 waves x 64)
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// Per centroid: bf16 hi/lo planes, ||c||^2 (fp32 and fp64); per head: R and ||c||max
+// (as float bits, via integer max of non-negative floats).
+__global__ __launch_bounds__(KM_D) void k_km_prep(const double* __restrict__ cent64, int C,
+                                                  bf16* __restrict__ hi, bf16* __restrict__ lo,
+                                                  float* __restrict__ cn32,
+                                                  double* __restrict__ cn64,
+                                                  unsigned* __restrict__ stats)
+{
+    __shared__ double s_a[KM_D], s_b[KM_D];
+    const int m = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+    const size_t i = ((size_t)h * C + m) * KM_D + t;
+    const double c = cent64[i];
+    const bf16 ch = f32_to_bf16((float)c);
+    const double r1 = c - (double)bf16_to_f32(ch);
+    const bf16 cl = f32_to_bf16((float)r1);
+    const double r2 = r1 - (double)bf16_to_f32(cl);
+    hi[i] = ch;
+    lo[i] = cl;
+    s_a[t] = c * c;
+    s_b[t] = r2 * r2;
+    __syncthreads();
+    for (int o = KM_D / 2; o >= 1; o >>= 1) {
+        if (t < o) {
+            s_a[t] += s_a[t + o];
+            s_b[t] += s_b[t + o];
+        }
+        __syncthreads();
+    }
+    if (t == 0) {
+        const double n2 = s_a[0];
+        cn64[(size_t)h * C + m] = n2;
+        cn32[(size_t)h * C + m] = (float)n2;
+        const float cmax = (float)(sqrt(n2) * (1.0 + 1e-6));
+        const float res = (float)(sqrt(s_b[0]) * (1.0 + 1e-6));
+        atomicMax(stats + 4 * h + 0, __float_as_uint(res));
+        atomicMax(stats + 4 * h + 1, __float_as_uint(cmax));
+    }
+}
+
+struct KmStage {
+    u32x4_t v[8];  // hi rows r, r + 16, r + 32, r + 48 then lo rows, chunk tid & 15
+    float cn;
+};
+
+__device__ __forceinline__ void km_load(KmStage& s, const bf16* __restrict__ hi,
+                                        const bf16* __restrict__ lo, const float* __restrict__ cn,
+                                        int m0, int C, int tid)
+{
+    const int ch = tid & 15, r = tid >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = m0 + r + 16 * i;
+        const bool ok = m < C;
+        s.v[i] = ok ? *(const u32x4_t*)(hi + (size_t)m * KM_D + ch * 8) : u32x4_t{0, 0, 0, 0};
+        s.v[4 + i] = ok ? *(const u32x4_t*)(lo + (size_t)m * KM_D + ch * 8) : u32x4_t{0, 0, 0, 0};
+    }
+    s.cn = (tid < KM_CB && m0 + tid < C) ? cn[m0 + tid] : __builtin_inff();
+}
+
+__device__ __forceinline__ void km_store(const KmStage& s, char* buf, int tid)
+{
+    const int ch = tid & 15, r = tid >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        *(u32x4_t*)(buf + (r + 16 * i) * KM_PITCH + ch * 16) = s.v[i];
+        *(u32x4_t*)(buf + KM_PLANE + (r + 16 * i) * KM_PITCH + ch * 16) = s.v[4 + i];
+    }
+    if (tid < KM_CB) ((float*)(buf + 2 * KM_PLANE))[tid] = s.cn;
+}
+
+// Screen: labels = screen argmin; near-ties appended to flags[h, *] (token ids).
+__global__ __launch_bounds__(256, 2) void k_assign_mfma(
+    const bf16* __restrict__ X, const bf16* __restrict__ hi, const bf16* __restrict__ lo,
+    const float* __restrict__ cn32, const unsigned* __restrict__ stats, int N, int C,
+    int32_t* __restrict__ labels, int32_t* __restrict__ flags, int* __restrict__ nflag)
+{
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int h = blockIdx.y;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tcol = lane & 31, half = lane >> 5;
+    const bf16* Xh = X + (size_t)h * N * KM_D;
+    const bf16* hih = hi + (size_t)h * C * KM_D;
+    const bf16* loh = lo + (size_t)h * C * KM_D;
+    const float* cnh = cn32 + (size_t)h * C;
+
+    // Token fragments (B operand): token tok[tb], dims 16 s + 8 half + 0..7.
+    bf16x8_t xf[2][8];
+    float nx[2];
+    int tok[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+        tok[tb] = blockIdx.x * KM_TOK + wave * 64 + tb * 32 + tcol;
+        const int row = tok[tb] < N ? tok[tb] : N - 1;
+        const bf16* xp = Xh + (size_t)row * KM_D + half * 8;
+        float ss = 0.f;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const u32x4_t w = *(const u32x4_t*)(xp + 16 * s);
+            xf[tb][s] = as_bf16x8(w);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float a = __uint_as_float(w[e] << 16), b = __uint_as_float(w[e] & 0xFFFF0000u);
+                ss = fmaf(a, a, ss);
+                ss = fmaf(b, b, ss);
+            }
+        }
+        ss += __shfl_xor(ss, 32);
+        nx[tb] = sqrtf(ss);
+    }
+
+    float b1[2], b2[2];
+    int i1[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+        b1[tb] = __builtin_inff();
+        b2[tb] = __builtin_inff();
+        i1[tb] = 0;
+    }
+
+    const int nchunk = (C + KM_CB - 1) / KM_CB;
+    KmStage stg;
+    km_load(stg, hih, loh, cnh, 0, C, tid);
+    km_store(stg, smem, tid);
+    __syncthreads();
+    for (int k = 0; k < nchunk; ++k) {
+        char* buf = smem + (k & 1) * KM_BUF;
+        const bool more = k + 1 < nchunk;
+        if (more) km_load(stg, hih, loh, cnh, (k + 1) * KM_CB, C, tid);
+        const float* s_cn = (const float*)(buf + 2 * KM_PLANE);
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+            f32x16_t acc[2] = {f32x16_t{0}, f32x16_t{0}};
+            const char* rh = buf + (cb * 32 + tcol) * KM_PITCH + half * 16;
+            const char* rl = rh + KM_PLANE;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const bf16x8_t ah = as_bf16x8(*(const u32x4_t*)(rh + s * 32));
+                const bf16x8_t al = as_bf16x8(*(const u32x4_t*)(rl + s * 32));
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb) {
+                    acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xf[tb][s], acc[tb], 0, 0, 0);
+                    acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xf[tb][s], acc[tb], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int r = cb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+                const float cnv = s_cn[r];  // +inf past the last centroid
+                const int m = k * KM_CB + r;
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb) {
+                    const float d = fmaf(-2.f, acc[tb][i], cnv);
+                    const float u = fmaxf(b1[tb], d);
+                    i1[tb] = d < b1[tb] ? m : i1[tb];
+                    b1[tb] = fminf(b1[tb], d);
+                    b2[tb] = fminf(b2[tb], u);
+                }
+            }
+        }
+        if (more) {
+            km_store(stg, smem + ((k + 1) & 1) * KM_BUF, tid);
+            __syncthreads();
+        }
+    }
+
+    const float R = __uint_as_float(stats[4 * h + 0]);
+    const float cmax = __uint_as_float(stats[4 * h + 1]);
+    const float u = 5.9604645e-8f;  // 2^-24
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+        // merge with the partner half-wave (other centroid rows, same token)
+        const float pb1 = __shfl_xor(b1[tb], 32), pb2 = __shfl_xor(b2[tb], 32);
+        const int pi1 = __shfl_xor(i1[tb], 32);
+        const bool take = pb1 < b1[tb] || (pb1 == b1[tb] && pi1 < i1[tb]);
+        const float nb1 = take ? pb1 : b1[tb];
+        const int ni1 = take ? pi1 : i1[tb];
+        const float nb2 = fminf(fminf(b2[tb], pb2), fmaxf(b1[tb], pb1));
+        if (half == 0 && tok[tb] < N) {
+            const float xn = nx[tb] * 1.0001f;
+            const float E = 1.01f * (2.f * xn * R + 64.f * u * xn * cmax +
+                                     2.f * u * (cmax * cmax + 2.f * xn * cmax));
+            labels[(size_t)h * N + tok[tb]] = ni1;
+            if (!(nb2 - nb1 > 2.f * E)) {
+                const int pos = atomicAdd(nflag + h, 1);
+                flags[(size_t)h * N + pos] = tok[tb];
+            }
+        }
+    }
+}
+
+// Exact settlement of queued tokens.  8 lanes per token: pass 1 finds the fp64
+// minimum of ||c||^2 - 2 x.c (fused multiply-adds); pass 2 evaluates, for every
+// centroid within a tolerance of that minimum, the distance exactly as the
+// oracle does (sum of (x_t - c_t)^2 in coordinate order, no fusion) and keeps
+// the smallest, lowest index first.
+constexpr int RC_TOK = 32;
+constexpr int RC_CB = 16;
+
+__global__ __launch_bounds__(256) void k_recheck(const bf16* __restrict__ X,
+                                                 const double* __restrict__ cent64,
+                                                 const double* __restrict__ cn64,
+                                                 const unsigned* __restrict__ stats, int N, int C,
+                                                 const int32_t* __restrict__ flags,
+                                                 const int* __restrict__ nflag,
+                                                 int32_t* __restrict__ labels)
+{
+#pragma clang fp contract(off)
+    __shared__ double s_x[RC_TOK][KM_D + 1];
+    __shared__ double s_c[RC_CB][KM_D + 1];
+    __shared__ double s_cn[RC_CB];
+    const int h = blockIdx.y;
+    const int cnt = nflag[h];
+    const int grp = threadIdx.x >> 3, sub = threadIdx.x & 7;
+    const double* ch = cent64 + (size_t)h * C * KM_D;
+    for (int base = blockIdx.x * RC_TOK; base < cnt; base += gridDim.x * RC_TOK) {
+        const int e = base + grp;
+        const bool act = e < cnt;
+        const int token = act ? flags[(size_t)h * N + e] : 0;
+        __syncthreads();
+        for (int t = sub; t < KM_D; t += 8)
+            s_x[grp][t] = act ? (double)bf16_to_f32(X[((size_t)h * N + token) * KM_D + t]) : 0.0;
+        double xx = 0.0;
+        // pass 1: fp64 minimum of the dot form
+        double dmin = __builtin_inf();
+        for (int m0 = 0; m0 < C; m0 += RC_CB) {
+            const int cn = min(RC_CB, C - m0);
+            __syncthreads();
+            for (int k = threadIdx.x; k < cn * KM_D; k += 256)
+                s_c[k / KM_D][k % KM_D] = ch[(size_t)m0 * KM_D + k];
+            if (threadIdx.x < cn) s_cn[threadIdx.x] = cn64[(size_t)h * C + m0 + threadIdx.x];
+            __syncthreads();
+            for (int j = sub; j < cn; j += 8) {
+                double dot = 0.0;
+                for (int t = 0; t < KM_D; ++t) dot = fma(s_x[grp][t], s_c[j][t], dot);
+                dmin = fmin(dmin, fma(-2.0, dot, s_cn[j]));
+            }
+        }
+        for (int o = 4; o >= 1; o >>= 1) dmin = fmin(dmin, __shfl_xor(dmin, o, 8));
+        for (int t = 0; t < KM_D; ++t) xx = fma(s_x[grp][t], s_x[grp][t], xx);
+        // |dot form - exact form| <= 260 * 2^-53 * (||x|| + ||c||)^2 for every centroid, so
+        // the exact minimiser lies within twice that of the dot-form minimum.
+        const double cmax = (double)__uint_as_float(stats[4 * h + 1]);
+        const double nxc = sqrt(xx) + cmax;
+        const double tol = 0x1p-42 * nxc * nxc;
+        // pass 2: exact distances of the candidates
+        double best = __builtin_inf();
+        int bi = 0x7fffffff;
+        for (int m0 = 0; m0 < C; m0 += RC_CB) {
+            const int cn = min(RC_CB, C - m0);
+            __syncthreads();
+            for (int k = threadIdx.x; k < cn * KM_D; k += 256)
+                s_c[k / KM_D][k % KM_D] = ch[(size_t)m0 * KM_D + k];
+            if (threadIdx.x < cn) s_cn[threadIdx.x] = cn64[(size_t)h * C + m0 + threadIdx.x];
+            __syncthreads();
+            for (int j = sub; j < cn; j += 8) {
+                double dot = 0.0;
+                for (int t = 0; t < KM_D; ++t) dot = fma(s_x[grp][t], s_c[j][t], dot);
+                if (fma(-2.0, dot, s_cn[j]) <= dmin + tol) {
+                    double s = 0.0;
+                    for (int t = 0; t < KM_D; ++t) {
+                        const double w = __dsub_rn(s_x[grp][t], s_c[j][t]);
+                        s = __dadd_rn(s, __dmul_rn(w, w));
+                    }
+                    if (s < best || (s == best && m0 + j < bi)) {
+                        best = s;
+                        bi = m0 + j;
+                    }
+                }
+            }
+        }
+        for (int o = 4; o >= 1; o >>= 1) {
+            const double ob = __shfl_xor(best, o, 8);
+            const int oi = __shfl_xor(bi, o, 8);
+            if (ob < best || (ob == best && oi < bi)) {
+                best = ob;
+                bi = oi;
+            }
+        }
+        if (act && sub == 0) labels[(size_t)h * N + token] = bi;
+    }
+}
+
+SVG_HIDDEN void zero_words(void* p, size_t bytes, hipStream_t st);
+
+SVG_HIDDEN bool assign_mfma_supported(const ClusterArgs& a)
+{
+    return a.dtype == SVGEAR_BF16 && a.d == KM_D;
+}
+
+SVG_HIDDEN hipError_t launch_assign_mfma(const ClusterArgs& a, const double* cent64, int*,
+                                         hipStream_t st)
+{
+    const Layout& L = *a.L;
+    char* s = a.scratch;
+    bf16* hi = (bf16*)(s + L.cl_hi);
+    bf16* lo = (bf16*)(s + L.cl_lo);
+    float* cn32 = (float*)(s + L.cl_cnorm);
+    double* cn64 = (double*)(s + L.cl_cn64);
+    unsigned* stats = (unsigned*)(s + L.cl_stats);
+    int32_t* flags = (int32_t*)(s + L.cl_flag);
+    int* nflag = (int*)(s + L.cl_nflag);
+    zero_words(stats, (size_t)a.H * 16, st);
+    zero_words(nflag, (size_t)a.H * 4, st);
+    hipLaunchKernelGGL(k_km_prep, dim3(a.C, a.H), dim3(KM_D), 0, st, cent64, a.C, hi, lo, cn32, cn64,
+                       stats);
+    hipLaunchKernelGGL(k_assign_mfma, dim3((a.N + KM_TOK - 1) / KM_TOK, a.H), dim3(256), KM_LDS, st,
+                       (const bf16*)a.X, hi, lo, cn32, stats, a.N, a.C, a.labels, flags, nflag);
+    const int rblocks = (a.N / 64 + RC_TOK - 1) / RC_TOK + 1;
+    hipLaunchKernelGGL(k_recheck, dim3(rblocks < 64 ? rblocks : 64, a.H), dim3(256), 0, st,
+                       (const bf16*)a.X, cent64, cn64, stats, a.N, a.C, flags, nflag, a.labels);
+    return hipGetLastError();
+}
+
+}  // namespace svg

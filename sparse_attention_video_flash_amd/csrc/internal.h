@@ -68,7 +68,7 @@ struct Layout {
     size_t log_ratio, mask, sel_cost;
     size_t scratch;  // start of the per-stage scratch
     // cluster scratch (relative to scratch)
-    size_t cl_err, cl_cent64, cl_sums, cl_cnt, cl_hi, cl_lo, cl_cnorm, cl_stats, cl_flag, cl_nflag,
+    size_t cl_err, cl_cent64, cl_sums, cl_cnt, cl_hi, cl_lo, cl_cnorm, cl_cn64, cl_stats, cl_flag, cl_nflag,
         cl_hist;
     size_t cl_end;
     // probe scratch (relative to scratch)
