@@ -51,8 +51,6 @@ SVG_HIDDEN Layout make_layout(const svgear_shape& s)
     off = 0;
     L.cl_err = take(256);
     L.cl_cent64 = take(H * C * d * 8);
-    L.cl_sums = take(H * C * d * 8);
-    L.cl_cnt = take(H * C * 4);
     L.cl_hi = take(H * C * d * 2);
     L.cl_lo = take(H * C * d * 2);
     L.cl_cnorm = take(H * C * 4);
@@ -61,6 +59,9 @@ SVG_HIDDEN Layout make_layout(const svgear_shape& s)
     L.cl_flag = take(H * N * 4);
     L.cl_nflag = take(H * 4);
     L.cl_hist = take(H * ntiles * C * 4);
+    L.cl_perm = take(H * N * 4);
+    L.cl_sums = take(H * C * d * 8);
+    L.cl_resid = take(H * C * 4);
     L.cl_end = off;
 
     off = 0;
@@ -78,6 +79,9 @@ SVG_HIDDEN Layout make_layout(const svgear_shape& s)
     L.at_tiles = take(H * (Cq + 1) * 4 + 256);
     L.at_segs = take(H * Cq * Ck * 8);
     L.at_nsegs = take(H * Cq * 4);
+    L.at_nkeys = take(H * Cq * 4);
+    L.at_comp = take(H * Cq * Ck * 4);
+    L.at_ncomp = take(H * Cq * 4);
     L.at_end = off;
 
     size_t sc = L.cl_end;

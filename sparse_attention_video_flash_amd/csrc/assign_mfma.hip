@@ -42,6 +42,7 @@ __global__ __launch_bounds__(KM_D) void k_km_prep(const double* __restrict__ cen
                                                   bf16* __restrict__ hi, bf16* __restrict__ lo,
                                                   float* __restrict__ cn32,
                                                   double* __restrict__ cn64,
+                                                  float* __restrict__ resid,
                                                   unsigned* __restrict__ stats)
 {
     __shared__ double s_a[KM_D], s_b[KM_D];
@@ -70,6 +71,7 @@ __global__ __launch_bounds__(KM_D) void k_km_prep(const double* __restrict__ cen
         cn32[(size_t)h * C + m] = (float)n2;
         const float cmax = (float)(sqrt(n2) * (1.0 + 1e-6));
         const float res = (float)(sqrt(s_b[0]) * (1.0 + 1e-6));
+        resid[(size_t)h * C + m] = res;
         atomicMax(stats + 4 * h + 0, __float_as_uint(res));
         atomicMax(stats + 4 * h + 1, __float_as_uint(cmax));
     }
@@ -146,12 +148,12 @@ __global__ __launch_bounds__(256, 2) void k_assign_mfma(
         nx[tb] = sqrtf(ss);
     }
 
+    // per lane and token block: the two smallest screen distances, index of the first
     float b1[2], b2[2];
     int i1[2];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-        b1[tb] = __builtin_inff();
-        b2[tb] = __builtin_inff();
+        b1[tb] = b2[tb] = __builtin_inff();
         i1[tb] = 0;
     }
 
@@ -226,14 +228,13 @@ __global__ __launch_bounds__(256, 2) void k_assign_mfma(
     }
 }
 
-// Exact settlement of queued tokens.  8 lanes per token: pass 1 finds the fp64
-// minimum of ||c||^2 - 2 x.c (fused multiply-adds); pass 2 evaluates, for every
-// centroid within a tolerance of that minimum, the distance exactly as the
-// oracle does (sum of (x_t - c_t)^2 in coordinate order, no fusion) and keeps
-// the smallest, lowest index first.
-constexpr int RC_TOK = 32;
-constexpr int RC_CB = 16;
-
+// Exact settlement of queued tokens (few per head), one workgroup per token.
+// Pass 1: every centroid's ||c||^2 - 2 x.c in fp64, each thread owning whole
+// centroid rows (16-byte loads, x broadcast from LDS).  Pass 2: for every
+// centroid within a tolerance of the minimum, the distance exactly as the
+// oracle evaluates it (sum of (x_t - c_t)^2 in coordinate order, no fusion),
+// rows staged in LDS; the smallest wins, lowest index first.
+constexpr int RC_ROWS = 8, RC_MAXCAND = 64;
 __global__ __launch_bounds__(256) void k_recheck(const bf16* __restrict__ X,
                                                  const double* __restrict__ cent64,
                                                  const double* __restrict__ cn64,
@@ -243,109 +244,152 @@ __global__ __launch_bounds__(256) void k_recheck(const bf16* __restrict__ X,
                                                  int32_t* __restrict__ labels)
 {
 #pragma clang fp contract(off)
-    __shared__ double s_x[RC_TOK][KM_D + 1];
-    __shared__ double s_c[RC_CB][KM_D + 1];
-    __shared__ double s_cn[RC_CB];
+    __shared__ double s_x[KM_D];
+    __shared__ double s_d[kMaxC];
+    __shared__ double s_rb[4];
+    __shared__ int s_ri[4];
+    __shared__ double s_c[RC_ROWS][KM_D];
+    __shared__ int s_cand[RC_MAXCAND];
+    __shared__ int s_nc;
     const int h = blockIdx.y;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int cnt = nflag[h];
-    const int grp = threadIdx.x >> 3, sub = threadIdx.x & 7;
     const double* ch = cent64 + (size_t)h * C * KM_D;
-    for (int base = blockIdx.x * RC_TOK; base < cnt; base += gridDim.x * RC_TOK) {
-        const int e = base + grp;
-        const bool act = e < cnt;
-        const int token = act ? flags[(size_t)h * N + e] : 0;
+    const double* cnh = cn64 + (size_t)h * C;
+    const double cmax = (double)__uint_as_float(stats[4 * h + 1]);
+    for (int e = blockIdx.x; e < cnt; e += gridDim.x) {
+        const int token = flags[(size_t)h * N + e];
         __syncthreads();
-        for (int t = sub; t < KM_D; t += 8)
-            s_x[grp][t] = act ? (double)bf16_to_f32(X[((size_t)h * N + token) * KM_D + t]) : 0.0;
-        double xx = 0.0;
-        // pass 1: fp64 minimum of the dot form
-        double dmin = __builtin_inf();
-        for (int m0 = 0; m0 < C; m0 += RC_CB) {
-            const int cn = min(RC_CB, C - m0);
-            __syncthreads();
-            for (int k = threadIdx.x; k < cn * KM_D; k += 256)
-                s_c[k / KM_D][k % KM_D] = ch[(size_t)m0 * KM_D + k];
-            if (threadIdx.x < cn) s_cn[threadIdx.x] = cn64[(size_t)h * C + m0 + threadIdx.x];
-            __syncthreads();
-            for (int j = sub; j < cn; j += 8) {
-                double dot = 0.0;
-                for (int t = 0; t < KM_D; ++t) dot = fma(s_x[grp][t], s_c[j][t], dot);
-                dmin = fmin(dmin, fma(-2.0, dot, s_cn[j]));
+        if (tid < KM_D) s_x[tid] = (double)bf16_to_f32(X[((size_t)h * N + token) * KM_D + tid]);
+        __syncthreads();
+        for (int m = tid; m < C; m += 256) {
+            const double2* cr = (const double2*)(ch + (size_t)m * KM_D);
+            double d0 = 0.0, d1 = 0.0, d2 = 0.0, d3 = 0.0;
+#pragma unroll 4
+            for (int t = 0; t < KM_D / 2; t += 2) {
+                const double2 a = cr[t], b = cr[t + 1];
+                d0 = fma(s_x[2 * t], a.x, d0);
+                d1 = fma(s_x[2 * t + 1], a.y, d1);
+                d2 = fma(s_x[2 * t + 2], b.x, d2);
+                d3 = fma(s_x[2 * t + 3], b.y, d3);
             }
+            s_d[m] = fma(-2.0, (d0 + d1) + (d2 + d3), cnh[m]);
         }
-        for (int o = 4; o >= 1; o >>= 1) dmin = fmin(dmin, __shfl_xor(dmin, o, 8));
-        for (int t = 0; t < KM_D; ++t) xx = fma(s_x[grp][t], s_x[grp][t], xx);
-        // |dot form - exact form| <= 260 * 2^-53 * (||x|| + ||c||)^2 for every centroid, so
-        // the exact minimiser lies within twice that of the dot-form minimum.
-        const double cmax = (double)__uint_as_float(stats[4 * h + 1]);
+        __syncthreads();
+        double dmin = __builtin_inf();
+        for (int m = tid; m < C; m += 256) dmin = fmin(dmin, s_d[m]);
+        for (int o = 32; o >= 1; o >>= 1) dmin = fmin(dmin, __shfl_xor(dmin, o));
+        if (lane == 0) s_rb[wave] = dmin;
+        __syncthreads();
+        dmin = fmin(fmin(s_rb[0], s_rb[1]), fmin(s_rb[2], s_rb[3]));
+        double xx = 0.0;
+        for (int t = 0; t < KM_D; ++t) xx = fma(s_x[t], s_x[t], xx);
+        // |dot form - exact form| <= 260 * 2^-53 * (||x|| + ||c||)^2 for every centroid,
+        // so the exact minimiser lies within twice that of the dot-form minimum.
         const double nxc = sqrt(xx) + cmax;
         const double tol = 0x1p-42 * nxc * nxc;
-        // pass 2: exact distances of the candidates
+        // candidates (usually one or two): compacted per block of RC_MAXCAND centroids,
+        // their rows staged in LDS for the sequential exact sums
         double best = __builtin_inf();
         int bi = 0x7fffffff;
-        for (int m0 = 0; m0 < C; m0 += RC_CB) {
-            const int cn = min(RC_CB, C - m0);
+        for (int m0 = 0; m0 < C; m0 += RC_MAXCAND) {
+            if (tid == 0) s_nc = 0;
             __syncthreads();
-            for (int k = threadIdx.x; k < cn * KM_D; k += 256)
-                s_c[k / KM_D][k % KM_D] = ch[(size_t)m0 * KM_D + k];
-            if (threadIdx.x < cn) s_cn[threadIdx.x] = cn64[(size_t)h * C + m0 + threadIdx.x];
+            if (tid < RC_MAXCAND && m0 + tid < C && s_d[m0 + tid] <= dmin + tol)
+                s_cand[atomicAdd(&s_nc, 1)] = m0 + tid;
             __syncthreads();
-            for (int j = sub; j < cn; j += 8) {
-                double dot = 0.0;
-                for (int t = 0; t < KM_D; ++t) dot = fma(s_x[grp][t], s_c[j][t], dot);
-                if (fma(-2.0, dot, s_cn[j]) <= dmin + tol) {
-                    double s = 0.0;
+            const int nc = s_nc;
+            for (int k0 = 0; k0 < nc; k0 += RC_ROWS) {
+                const int kn = min(RC_ROWS, nc - k0);
+                for (int k = tid; k < kn * KM_D; k += 256)
+                    s_c[k / KM_D][k % KM_D] = ch[(size_t)s_cand[k0 + k / KM_D] * KM_D + k % KM_D];
+                __syncthreads();
+                if (tid < kn) {
+                    const int m = s_cand[k0 + tid];
+                    double sd = 0.0;
                     for (int t = 0; t < KM_D; ++t) {
-                        const double w = __dsub_rn(s_x[grp][t], s_c[j][t]);
-                        s = __dadd_rn(s, __dmul_rn(w, w));
+                        const double w = __dsub_rn(s_x[t], s_c[tid][t]);
+                        sd = __dadd_rn(sd, __dmul_rn(w, w));
                     }
-                    if (s < best || (s == best && m0 + j < bi)) {
-                        best = s;
-                        bi = m0 + j;
+                    if (sd < best || (sd == best && m < bi)) {
+                        best = sd;
+                        bi = m;
                     }
                 }
+                __syncthreads();
             }
         }
-        for (int o = 4; o >= 1; o >>= 1) {
-            const double ob = __shfl_xor(best, o, 8);
-            const int oi = __shfl_xor(bi, o, 8);
+        for (int o = 32; o >= 1; o >>= 1) {
+            const double ob = __shfl_xor(best, o);
+            const int oi = __shfl_xor(bi, o);
             if (ob < best || (ob == best && oi < bi)) {
                 best = ob;
                 bi = oi;
             }
         }
-        if (act && sub == 0) labels[(size_t)h * N + token] = bi;
+        __syncthreads();
+        if (lane == 0) {
+            s_rb[wave] = best;
+            s_ri[wave] = bi;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            for (int w = 1; w < 4; ++w)
+                if (s_rb[w] < best || (s_rb[w] == best && s_ri[w] < bi)) {
+                    best = s_rb[w];
+                    bi = s_ri[w];
+                }
+            labels[(size_t)h * N + token] = bi;
+        }
     }
 }
 
-SVG_HIDDEN void zero_words(void* p, size_t bytes, hipStream_t st);
+struct KmPlanes {
+    bf16* hi;
+    bf16* lo;
+    float* cn32;
+    double* cn64;
+    unsigned* stats;
+    int32_t* flags;
+    int* nflag;
+};
+
+SVG_HIDDEN KmPlanes km_planes(const ClusterArgs& a)
+{
+    const Layout& L = *a.L;
+    char* s = a.scratch;
+    KmPlanes P;
+    P.hi = (bf16*)(s + L.cl_hi);
+    P.lo = (bf16*)(s + L.cl_lo);
+    P.cn32 = (float*)(s + L.cl_cnorm);
+    P.cn64 = (double*)(s + L.cl_cn64);
+    P.stats = (unsigned*)(s + L.cl_stats);
+    P.flags = (int32_t*)(s + L.cl_flag);
+    P.nflag = (int*)(s + L.cl_nflag);
+    return P;
+}
 
 SVG_HIDDEN bool assign_mfma_supported(const ClusterArgs& a)
 {
     return a.dtype == SVGEAR_BF16 && a.d == KM_D;
 }
 
-SVG_HIDDEN hipError_t launch_assign_mfma(const ClusterArgs& a, const double* cent64, int*,
-                                         hipStream_t st)
+SVG_HIDDEN hipError_t launch_km_prep(const ClusterArgs& a, const double* cent64, const KmPlanes& P,
+                                     hipStream_t st)
 {
-    const Layout& L = *a.L;
-    char* s = a.scratch;
-    bf16* hi = (bf16*)(s + L.cl_hi);
-    bf16* lo = (bf16*)(s + L.cl_lo);
-    float* cn32 = (float*)(s + L.cl_cnorm);
-    double* cn64 = (double*)(s + L.cl_cn64);
-    unsigned* stats = (unsigned*)(s + L.cl_stats);
-    int32_t* flags = (int32_t*)(s + L.cl_flag);
-    int* nflag = (int*)(s + L.cl_nflag);
-    zero_words(stats, (size_t)a.H * 16, st);
-    zero_words(nflag, (size_t)a.H * 4, st);
-    hipLaunchKernelGGL(k_km_prep, dim3(a.C, a.H), dim3(KM_D), 0, st, cent64, a.C, hi, lo, cn32, cn64,
-                       stats);
+    hipLaunchKernelGGL(k_km_prep, dim3(a.C, a.H), dim3(KM_D), 0, st, cent64, a.C, P.hi, P.lo, P.cn32,
+                       P.cn64, (float*)(a.scratch + a.L->cl_resid), P.stats);
+    return hipGetLastError();
+}
+
+SVG_HIDDEN hipError_t launch_assign_mfma(const ClusterArgs& a, const double* cent64,
+                                         const KmPlanes& P, hipStream_t st)
+{
     hipLaunchKernelGGL(k_assign_mfma, dim3((a.N + KM_TOK - 1) / KM_TOK, a.H), dim3(256), KM_LDS, st,
-                       (const bf16*)a.X, hi, lo, cn32, stats, a.N, a.C, a.labels, flags, nflag);
-    const int rblocks = (a.N / 64 + RC_TOK - 1) / RC_TOK + 1;
-    hipLaunchKernelGGL(k_recheck, dim3(rblocks < 64 ? rblocks : 64, a.H), dim3(256), 0, st,
-                       (const bf16*)a.X, cent64, cn64, stats, a.N, a.C, flags, nflag, a.labels);
+                       (const bf16*)a.X, P.hi, P.lo, P.cn32, P.stats, a.N, a.C, a.labels, P.flags,
+                       P.nflag);
+    hipLaunchKernelGGL(k_recheck, dim3(64, a.H), dim3(256), 0, st, (const bf16*)a.X, cent64, P.cn64,
+                       P.stats, a.N, a.C, P.flags, P.nflag, a.labels);
     return hipGetLastError();
 }
 

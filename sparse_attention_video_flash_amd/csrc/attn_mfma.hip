@@ -7,18 +7,24 @@
 // S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so every lane holds one query
 // column and the softmax row statistics stay inside a lane (one exchange with
 // the partner half-wave per tile for the running max).  The probabilities are
-// already laid out as the B operand of O^T = V^T P^T, provided the value tile
-// is stored transposed in LDS with key slots permuted (bits 2 and 3 of the key
-// index swapped), so each lane reads its 8 keys with one 16-byte load.
+// then already the B operand of O^T = V^T P^T; the V^T operand is read from the
+// row-major value tile with ds_read_b64_tr_b16 (within each 16-lane group,
+// result lane i, element k comes from source lane 4k + i/4, element i % 4), two
+// loads per fragment.
 //
-// Key tiles of BN = 64:
-//   1. compensation tiles: the centroids of all key clusters, split into bf16
-//      hi + lo planes (k-bar and v-bar are fp32), logits tau q.kbar_g + ln m_g,
-//      masked to the clusters that are skipped for c and non-empty;
-//   2. exact tiles: the keys of every routed (mask = 1) key cluster, segment by
-//      segment (a segment's last tile is masked), K/V double-buffered in LDS
-//      with the next tile's global loads in flight during the current tile.
+// Key tiles of BN = 64 rows, packed: a tile takes the next 64 entries of the
+// cluster's key list, so no tile is padded at a key-cluster boundary.
+//   1. compensation tiles: the centroids of the key clusters that are skipped
+//      for c and non-empty, split into bf16 hi + lo planes (k-bar and v-bar are
+//      fp32), with logit tau q.kbar_g + ln m_g;
+//   2. exact tiles: the keys of every routed key cluster, K and V
+//      double-buffered in LDS, the next tile's global loads in flight during
+//      the current tile's math.
 // One online softmax (base-2 exponent) covers both kinds of terms.
+//
+// Workgroups are ordered so that the query tiles of one cluster run
+// back-to-back on the same XCD (workgroup ids are dealt round-robin over the
+// eight XCDs), letting them share key/value lines in that XCD's L2.
 #include "internal.h"
 
 namespace svg {
@@ -27,18 +33,19 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr int AT_BM = 128;
 constexpr int AT_BN = 64;
 constexpr int AT_D = 128;
 constexpr int AT_THREADS = 256;
-constexpr int K_PITCH = AT_D * 2 + 16;   // bytes per key row of a K tile in LDS
-constexpr int V_PITCH = AT_BN * 2 + 16;  // bytes per d row of a transposed V tile
-constexpr int K_BUF = AT_BN * K_PITCH;   // 17408
-constexpr int V_BUF = AT_D * V_PITCH;    // 18432
-constexpr int AT_LDS = 2 * K_BUF + 2 * V_BUF + AT_BN * 4;
-
-__device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+constexpr int K_PITCH = AT_D * 2 + 16;  // 272 B: 16 consecutive rows hit distinct banks (b128)
+constexpr int V_PITCH = AT_D * 2 + 64;  // 320 B: transpose reads of 4 rows x 2 column groups
+constexpr int K_BUF = AT_BN * K_PITCH;  // 17408
+constexpr int V_BUF = AT_BN * V_PITCH;  // 20480
+constexpr int AT_LDS = 2 * K_BUF + 2 * V_BUF + AT_BN * 4 + 2 * AT_BN * 4 + 16;
+constexpr int AT_XCD = 8;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
@@ -64,40 +71,62 @@ __global__ void k_comp_planes(const float* __restrict__ kbar, const float* __res
     }
 }
 
-// Routed key segments of each (head, query cluster), in key-cluster order:
-// (first reordered key, length) of every g with mask[c, g] = 1 and m_g > 0.
+// Per (head, query cluster), in key-cluster order: the routed segments
+// (first reordered key, length) of every g with mask[c, g] = 1 and m_g > 0, their
+// total length, and the list of compensated clusters (mask = 0, m_g > 0).
 __global__ __launch_bounds__(256) void k_seg_list(const uint8_t* __restrict__ mask,
                                                   const int32_t* __restrict__ offsets_k, int Cq,
                                                   int Ck, int2* __restrict__ segs,
-                                                  int* __restrict__ nsegs)
+                                                  int* __restrict__ nsegs, int* __restrict__ nkeys,
+                                                  int* __restrict__ comp, int* __restrict__ ncomp)
 {
-    __shared__ int s_cnt[256];
+    __shared__ int s_a[256], s_b[256];
     const int c = blockIdx.x, h = blockIdx.y;
     const uint8_t* mrow = mask + ((size_t)h * Cq + c) * Ck;
     const int32_t* ok = offsets_k + (size_t)h * (Ck + 1);
     int2* out = segs + ((size_t)h * Cq + c) * Ck;
-    int base = 0;
+    int* cout = comp + ((size_t)h * Cq + c) * Ck;
+    int base = 0, cbase = 0, keys = 0;
     for (int g0 = 0; g0 < Ck; g0 += 256) {
         const int g = g0 + threadIdx.x;
-        int sel = 0, start = 0, len = 0;
+        int sel = 0, cmp = 0, start = 0, len = 0;
         if (g < Ck) {
             start = ok[g];
             len = ok[g + 1] - start;
             sel = mrow[g] && len > 0;
+            cmp = !mrow[g] && len > 0;
         }
-        s_cnt[threadIdx.x] = sel;
+        s_a[threadIdx.x] = sel;
+        s_b[threadIdx.x] = cmp;
         __syncthreads();
         for (int off = 1; off < 256; off <<= 1) {
-            int v = threadIdx.x >= off ? s_cnt[threadIdx.x - off] : 0;
+            const int va = threadIdx.x >= off ? s_a[threadIdx.x - off] : 0;
+            const int vb = threadIdx.x >= off ? s_b[threadIdx.x - off] : 0;
             __syncthreads();
-            s_cnt[threadIdx.x] += v;
+            s_a[threadIdx.x] += va;
+            s_b[threadIdx.x] += vb;
             __syncthreads();
         }
-        if (sel) out[base + s_cnt[threadIdx.x] - 1] = make_int2(start, len);
-        base += s_cnt[255];
+        if (sel) out[base + s_a[threadIdx.x] - 1] = make_int2(start, len);
+        if (cmp) cout[cbase + s_b[threadIdx.x] - 1] = g;
+        base += s_a[255];
+        cbase += s_b[255];
+        __syncthreads();
+        // routed keys in this chunk
+        s_a[threadIdx.x] = sel ? len : 0;
+        __syncthreads();
+        for (int off = 128; off >= 1; off >>= 1) {
+            if (threadIdx.x < off) s_a[threadIdx.x] += s_a[threadIdx.x + off];
+            __syncthreads();
+        }
+        keys += s_a[0];
         __syncthreads();
     }
-    if (threadIdx.x == 0) nsegs[(size_t)h * Cq + c] = base;
+    if (threadIdx.x == 0) {
+        nsegs[(size_t)h * Cq + c] = base;
+        ncomp[(size_t)h * Cq + c] = cbase;
+        nkeys[(size_t)h * Cq + c] = keys;
+    }
 }
 
 // Per head: first query tile of each cluster (exclusive prefix of ceil(n_c/BM)).
@@ -133,81 +162,47 @@ __global__ __launch_bounds__(1024) void k_tile_prefix(const int32_t* __restrict_
 
 // ----------------------------------------------------------------------------- tile staging
 
+// Rows kr + 16 i (i = 0..3), 16-byte chunk kc of K and V; row r of the tile is
+// source row map[r] (always a valid row: rows past the list are clamped and
+// masked out later).
 struct Stage {
-    u32x4_t k[4];  // rows kr + 16 i, chunk kc
-    u32x4_t v[4];  // keys 4 vg + i, chunk vc
+    u32x4_t k[4];
+    u32x4_t v[4];
 };
 
-// Global -> registers.  Rows at or beyond nvalid are zero.
-__device__ __forceinline__ void stage_load(Stage& s, const bf16* __restrict__ Kbase,
-                                           const bf16* __restrict__ Vbase, int nvalid, int tid)
+__device__ __forceinline__ void stage_load(Stage& s, const bf16* __restrict__ K,
+                                           const bf16* __restrict__ V, const int* map, int tid)
 {
     const int kc = tid & 15, kr = tid >> 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int r = kr + 16 * i;
-        s.k[i] = r < nvalid ? *(const u32x4_t*)(Kbase + (size_t)r * AT_D + kc * 8) : u32x4_t{0, 0, 0, 0};
-    }
-    const int vc = tid & 15, vg = tid >> 4;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 4 * vg + i;
-        s.v[i] = r < nvalid ? *(const u32x4_t*)(Vbase + (size_t)r * AT_D + vc * 8) : u32x4_t{0, 0, 0, 0};
+        const size_t row = (size_t)map[kr + 16 * i];
+        s.k[i] = *(const u32x4_t*)(K + row * AT_D + kc * 8);
+        s.v[i] = *(const u32x4_t*)(V + row * AT_D + kc * 8);
     }
 }
 
-// Registers -> LDS: K row-major, V transposed with permuted key slots.
 __device__ __forceinline__ void stage_store(const Stage& s, char* kbuf, char* vbuf, int tid)
 {
     const int kc = tid & 15, kr = tid >> 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *(u32x4_t*)(kbuf + (kr + 16 * i) * K_PITCH + kc * 16) = s.k[i];
-    const int vc = tid & 15, vg = tid >> 4;
-    const int key0 = 4 * vg;
-    const int slot0 = (key0 & 32) + swap23(key0 & 31);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        // d = 8 vc + 2j (low halves) and 8 vc + 2j + 1 (high halves)
-        const unsigned a0 = s.v[0][j], a1 = s.v[1][j], a2 = s.v[2][j], a3 = s.v[3][j];
-        u32x2_t lo, hi;
-        lo[0] = (a0 & 0xFFFFu) | (a1 << 16);
-        lo[1] = (a2 & 0xFFFFu) | (a3 << 16);
-        hi[0] = (a0 >> 16) | (a1 & 0xFFFF0000u);
-        hi[1] = (a2 >> 16) | (a3 & 0xFFFF0000u);
-        const int d = 8 * vc + 2 * j;
-        *(u32x2_t*)(vbuf + d * V_PITCH + slot0 * 2) = lo;
-        *(u32x2_t*)(vbuf + (d + 1) * V_PITCH + slot0 * 2) = hi;
+    for (int i = 0; i < 4; ++i) {
+        *(u32x4_t*)(kbuf + (kr + 16 * i) * K_PITCH + kc * 16) = s.k[i];
+        *(u32x4_t*)(vbuf + (kr + 16 * i) * V_PITCH + kc * 16) = s.v[i];
     }
 }
 
 // ----------------------------------------------------------------------------- per-tile math
 
 struct Softmax {
-    float m;      // running max (base-2 logits), shared by both half-waves
-    float l;      // this half-wave's partial sum of probabilities
+    float m;        // running max of the base-2 logits, shared by both half-waves
+    float l;        // this half-wave's partial sum of probabilities
     f32x16_t o[4];  // O^T blocks: d rows 32 db + ..., query column lane & 31
 };
 
-// S^T for a 64-key tile: two 32x32 blocks.
+// acc (+)= K Q^T for a 64-key tile: two 32x32 blocks.
 __device__ __forceinline__ void tile_scores(f32x16_t acc[2], const char* kbuf, const bf16x8_t qf[8],
                                             int lane)
-{
-    const int row = lane & 31, half = lane >> 5;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        f32x16_t a = {0};
-        const char* kr = kbuf + (kb * 32 + row) * K_PITCH + half * 16;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const bf16x8_t kf = as_bf16x8(*(const u32x4_t*)(kr + s * 32));
-            a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], a, 0, 0, 0);
-        }
-        acc[kb] = a;
-    }
-}
-
-__device__ __forceinline__ void tile_scores_acc(f32x16_t acc[2], const char* kbuf,
-                                                const bf16x8_t qf[8], int lane)
 {
     const int row = lane & 31, half = lane >> 5;
 #pragma unroll
@@ -223,19 +218,25 @@ __device__ __forceinline__ void tile_scores_acc(f32x16_t acc[2], const char* kbu
     }
 }
 
-// Online softmax update with the tile's base-2 logits x[kb][i]; returns the
-// probabilities as PV B-operand fragments pf[kb*2 + ks].
-__device__ __forceinline__ void softmax_update(Softmax& st, f32x16_t x[2], bf16x8_t pf[4])
+// Online softmax with raw scores x (logit = x * scale2 + bias, base 2).
+// Returns the probabilities as PV B-operand fragments pf[kb * 2 + ks].
+__device__ __forceinline__ void softmax_update(Softmax& st, const f32x16_t x[2], float scale2,
+                                               bf16x8_t pf[4])
 {
     float mloc = -__builtin_inff();
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, x[kb][i]);
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * scale2;
     const float mnew = fmaxf(st.m, mloc);
     const float muse = mnew == -__builtin_inff() ? 0.f : mnew;
-    const float alpha = __builtin_amdgcn_exp2f(st.m - muse);
+    if (__any(mnew > st.m)) {
+        const float alpha = __builtin_amdgcn_exp2f(st.m - muse);
+        st.l *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) st.o[db] *= alpha;
+    }
     st.m = mnew;
     float sum = 0.f;
 #pragma unroll
@@ -245,31 +246,62 @@ __device__ __forceinline__ void softmax_update(Softmax& st, f32x16_t x[2], bf16x
             bf16x8_t f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const float p = __builtin_amdgcn_exp2f(x[kb][8 * ks + i] - muse);
+                const float p = __builtin_amdgcn_exp2f(fmaf(x[kb][8 * ks + i], scale2, -muse));
                 sum += p;
                 f[i] = (__bf16)p;
             }
             pf[kb * 2 + ks] = f;
         }
     }
-    st.l = fmaf(st.l, alpha, sum);
-#pragma unroll
-    for (int db = 0; db < 4; ++db) st.o[db] *= alpha;
+    st.l += sum;
 }
 
-// O^T += V^T P^T for one 64-key tile held transposed in vbuf.
+// O^T += V^T P^T for one 64-key tile held row-major in vbuf (transpose loads).
 __device__ __forceinline__ void tile_pv(Softmax& st, const char* vbuf, const bf16x8_t pf[4], int lane)
 {
-    const int row = lane & 31, half = lane >> 5;
+    const int j = lane & 15, grp = lane >> 4;
+    const int half = grp >> 1;
+    // row 4 half + j / 4 (+16 kk, +8 for the second load), column 16 (grp & 1) + 4 (j & 3)
+    const char* base = vbuf + (4 * half + (j >> 2)) * V_PITCH + (16 * (grp & 1) + 4 * (j & 3)) * 2;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-        const char* vr = vbuf + (db * 32 + row) * V_PITCH + half * 16;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {  // kk = kb * 2 + ks: slots 16 kk + 8 half
-            const bf16x8_t vf = as_bf16x8(*(const u32x4_t*)(vr + kk * 32));
+        for (int kk = 0; kk < 4; ++kk) {
+            const char* a = base + (16 * kk) * V_PITCH + (32 * db) * 2;
+            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a);
+            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a + 8 * V_PITCH));
+            const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+            const bf16x8_t vf = as_bf16x8(u32x4_t{l2[0], l2[1], h2[0], h2[1]});
             st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], st.o[db], 0, 0, 0);
         }
     }
+}
+
+// Tile rows past nvalid get -inf.
+__device__ __forceinline__ void mask_rows(f32x16_t x[2], int nvalid, int half)
+{
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int kt = kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+            x[kb][i] = kt < nvalid ? x[kb][i] : -__builtin_inff();
+        }
+}
+
+// Source rows of the exact tile starting at list position v0, for thread p < 64:
+// walk the routed segments from the cursor (si, off) = position v0.
+__device__ __forceinline__ int key_of(const int2* __restrict__ sl, int ns, int si, int off, int p,
+                                      int fallback)
+{
+    int o = off + p;
+    while (si < ns) {
+        const int2 sg = sl[si];
+        if (o < sg.y) return sg.x + o;
+        o -= sg.y;
+        ++si;
+    }
+    return fallback;
 }
 
 // ----------------------------------------------------------------------------- main kernel
@@ -278,18 +310,25 @@ __global__ __launch_bounds__(AT_THREADS, 2) void k_attn_mfma(
     const bf16* __restrict__ Qp, const int32_t* __restrict__ offsets_q,
     const int32_t* __restrict__ perm_q, const bf16* __restrict__ Kp, const bf16* __restrict__ Vp,
     const bf16* __restrict__ kbh, const bf16* __restrict__ kbl, const bf16* __restrict__ vbh,
-    const bf16* __restrict__ vbl, const float* __restrict__ logm2, const uint8_t* __restrict__ mask,
-    const int2* __restrict__ segs, const int* __restrict__ nsegs, const int* __restrict__ tstart,
-    int Nq, int Nk, int Cq, int Ck, float scale2, bf16* __restrict__ O)
+    const bf16* __restrict__ vbl, const float* __restrict__ logm2, const int2* __restrict__ segs,
+    const int* __restrict__ nsegs, const int* __restrict__ nkeys, const int* __restrict__ comp,
+    const int* __restrict__ ncomp, const int* __restrict__ tstart, int H, int Nq, int Nk, int Cq,
+    int Ck, int tiles_per_head, int grid_per_xcd, float scale2, bf16* __restrict__ O)
 {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     char* const kbuf0 = smem;
     char* const vbuf0 = smem + 2 * K_BUF;
-    float* s_bias = (float*)(smem + 2 * K_BUF + 2 * V_BUF);
+    float* const s_bias = (float*)(smem + 2 * K_BUF + 2 * V_BUF);
+    int* const s_map = (int*)(smem + 2 * K_BUF + 2 * V_BUF + AT_BN * 4);  // [2][64]
+    int* const s_cur = s_map + 2 * AT_BN;                                  // cursor (si, off)
 #define KBUF(b) (kbuf0 + (b) * K_BUF)
 #define VBUF(b) (vbuf0 + (b) * V_BUF)
 
-    const int h = blockIdx.y, t = blockIdx.x;
+    // XCD-aware order: logical tile = XCD-major position of this workgroup.
+    const int p = blockIdx.x;
+    const int logical = (p % AT_XCD) * grid_per_xcd + p / AT_XCD;
+    if (logical >= tiles_per_head * H) return;
+    const int h = logical / tiles_per_head, t = logical - h * tiles_per_head;
     const int* ts = tstart + (size_t)h * (Cq + 1);
     if (t >= ts[Cq]) return;
     int lo = 0, hi = Cq - 1;  // query cluster: last c with ts[c] <= t
@@ -321,85 +360,102 @@ __global__ __launch_bounds__(AT_THREADS, 2) void k_attn_mfma(
 #pragma unroll
     for (int db = 0; db < 4; ++db) st.o[db] = f32x16_t{0};
 
-    const uint8_t* mrow = mask + ((size_t)h * Cq + c) * Ck;
+    const size_t hc = (size_t)h * Cq + c;
     const float* lm = logm2 + (size_t)h * Ck;
 
-    // 1. compensation tiles
-    for (int g0 = 0; g0 < Ck; g0 += AT_BN) {
-        const int nv = min(AT_BN, Ck - g0);
-        float b = -__builtin_inff();
-        if (tid < AT_BN && tid < nv && !mrow[g0 + tid]) b = lm[g0 + tid];
-        if (!__syncthreads_or(b != -__builtin_inff())) continue;
-        if (tid < AT_BN) s_bias[tid] = b;
-        Stage sh, sl;
-        const size_t cb = ((size_t)h * Ck + g0) * AT_D;
-        stage_load(sh, kbh + cb, vbh + cb, nv, tid);
-        stage_load(sl, kbl + cb, vbl + cb, nv, tid);
-        stage_store(sh, KBUF(0), VBUF(0), tid);
-        stage_store(sl, KBUF(1), VBUF(1), tid);
-        __syncthreads();
-        f32x16_t acc[2];
-        tile_scores(acc, KBUF(0), qf, lane);
-        tile_scores_acc(acc, KBUF(1), qf, lane);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int kt = kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-                acc[kb][i] = fmaf(acc[kb][i], scale2, s_bias[kt]);
+    // 1. compensation tiles: packed list of skipped non-empty key clusters
+    {
+        const int nc = ncomp[hc];
+        const int* cl = comp + hc * Ck;
+        const size_t pb = (size_t)h * Ck * AT_D;
+        for (int v0 = 0; v0 < nc; v0 += AT_BN) {
+            const int nv = min(AT_BN, nc - v0);
+            if (tid < AT_BN) {
+                const int g = cl[v0 + (tid < nv ? tid : 0)];
+                s_map[tid] = g;
+                s_bias[tid] = tid < nv ? lm[g] : -__builtin_inff();
             }
-        bf16x8_t pf[4];
-        softmax_update(st, acc, pf);
-        tile_pv(st, VBUF(0), pf, lane);
-        tile_pv(st, VBUF(1), pf, lane);
-        __syncthreads();
-    }
-
-    // 2. exact tiles, double-buffered
-    const int ns = nsegs[(size_t)h * Cq + c];
-    const int2* sl = segs + ((size_t)h * Cq + c) * Ck;
-    const bf16* Kh = Kp + (size_t)h * Nk * AT_D;
-    const bf16* Vh = Vp + (size_t)h * Nk * AT_D;
-    if (ns > 0) {
-        int si = 0, off = 0;
-        int2 sg = sl[0];
-        int cur_start = sg.x, cur_n = min(AT_BN, sg.y);
-        Stage sbuf;
-        stage_load(sbuf, Kh + (size_t)cur_start * AT_D, Vh + (size_t)cur_start * AT_D, cur_n, tid);
-        stage_store(sbuf, KBUF(0), VBUF(0), tid);
-        __syncthreads();
-        int buf = 0;
-        while (true) {
-            // advance to the next tile
-            off += AT_BN;
-            if (off >= sg.y) {
-                ++si;
-                off = 0;
-                if (si < ns) sg = sl[si];
-            }
-            const bool has_next = si < ns;
-            const int nxt_start = sg.x + off;
-            const int nxt_n = has_next ? min(AT_BN, sg.y - off) : 0;
-            if (has_next)
-                stage_load(sbuf, Kh + (size_t)nxt_start * AT_D, Vh + (size_t)nxt_start * AT_D, nxt_n,
-                           tid);
-            f32x16_t acc[2];
-            tile_scores(acc, KBUF(buf), qf, lane);
+            __syncthreads();
+            Stage sh, sl;
+            stage_load(sh, kbh + pb, vbh + pb, s_map, tid);
+            stage_load(sl, kbl + pb, vbl + pb, s_map, tid);
+            stage_store(sh, KBUF(0), VBUF(0), tid);
+            stage_store(sl, KBUF(1), VBUF(1), tid);
+            __syncthreads();
+            f32x16_t acc[2] = {f32x16_t{0}, f32x16_t{0}};
+            tile_scores(acc, KBUF(0), qf, lane);
+            tile_scores(acc, KBUF(1), qf, lane);
+            // logit = acc * scale2 + bias: fold the bias in as acc + bias / scale2
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int kt = kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-                    acc[kb][i] = kt < cur_n ? acc[kb][i] * scale2 : -__builtin_inff();
+                    acc[kb][i] = fmaf(s_bias[kt], 1.0f / scale2, acc[kb][i]);
                 }
             bf16x8_t pf[4];
-            softmax_update(st, acc, pf);
+            softmax_update(st, acc, scale2, pf);
+            tile_pv(st, VBUF(0), pf, lane);
+            tile_pv(st, VBUF(1), pf, lane);
+            __syncthreads();
+        }
+    }
+
+    // 2. exact tiles (packed routed keys), double-buffered
+    const int nk = nkeys[hc];
+    if (nk > 0) {
+        const int ns = nsegs[hc];
+        const int2* sl = segs + hc * Ck;
+        const bf16* Kh = Kp + (size_t)h * Nk * AT_D;
+        const bf16* Vh = Vp + (size_t)h * Nk * AT_D;
+        const int first = sl[0].x;
+        const int ntiles = (nk + AT_BN - 1) / AT_BN;
+        // maps of tiles 0 and 1, cursor at tile 2
+        if (tid < AT_BN) {
+            s_map[tid] = key_of(sl, ns, 0, 0, tid, first);
+            s_map[AT_BN + tid] = key_of(sl, ns, 0, 0, AT_BN + tid, first);
+        }
+        if (tid == 0) {
+            int si = 0, o = 2 * AT_BN;
+            while (si < ns && o >= sl[si].y) {
+                o -= sl[si].y;
+                ++si;
+            }
+            s_cur[0] = si;
+            s_cur[1] = o;
+        }
+        __syncthreads();
+        Stage sbuf;
+        stage_load(sbuf, Kh, Vh, s_map, tid);
+        stage_store(sbuf, KBUF(0), VBUF(0), tid);
+        __syncthreads();
+        for (int it = 0; it < ntiles; ++it) {
+            const int buf = it & 1;
+            const bool has_next = it + 1 < ntiles;
+            if (has_next) stage_load(sbuf, Kh, Vh, s_map + (buf ^ 1) * AT_BN, tid);
+            f32x16_t acc[2] = {f32x16_t{0}, f32x16_t{0}};
+            tile_scores(acc, KBUF(buf), qf, lane);
+            const int nvalid = nk - it * AT_BN;
+            if (nvalid < AT_BN) mask_rows(acc, nvalid, half);
+            bf16x8_t pf[4];
+            softmax_update(st, acc, scale2, pf);
             tile_pv(st, VBUF(buf), pf, lane);
             if (!has_next) break;
             stage_store(sbuf, KBUF(buf ^ 1), VBUF(buf ^ 1), tid);
+            // map of tile it + 2 into the slot tile it used
+            const int si = s_cur[0], off = s_cur[1];
             __syncthreads();
-            buf ^= 1;
-            cur_n = nxt_n;
+            if (tid < AT_BN) s_map[buf * AT_BN + tid] = key_of(sl, ns, si, off, tid, first);
+            if (tid == 0) {
+                int s2 = si, o = off + AT_BN;
+                while (s2 < ns && o >= sl[s2].y) {
+                    o -= sl[s2].y;
+                    ++s2;
+                }
+                s_cur[0] = s2;
+                s_cur[1] = o;
+            }
+            __syncthreads();
         }
     }
 
@@ -407,8 +463,6 @@ __global__ __launch_bounds__(AT_THREADS, 2) void k_attn_mfma(
     const float ltot = st.l + __shfl_xor(st.l, 32);
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     __syncthreads();
-#undef KBUF
-#undef VBUF
     char* ost = smem;  // 128 rows x K_PITCH bytes = 2 K buffers
     {
         const int r = wave * 32 + qcol;
@@ -435,6 +489,8 @@ __global__ __launch_bounds__(AT_THREADS, 2) void k_attn_mfma(
                 *(const u32x4_t*)(ost + r * K_PITCH + ch * 16);
         }
     }
+#undef KBUF
+#undef VBUF
 }
 
 // ----------------------------------------------------------------------------- dispatch
@@ -457,17 +513,23 @@ SVG_HIDDEN hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t st)
     int* tstart = (int*)(s + L.at_tiles);
     int2* segs = (int2*)(s + L.at_segs);
     int* nsegs = (int*)(s + L.at_nsegs);
+    int* nkeys = (int*)(s + L.at_nkeys);
+    int* comp = (int*)(s + L.at_comp);
+    int* ncomp = (int*)(s + L.at_ncomp);
     hipLaunchKernelGGL(k_comp_planes, dim3(a.Ck, a.H), dim3(AT_D), 0, st, a.kbar, a.vbar, a.counts_k,
                        a.Ck, kbh, kbl, vbh, vbl, logm2);
     hipLaunchKernelGGL(k_seg_list, dim3(a.Cq, a.H), dim3(256), 0, st, a.mask, a.offsets_k, a.Cq,
-                       a.Ck, segs, nsegs);
+                       a.Ck, segs, nsegs, nkeys, comp, ncomp);
     hipLaunchKernelGGL(k_tile_prefix, dim3(a.H), dim3(1024), 0, st, a.offsets_q, a.Cq, tstart);
-    const int max_tiles = (a.Nq + AT_BM - 1) / AT_BM + a.Cq;
+    const int tiles_per_head = (a.Nq + AT_BM - 1) / AT_BM + a.Cq;
+    const long total = (long)tiles_per_head * a.H;
+    const int per_xcd = (int)((total + AT_XCD - 1) / AT_XCD);
     const float scale2 = (float)(1.4426950408889634 / sqrt((double)AT_D));
-    hipLaunchKernelGGL(k_attn_mfma, dim3(max_tiles, a.H), dim3(AT_THREADS), AT_LDS, st,
+    hipLaunchKernelGGL(k_attn_mfma, dim3(per_xcd * AT_XCD), dim3(AT_THREADS), AT_LDS, st,
                        (const bf16*)a.Qp, a.offsets_q, a.perm_q, (const bf16*)a.Kp,
-                       (const bf16*)a.Vp, kbh, kbl, vbh, vbl, logm2, a.mask, segs, nsegs, tstart,
-                       a.Nq, a.Nk, a.Cq, a.Ck, scale2, (bf16*)a.O);
+                       (const bf16*)a.Vp, kbh, kbl, vbh, vbl, logm2, segs, nsegs, nkeys, comp, ncomp,
+                       tstart, a.H, a.Nq, a.Nk, a.Cq, a.Ck, tiles_per_head, per_xcd, scale2,
+                       (bf16*)a.O);
     return hipGetLastError();
 }
 

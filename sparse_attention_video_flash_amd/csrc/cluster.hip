@@ -7,8 +7,9 @@
 // Euclidean distance with ties to the lowest index.  Centroids are kept in fp64
 // and are the exact member means: member rows are summed as 64-bit fixed-point
 // integers (every bf16/fp32 input with |x| < 256 and magnitude above 2^-S is an
-// exact multiple of 2^-S), so the sum is order-independent and integer atomics
-// keep it deterministic; one rounding to fp64 and one fp64 division follow.
+// exact multiple of 2^-S), so the sum does not depend on the order of the rows;
+// one rounding to fp64 and one fp64 division follow.  Each update buckets the
+// token ids by label and one block per cluster sums its rows (no atomics).
 // Distances are either evaluated directly in fp64 (generic kernel) or screened
 // with bf16 MFMA and re-evaluated in fp64 whenever the screen cannot separate
 // the best two candidates (assign_mfma.hip).
@@ -92,84 +93,6 @@ __global__ __launch_bounds__(256) void k_assign_exact(const T* __restrict__ X,
     if (i < N) labels[(size_t)h * N + i] = bi;
 }
 
-// Exact member sums.  Each wave walks 64 consecutive tokens; a run of equal
-// labels is accumulated in 64-bit fixed point (scale 2^shift) and flushed with
-// one integer atomic per coordinate, plus the run length into the count.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void k_fixed_sums(const T* __restrict__ X,
-                                                    const int32_t* __restrict__ labels, int N,
-                                                    int C, int shift,
-                                                    unsigned long long* __restrict__ sums,
-                                                    int* __restrict__ cnt, int* __restrict__ err)
-{
-    constexpr int EPL = D / 64;
-    const int h = blockIdx.y;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int i0 = (blockIdx.x * 4 + wave) * 64;
-    if (i0 >= N) return;
-    const int i1 = min(i0 + 64, N);
-    const double scale = ldexp(1.0, shift);
-    const int32_t* lab = labels + (size_t)h * N;
-    long long acc[EPL];
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = 0;
-    int cur = lab[i0], run = 0;
-    auto flush = [&]() {
-        if (cur >= 0 && cur < C) {
-            unsigned long long* s = sums + ((size_t)h * C + cur) * D + lane * EPL;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) atomicAdd(s + e, (unsigned long long)acc[e]);
-            if (lane == 0) atomicAdd(cnt + (size_t)h * C + cur, run);
-        } else if (lane == 0) {
-            atomicOr(err, ERR_LABEL);
-        }
-    };
-    for (int i = i0; i < i1; ++i) {
-        const int l = lab[i];
-        if (l != cur) {
-            flush();
-            cur = l;
-            run = 0;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[e] = 0;
-        }
-        const T* x = X + ((size_t)h * N + i) * D + lane * EPL;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] += (long long)((double)to_f32<T>(x[e]) * scale);
-        ++run;
-    }
-    flush();
-}
-
-// Centroid = exact sum / count in fp64; an empty cluster keeps its centroid
-// (k-means) or becomes zero (plain means).  Optionally writes fp32 copies and
-// the counts; then clears the sums and counts for the next pass.
-__global__ void k_finalize_means(unsigned long long* __restrict__ sums, int* __restrict__ cnt,
-                                 int d, int C, int shift, int zero_empty, double* __restrict__ cent64,
-                                 float* __restrict__ cent_out)
-{
-    const int m = blockIdx.x, h = blockIdx.y;
-    const size_t row = (size_t)h * C + m;
-    const int n = cnt[row];
-    const double inv_scale = ldexp(1.0, -shift);
-    for (int t = threadIdx.x; t < d; t += blockDim.x) {
-        double c;
-        if (n > 0) {
-            c = ((double)(long long)sums[row * d + t] * inv_scale) / (double)n;
-            cent64[row * d + t] = c;
-        } else if (zero_empty) {
-            c = 0.0;
-            cent64[row * d + t] = c;
-        } else {
-            c = cent64[row * d + t];
-        }
-        if (cent_out) cent_out[row * d + t] = (float)c;
-        sums[row * d + t] = 0ull;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) cnt[row] = 0;
-}
-
 // ----------------------------------------------------------------------------- counting sort
 
 // Per-tile label histogram (tiles of kTile consecutive tokens).
@@ -195,26 +118,47 @@ __global__ __launch_bounds__(256) void k_tile_hist(const int32_t* __restrict__ l
     for (int c = threadIdx.x; c < C; c += 256) out[c] = s_h[c];
 }
 
-// Per head: exclusive prefix of every label's tile counts (in place), the
-// label counts, and their exclusive prefix (cluster offsets).
-__global__ __launch_bounds__(1024) void k_hist_scan(int* __restrict__ hist, int C, int ntiles,
-                                                    int32_t* __restrict__ counts,
-                                                    int32_t* __restrict__ offsets)
+// Per-label exclusive prefix of the tile counts, in place, and the label
+// counts.  One block per 32 labels of a head; tiles are staged through LDS 64 at
+// a time so the loads of a chunk are issued together.
+constexpr int HC_L = 32, HC_T = 64;
+__global__ __launch_bounds__(256) void k_hist_cols(int* __restrict__ hist, int C, int ntiles,
+                                                   int32_t* __restrict__ counts)
+{
+    __shared__ int s_t[HC_T][HC_L + 1];
+    const int h = blockIdx.y, l0 = blockIdx.x * HC_L;
+    const int lab = threadIdx.x & (HC_L - 1), tr = threadIdx.x / HC_L;  // 8 tile rows per pass
+    int* hb = hist + (size_t)h * ntiles * C;
+    int run = 0;
+    for (int t0 = 0; t0 < ntiles; t0 += HC_T) {
+        const int tn = min(HC_T, ntiles - t0);
+        for (int t = tr; t < tn; t += 256 / HC_L)
+            s_t[t][lab] = (l0 + lab < C) ? hb[(size_t)(t0 + t) * C + l0 + lab] : 0;
+        __syncthreads();
+        if (threadIdx.x < HC_L) {
+            for (int t = 0; t < tn; ++t) {
+                const int v = s_t[t][lab];
+                s_t[t][lab] = run;
+                run += v;
+            }
+        }
+        __syncthreads();
+        for (int t = tr; t < tn; t += 256 / HC_L)
+            if (l0 + lab < C) hb[(size_t)(t0 + t) * C + l0 + lab] = s_t[t][lab];
+        __syncthreads();
+    }
+    if (threadIdx.x < HC_L && l0 + lab < C) counts[(size_t)h * C + l0 + lab] = run;
+}
+
+// Per head: cluster offsets = exclusive prefix of the counts.  Also clears the
+// per-head words the next k-means iteration accumulates into (stats, nflag).
+__global__ __launch_bounds__(1024) void k_count_scan(const int32_t* __restrict__ counts, int C,
+                                                     int32_t* __restrict__ offsets,
+                                                     unsigned* __restrict__ stats,
+                                                     int* __restrict__ nflag)
 {
     __shared__ int s_part[1024];
     const int h = blockIdx.x;
-    int* hb = hist + (size_t)h * ntiles * C;
-    for (int c = threadIdx.x; c < C; c += 1024) {
-        int run = 0;
-        for (int t = 0; t < ntiles; ++t) {
-            int v = hb[(size_t)t * C + c];
-            hb[(size_t)t * C + c] = run;
-            run += v;
-        }
-        counts[(size_t)h * C + c] = run;
-    }
-    __syncthreads();
-    // exclusive scan of counts[h, 0..C): each thread owns a contiguous chunk
     const int per = (C + 1023) / 1024;
     const int c0 = threadIdx.x * per;
     int local = 0;
@@ -236,6 +180,193 @@ __global__ __launch_bounds__(1024) void k_hist_scan(int* __restrict__ hist, int 
         }
     }
     if (threadIdx.x == 1023) offsets[(size_t)h * (C + 1) + C] = s_part[1023];
+    if (stats && threadIdx.x < 4) stats[4 * h + threadIdx.x] = 0u;
+    if (nflag && threadIdx.x == 0) nflag[h] = 0;
+}
+
+// Unstable bucket fill: every token goes to its cluster's range (order within a
+// cluster does not matter to the exact sums).  Ranks inside a tile come from
+// LDS atomics.
+__global__ __launch_bounds__(256) void k_bucket(const int32_t* __restrict__ labels, int N, int C,
+                                                int ntiles, const int* __restrict__ hist,
+                                                const int32_t* __restrict__ offsets,
+                                                int32_t* __restrict__ perm)
+{
+    extern __shared__ int s_r[];
+    const int tile = blockIdx.x, h = blockIdx.y;
+    for (int c = threadIdx.x; c < C; c += 256) s_r[c] = 0;
+    __syncthreads();
+    const int i = tile * kTile + threadIdx.x;
+    if (i < N) {
+        const int l = labels[(size_t)h * N + i];
+        if (l >= 0 && l < C) {
+            const int rank = atomicAdd(&s_r[l], 1);
+            const int pos =
+                offsets[(size_t)h * (C + 1) + l] + hist[((size_t)h * ntiles + tile) * C + l] + rank;
+            perm[(size_t)h * N + pos] = i;
+        }
+    }
+}
+
+// Cluster means from exact fixed-point sums.  The bucketed token order is cut
+// into chunks of MC_ROWS positions, one block each; a block sums the rows of
+// every cluster segment in its chunk as 64-bit integers (scale 2^shift) and adds
+// them to the cluster's running sums with integer atomics (exact, so the order
+// does not matter).  k_cluster_finalize then turns the sums into means.
+constexpr int MC_ROWS = 512;
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_cluster_chunks(const T* __restrict__ X,
+                                                        const int32_t* __restrict__ perm,
+                                                        const int32_t* __restrict__ offsets, int N,
+                                                        int C, int shift,
+                                                        unsigned long long* __restrict__ sums)
+{
+    constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+    constexpr int CPR = D / EPC;               // chunks per row
+    constexpr int RPP = 256 / CPR;             // rows per pass
+    __shared__ long long s_sum[RPP][D];
+    __shared__ int s_idx[MC_ROWS];
+    const int h = blockIdx.y;
+    const int p0 = blockIdx.x * MC_ROWS;
+    if (p0 >= N) return;
+    const int p1 = min(N, p0 + MC_ROWS);
+    const int32_t* oh = offsets + (size_t)h * (C + 1);
+    const int ch = threadIdx.x % CPR, rg = threadIdx.x / CPR;
+    const T* Xh = X + (size_t)h * N * D + ch * EPC;
+    for (int k = threadIdx.x; k < p1 - p0; k += 256) s_idx[k] = perm[(size_t)h * N + p0 + k];
+    // first cluster whose range ends after p0
+    int lo_c = 0, hi_c = C - 1;
+    while (lo_c < hi_c) {
+        const int mid = (lo_c + hi_c) >> 1;
+        if (oh[mid + 1] > p0) hi_c = mid; else lo_c = mid + 1;
+    }
+    __syncthreads();
+    for (int m = lo_c; m < C && oh[m] < p1; ++m) {
+        const int a0 = max(oh[m], p0) - p0, a1 = min(oh[m + 1], p1) - p0;
+        if (a1 <= a0) continue;
+        long long acc[EPC];
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[e] = 0;
+        int j = a0 + rg;
+        for (; j + 3 * RPP < a1; j += 4 * RPP) {
+            uint4 w[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) w[u] = *(const uint4*)(Xh + (size_t)s_idx[j + u * RPP] * D);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const T* v = (const T*)&w[u];
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) acc[e] += to_fixed<T>(v[e], shift);
+            }
+        }
+        for (; j < a1; j += RPP) {
+            const uint4 w0 = *(const uint4*)(Xh + (size_t)s_idx[j] * D);
+            const T* v0 = (const T*)&w0;
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) acc[e] += to_fixed<T>(v0[e], shift);
+        }
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) s_sum[rg][ch * EPC + e] = acc[e];
+        __syncthreads();
+        if ((int)threadIdx.x < D) {
+            long long tot = 0;
+#pragma unroll
+            for (int g = 0; g < RPP; ++g) tot += s_sum[g][threadIdx.x];
+            atomicAdd(sums + ((size_t)h * C + m) * D + threadIdx.x, (unsigned long long)tot);
+        }
+        __syncthreads();
+    }
+}
+
+// centroid = (double)sum * 2^-shift / count for every non-empty cluster (one
+// wave per cluster); an empty cluster keeps its centroid (k-means) or becomes
+// zero (plain means).  Optionally writes an fp32 copy; with PLANES also the
+// bf16 hi/lo planes, ||c||^2 (fp32, fp64) and the split residual norm that the
+// MFMA screen of the next assignment needs.  Clears the sums for the next pass.
+template <int D, bool PLANES>
+__global__ __launch_bounds__(256) void k_cluster_finalize(
+    const int32_t* __restrict__ counts, int C, int shift, int zero_empty,
+    unsigned long long* __restrict__ sums, double* __restrict__ cent64, float* __restrict__ cent_out,
+    bf16* __restrict__ hi, bf16* __restrict__ lo, float* __restrict__ cn32,
+    double* __restrict__ cn64, float* __restrict__ resid)
+{
+    constexpr int EPL = D / 64;
+    const int h = blockIdx.y;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const double inv_scale = ldexp(1.0, -shift);
+    for (int m = blockIdx.x * 4 + wave; m < C; m += gridDim.x * 4) {
+        const size_t row = (size_t)h * C + m;
+        const int n = counts[row];
+        double a2 = 0.0, r2s = 0.0;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            const size_t i = row * D + lane * EPL + e;
+            double c;
+            if (n > 0) {
+                c = ((double)(long long)sums[i] * inv_scale) / (double)n;
+                cent64[i] = c;
+                sums[i] = 0ull;
+            } else if (zero_empty) {
+                c = 0.0;
+                cent64[i] = c;
+            } else {
+                c = cent64[i];
+            }
+            if (cent_out) cent_out[i] = (float)c;
+            if constexpr (PLANES) {
+                const bf16 chh = f32_to_bf16((float)c);
+                const double r1 = c - (double)bf16_to_f32(chh);
+                const bf16 cl = f32_to_bf16((float)r1);
+                const double r2 = r1 - (double)bf16_to_f32(cl);
+                hi[i] = chh;
+                lo[i] = cl;
+                a2 = fma(c, c, a2);
+                r2s = fma(r2, r2, r2s);
+            }
+        }
+        if constexpr (PLANES) {
+            for (int o = 32; o >= 1; o >>= 1) {
+                a2 += __shfl_xor(a2, o);
+                r2s += __shfl_xor(r2s, o);
+            }
+            if (lane == 0) {
+                cn64[row] = a2;
+                cn32[row] = (float)a2;
+                resid[row] = (float)(sqrt(r2s) * (1.0 + 1e-6));
+            }
+        }
+    }
+}
+
+// Per-head maxima, over all clusters, of the split residual and of ||c|| (the
+// bounds of the next MFMA screen).
+__global__ __launch_bounds__(256) void k_plane_stats(int C, const double* __restrict__ cn64,
+                                                     const float* __restrict__ resid,
+                                                     unsigned* __restrict__ stats)
+{
+    __shared__ float s_r[256], s_c[256];
+    const int h = blockIdx.x;
+    float rmax = 0.f, cmax = 0.f;
+    for (int m = threadIdx.x; m < C; m += 256) {
+        const size_t row = (size_t)h * C + m;
+        rmax = fmaxf(rmax, resid[row]);
+        cmax = fmaxf(cmax, (float)(sqrt(cn64[row]) * (1.0 + 1e-6)));
+    }
+    s_r[threadIdx.x] = rmax;
+    s_c[threadIdx.x] = cmax;
+    __syncthreads();
+    for (int o = 128; o >= 1; o >>= 1) {
+        if ((int)threadIdx.x < o) {
+            s_r[threadIdx.x] = fmaxf(s_r[threadIdx.x], s_r[threadIdx.x + o]);
+            s_c[threadIdx.x] = fmaxf(s_c[threadIdx.x], s_c[threadIdx.x + o]);
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        stats[4 * h + 0] = __float_as_uint(s_r[0]);
+        stats[4 * h + 1] = __float_as_uint(s_c[0]);
+    }
 }
 
 // Stable scatter: position = offset of the label + tokens of that label in
@@ -286,8 +417,20 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ lab
 
 // ----------------------------------------------------------------------------- driver
 
-SVG_HIDDEN hipError_t launch_assign_mfma(const ClusterArgs& a, const double* cent64, int* err,
-                                         hipStream_t st);
+struct KmPlanes {
+    bf16* hi;
+    bf16* lo;
+    float* cn32;
+    double* cn64;
+    unsigned* stats;
+    int32_t* flags;
+    int* nflag;
+};
+SVG_HIDDEN KmPlanes km_planes(const ClusterArgs& a);
+SVG_HIDDEN hipError_t launch_km_prep(const ClusterArgs& a, const double* cent64, const KmPlanes& P,
+                                     hipStream_t st);
+SVG_HIDDEN hipError_t launch_assign_mfma(const ClusterArgs& a, const double* cent64,
+                                         const KmPlanes& P, hipStream_t st);
 SVG_HIDDEN bool assign_mfma_supported(const ClusterArgs& a);
 
 template <typename T, int D>
@@ -297,60 +440,82 @@ static hipError_t run_cluster(const ClusterArgs& a, hipStream_t st)
     char* s = a.scratch;
     int* err = (int*)(s + L.cl_err);
     double* cent64 = (double*)(s + L.cl_cent64);
-    unsigned long long* sums = (unsigned long long*)(s + L.cl_sums);
-    int* cnt = (int*)(s + L.cl_cnt);
     int* hist = (int*)(s + L.cl_hist);
+    int32_t* pwork = (int32_t*)(s + L.cl_perm);
     const int H = a.H, N = a.N, C = a.C;
     const T* X = (const T*)a.X;
-    const dim3 grid_sums((N + 255) / 256, H), grid_cent(C, H);
-    const int cthreads = D;
-
+    const int ntiles = (N + kTile - 1) / kTile;
+    const dim3 gtiles(ntiles, H), gcent(C, H), gcols((C + HC_L - 1) / HC_L, H);
+    const bool mfma = assign_mfma_supported(a);
+    const KmPlanes P = km_planes(a);
+    unsigned long long* sums = (unsigned long long*)(s + L.cl_sums);
+    float* resid = (float*)(s + L.cl_resid);
+    const dim3 gchunks((N + MC_ROWS - 1) / MC_ROWS, H), gfin((C + 3) / 4 < 64 ? (C + 3) / 4 : 64, H);
     zero_words(sums, (size_t)H * C * D * 8, st);
-    zero_words(cnt, (size_t)H * C * 4, st);
+    // plain mean pass (no planes)
+    auto mean_pass = [&](const T* src, const int32_t* order, int zero_empty, float* out) {
+        hipLaunchKernelGGL((k_cluster_chunks<T, D>), gchunks, dim3(256), 0, st, src, order, a.offsets,
+                           N, C, a.shift, sums);
+        hipLaunchKernelGGL((k_cluster_finalize<D, false>), gfin, dim3(256), 0, st, a.counts, C,
+                           a.shift, zero_empty, sums, cent64, out, (bf16*)nullptr, (bf16*)nullptr,
+                           (float*)nullptr, (double*)nullptr, (float*)nullptr);
+    };
+
+    // counting-sort front half: tile histograms, per-label tile prefixes, counts, offsets
+    auto sort_front = [&](unsigned* stats, int* nflag) {
+        hipLaunchKernelGGL(k_tile_hist, gtiles, dim3(256), (size_t)C * 4, st, a.labels, N, C,
+                           ntiles, hist, err);
+        hipLaunchKernelGGL(k_hist_cols, gcols, dim3(256), 0, st, hist, C, ntiles, a.counts);
+        hipLaunchKernelGGL(k_count_scan, dim3(H), dim3(1024), 0, st, a.counts, C, a.offsets, stats,
+                           nflag);
+    };
 
     if (!(a.flags & SVGEAR_LABELS_GIVEN)) {
-        hipLaunchKernelGGL((k_init_centroids<T>), grid_cent, dim3(cthreads), 0, st, X, a.init, N,
-                           D, C, cent64, err);
-        const bool mfma = assign_mfma_supported(a);
+        hipLaunchKernelGGL((k_init_centroids<T>), gcent, dim3(D), 0, st, X, a.init, N, D, C, cent64,
+                           err);
+        if (mfma) {
+            zero_words(P.stats, (size_t)H * 16, st);
+            zero_words(P.nflag, (size_t)H * 4, st);
+            hipError_t e = launch_km_prep(a, cent64, P, st);
+            if (e != hipSuccess) return e;
+        }
         for (int it = 0; it < a.iters; ++it) {
             if (mfma) {
-                hipError_t e = launch_assign_mfma(a, cent64, err, st);
+                hipError_t e = launch_assign_mfma(a, cent64, P, st);
                 if (e != hipSuccess) return e;
             } else {
                 hipLaunchKernelGGL((k_assign_exact<T, D>), dim3((N + 255) / 256, H), dim3(256), 0,
                                    st, X, cent64, N, C, a.labels);
             }
-            hipLaunchKernelGGL((k_fixed_sums<T, D>), grid_sums, dim3(256), 0, st, X, a.labels, N, C,
-                               a.shift, sums, cnt, err);
-            const bool last = it == a.iters - 1;
-            hipLaunchKernelGGL(k_finalize_means, grid_cent, dim3(cthreads), 0, st, sums, cnt, D, C,
-                               a.shift, 0, cent64, last ? a.cent : (float*)nullptr);
+            if (it == a.iters - 1) break;
+            // update: unstable bucket order + exact per-cluster means (and next planes)
+            sort_front(nullptr, mfma ? P.nflag : nullptr);
+            hipLaunchKernelGGL(k_bucket, gtiles, dim3(256), (size_t)C * 4, st, a.labels, N, C,
+                               ntiles, hist, a.offsets, pwork);
+            if (mfma && D == 128) {
+                hipLaunchKernelGGL((k_cluster_chunks<T, D>), gchunks, dim3(256), 0, st, X, pwork,
+                                   a.offsets, N, C, a.shift, sums);
+                hipLaunchKernelGGL((k_cluster_finalize<D, D == 128>), gfin, dim3(256), 0, st, a.counts,
+                                   C, a.shift, 0, sums, cent64, (float*)nullptr, P.hi, P.lo, P.cn32,
+                                   P.cn64, resid);
+                hipLaunchKernelGGL(k_plane_stats, dim3(H), dim3(256), 0, st, C, P.cn64, resid,
+                                   P.stats);
+            } else {
+                mean_pass(X, pwork, 0, (float*)nullptr);
+            }
         }
-    } else {
-        hipLaunchKernelGGL((k_fixed_sums<T, D>), grid_sums, dim3(256), 0, st, X, a.labels, N, C,
-                           a.shift, sums, cnt, err);
-        hipLaunchKernelGGL(k_finalize_means, grid_cent, dim3(cthreads), 0, st, sums, cnt, D, C,
-                           a.shift, 1, cent64, a.cent);
     }
 
-    // Reorder (stable counting sort) and gather rows.
-    const int ntiles = (N + kTile - 1) / kTile;
-    hipLaunchKernelGGL(k_tile_hist, dim3(ntiles, H), dim3(256), (size_t)C * 4, st, a.labels, N, C,
-                       ntiles, hist, err);
-    hipLaunchKernelGGL(k_hist_scan, dim3(H), dim3(1024), 0, st, hist, C, ntiles, a.counts,
-                       a.offsets);
+    // Final reorder (stable counting sort), rows gathered, means of the final labels.
+    sort_front(nullptr, nullptr);
     const int row_chunks = (int)(D * sizeof(T) / 16);
-    hipLaunchKernelGGL(k_scatter, dim3(ntiles, H), dim3(256), 0, st, a.labels, N, C, ntiles, hist,
-                       a.offsets, a.perm, a.inv_perm, (const uint4*)a.X, (uint4*)a.Xp,
-                       (const uint4*)a.V, (uint4*)a.Vp, row_chunks);
-
-    // V-bar: mean of V over the key clusters (zero for an empty cluster).
-    if (a.side == 1) {
-        hipLaunchKernelGGL((k_fixed_sums<T, D>), grid_sums, dim3(256), 0, st, (const T*)a.V,
-                           a.labels, N, C, a.shift, sums, cnt, err);
-        hipLaunchKernelGGL(k_finalize_means, grid_cent, dim3(cthreads), 0, st, sums, cnt, D, C,
-                           a.shift, 1, cent64, a.vbar);
-    }
+    hipLaunchKernelGGL(k_scatter, gtiles, dim3(256), 0, st, a.labels, N, C, ntiles, hist, a.offsets,
+                       a.perm, a.inv_perm, (const uint4*)a.X, (uint4*)a.Xp, (const uint4*)a.V,
+                       (uint4*)a.Vp, row_chunks);
+    mean_pass(X, a.perm, (a.flags & SVGEAR_LABELS_GIVEN) ? 1 : 0, a.cent);
+    // V-bar: mean of V over the key clusters (zero for an empty cluster).  cent64
+    // is no longer needed and serves as scratch.
+    if (a.side == 1) mean_pass((const T*)a.V, a.perm, 1, a.vbar);
     return hipGetLastError();
 }
 

@@ -36,6 +36,31 @@ template <typename T> __device__ __forceinline__ float to_f32(T x);
 template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ float to_f32<bf16>(bf16 x) { return bf16_to_f32(x); }
 
+// Exact fixed-point image of an input value: trunc(x * 2^S) as a 64-bit integer
+// (equal to (long long)((double)x * 2^S) for finite |x| < 2^(62 - S)), computed
+// from the sign, exponent and significand bits.
+template <typename T> __device__ __forceinline__ long long to_fixed(T x, int S);
+template <> __device__ __forceinline__ long long to_fixed<bf16>(bf16 x, int S)
+{
+    const unsigned u = x;
+    const int E = (u >> 7) & 0xFF;
+    if (E == 0) return 0;  // zero or below 2^-126: truncates to 0
+    const long long M = 0x80 | (u & 0x7F);
+    const int sh = E - 134 + S;
+    const long long v = sh >= 0 ? (M << sh) : (sh > -64 ? (M >> -sh) : 0);
+    return (u & 0x8000u) ? -v : v;
+}
+template <> __device__ __forceinline__ long long to_fixed<float>(float x, int S)
+{
+    const unsigned u = __float_as_uint(x);
+    const int E = (u >> 23) & 0xFF;
+    if (E == 0) return 0;
+    const long long M = 0x800000 | (u & 0x7FFFFF);
+    const int sh = E - 150 + S;
+    const long long v = sh >= 0 ? (M << sh) : (sh > -64 ? (M >> -sh) : 0);
+    return (u & 0x80000000u) ? -v : v;
+}
+
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return f32_to_bf16(x); }
@@ -68,14 +93,14 @@ struct Layout {
     size_t log_ratio, mask, sel_cost;
     size_t scratch;  // start of the per-stage scratch
     // cluster scratch (relative to scratch)
-    size_t cl_err, cl_cent64, cl_sums, cl_cnt, cl_hi, cl_lo, cl_cnorm, cl_cn64, cl_stats, cl_flag, cl_nflag,
-        cl_hist;
+    size_t cl_err, cl_cent64, cl_hi, cl_lo, cl_cnorm, cl_cn64, cl_stats, cl_flag, cl_nflag,
+        cl_hist, cl_perm, cl_sums, cl_resid;
     size_t cl_end;
     // probe scratch (relative to scratch)
     size_t pr_err, pr_qplanes, pr_sbar, pr_keys, pr_pg;
     size_t pr_end;
     // attention scratch (relative to scratch)
-    size_t at_err, at_kvplanes, at_logm, at_tiles, at_segs, at_nsegs;
+    size_t at_err, at_kvplanes, at_logm, at_tiles, at_segs, at_nsegs, at_nkeys, at_comp, at_ncomp;
     size_t at_end;
     size_t total;
 };
