@@ -212,7 +212,10 @@ __global__ __launch_bounds__(256) void k_bucket(const int32_t* __restrict__ labe
 // into chunks of MC_ROWS positions, one block each; a block sums the rows of
 // every cluster segment in its chunk as 64-bit integers (scale 2^shift) and adds
 // them to the cluster's running sums with integer atomics (exact, so the order
-// does not matter).  k_cluster_finalize then turns the sums into means.
+// does not matter).  k_cluster_finalize then turns the sums into means.  The
+// fixed-point image of each element is its value times 2^shift rounded to the
+// nearest integer (fixed_bits), exact for every input that is a multiple of
+// 2^-shift.
 constexpr int MC_ROWS = 512;
 
 template <typename T, int D>
@@ -234,6 +237,7 @@ __global__ __launch_bounds__(256) void k_cluster_chunks(const T* __restrict__ X,
     const int32_t* oh = offsets + (size_t)h * (C + 1);
     const int ch = threadIdx.x % CPR, rg = threadIdx.x / CPR;
     const T* Xh = X + (size_t)h * N * D + ch * EPC;
+    const double scale = ldexp(1.0, shift);
     for (int k = threadIdx.x; k < p1 - p0; k += 256) s_idx[k] = perm[(size_t)h * N + p0 + k];
     // first cluster whose range ends after p0
     int lo_c = 0, hi_c = C - 1;
@@ -245,7 +249,7 @@ __global__ __launch_bounds__(256) void k_cluster_chunks(const T* __restrict__ X,
     for (int m = lo_c; m < C && oh[m] < p1; ++m) {
         const int a0 = max(oh[m], p0) - p0, a1 = min(oh[m + 1], p1) - p0;
         if (a1 <= a0) continue;
-        long long acc[EPC];
+        unsigned long long acc[EPC];
 #pragma unroll
         for (int e = 0; e < EPC; ++e) acc[e] = 0;
         int j = a0 + rg;
@@ -257,17 +261,21 @@ __global__ __launch_bounds__(256) void k_cluster_chunks(const T* __restrict__ X,
             for (int u = 0; u < 4; ++u) {
                 const T* v = (const T*)&w[u];
 #pragma unroll
-                for (int e = 0; e < EPC; ++e) acc[e] += to_fixed<T>(v[e], shift);
+                for (int e = 0; e < EPC; ++e) acc[e] += fixed_bits<T>(v[e], scale);
             }
         }
         for (; j < a1; j += RPP) {
             const uint4 w0 = *(const uint4*)(Xh + (size_t)s_idx[j] * D);
             const T* v0 = (const T*)&w0;
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) acc[e] += to_fixed<T>(v0[e], shift);
+            for (int e = 0; e < EPC; ++e) acc[e] += fixed_bits<T>(v0[e], scale);
         }
+        // remove the offset carried by every accumulated row
+        const unsigned long long rows = (unsigned long long)((a1 - a0 - rg + RPP - 1) / RPP);
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) s_sum[rg][ch * EPC + e] = acc[e];
+        for (int e = 0; e < EPC; ++e) acc[e] -= rows * kFixMagicBits;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) s_sum[rg][ch * EPC + e] = (long long)acc[e];
         __syncthreads();
         if ((int)threadIdx.x < D) {
             long long tot = 0;

@@ -36,29 +36,19 @@ template <typename T> __device__ __forceinline__ float to_f32(T x);
 template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ float to_f32<bf16>(bf16 x) { return bf16_to_f32(x); }
 
-// Exact fixed-point image of an input value: trunc(x * 2^S) as a 64-bit integer
-// (equal to (long long)((double)x * 2^S) for finite |x| < 2^(62 - S)), computed
-// from the sign, exponent and significand bits.
-template <typename T> __device__ __forceinline__ long long to_fixed(T x, int S);
-template <> __device__ __forceinline__ long long to_fixed<bf16>(bf16 x, int S)
+// Exact fixed-point image of an input value.  x * 2^S is formed exactly in
+// fp64 and added to 1.5 * 2^52, which rounds it to the nearest integer (an exact
+// operation whenever x is a multiple of 2^-S, i.e. every input of magnitude at
+// least 2^(-S+7) for bf16 or 2^(-S+23) for fp32, and |x| < 2^(51 - S)); the
+// integer is read from the low bits.  Accumulating the raw bit patterns and
+// subtracting count * bits(1.5 * 2^52) once at the end gives the sum of the
+// integers modulo 2^64, which is the exact sum while it fits in 63 bits.
+constexpr double kFixMagic = 6755399441055744.0;               // 1.5 * 2^52
+constexpr unsigned long long kFixMagicBits = 0x4338000000000000ull;
+template <typename T>
+__device__ __forceinline__ unsigned long long fixed_bits(T x, double scale)
 {
-    const unsigned u = x;
-    const int E = (u >> 7) & 0xFF;
-    if (E == 0) return 0;  // zero or below 2^-126: truncates to 0
-    const long long M = 0x80 | (u & 0x7F);
-    const int sh = E - 134 + S;
-    const long long v = sh >= 0 ? (M << sh) : (sh > -64 ? (M >> -sh) : 0);
-    return (u & 0x8000u) ? -v : v;
-}
-template <> __device__ __forceinline__ long long to_fixed<float>(float x, int S)
-{
-    const unsigned u = __float_as_uint(x);
-    const int E = (u >> 23) & 0xFF;
-    if (E == 0) return 0;
-    const long long M = 0x800000 | (u & 0x7FFFFF);
-    const int sh = E - 150 + S;
-    const long long v = sh >= 0 ? (M << sh) : (sh > -64 ? (M >> -sh) : 0);
-    return (u & 0x80000000u) ? -v : v;
+    return (unsigned long long)__double_as_longlong(fma((double)to_f32<T>(x), scale, kFixMagic));
 }
 
 template <typename T> __device__ __forceinline__ T from_f32(float x);
