@@ -82,6 +82,7 @@ SVG_HIDDEN Layout make_layout(const svgear_shape& s)
     L.at_nkeys = take(H * Cq * 4);
     L.at_comp = take(H * Cq * Ck * 4);
     L.at_ncomp = take(H * Cq * 4);
+    L.at_rowmap = take(H * Cq * Nk * 4);
     L.at_end = off;
 
     size_t sc = L.cl_end;

@@ -200,22 +200,32 @@ struct Softmax {
     f32x16_t o[4];  // O^T blocks: d rows 32 db + ..., query column lane & 31
 };
 
-// acc (+)= K Q^T for a 64-key tile: two 32x32 blocks.
+// acc (+)= K Q^T for a 64-key tile: two 32x32 blocks, the two accumulation
+// chains interleaved and the fragment reads scheduled two steps ahead.
 __device__ __forceinline__ void tile_scores(f32x16_t acc[2], const char* kbuf, const bf16x8_t qf[8],
                                             int lane)
 {
     const int row = lane & 31, half = lane >> 5;
+    const char* kr0 = kbuf + row * K_PITCH + half * 16;
+    const char* kr1 = kr0 + 32 * K_PITCH;
+    f32x16_t a0 = acc[0], a1 = acc[1];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        f32x16_t a = acc[kb];
-        const char* kr = kbuf + (kb * 32 + row) * K_PITCH + half * 16;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const bf16x8_t kf = as_bf16x8(*(const u32x4_t*)(kr + s * 32));
-            a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], a, 0, 0, 0);
-        }
-        acc[kb] = a;
+    for (int s = 0; s < 8; ++s) {
+        const bf16x8_t k0 = as_bf16x8(*(const u32x4_t*)(kr0 + s * 32));
+        const bf16x8_t k1 = as_bf16x8(*(const u32x4_t*)(kr1 + s * 32));
+        a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[s], a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[s], a1, 0, 0, 0);
     }
+    // pipeline: 6 reads up front, then (2 MFMA, 2 reads) x 5, then 6 MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int s = 0; s < 5; ++s) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+    acc[0] = a0;
+    acc[1] = a1;
 }
 
 // Online softmax with raw scores x (logit = x * scale2 + bias, base 2).
@@ -256,7 +266,8 @@ __device__ __forceinline__ void softmax_update(Softmax& st, const f32x16_t x[2],
     st.l += sum;
 }
 
-// O^T += V^T P^T for one 64-key tile held row-major in vbuf (transpose loads).
+// O^T += V^T P^T for one 64-key tile held row-major in vbuf (transpose loads),
+// the transpose reads scheduled ahead of the MFMAs.
 __device__ __forceinline__ void tile_pv(Softmax& st, const char* vbuf, const bf16x8_t pf[4], int lane)
 {
     const int j = lane & 15, grp = lane >> 4;
@@ -264,9 +275,9 @@ __device__ __forceinline__ void tile_pv(Softmax& st, const char* vbuf, const bf1
     // row 4 half + j / 4 (+16 kk, +8 for the second load), column 16 (grp & 1) + 4 (j & 3)
     const char* base = vbuf + (4 * half + (j >> 2)) * V_PITCH + (16 * (grp & 1) + 4 * (j & 3)) * 2;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+    for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        for (int db = 0; db < 4; ++db) {
             const char* a = base + (16 * kk) * V_PITCH + (32 * db) * 2;
             const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a);
             const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a + 8 * V_PITCH));
@@ -275,6 +286,13 @@ __device__ __forceinline__ void tile_pv(Softmax& st, const char* vbuf, const bf1
             st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], st.o[db], 0, 0, 0);
         }
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int s = 0; s < 13; ++s) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
 }
 
 // Tile rows past nvalid get -inf.

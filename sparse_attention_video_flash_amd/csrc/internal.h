@@ -90,7 +90,8 @@ struct Layout {
     size_t pr_err, pr_qplanes, pr_sbar, pr_keys, pr_pg;
     size_t pr_end;
     // attention scratch (relative to scratch)
-    size_t at_err, at_kvplanes, at_logm, at_tiles, at_segs, at_nsegs, at_nkeys, at_comp, at_ncomp;
+    size_t at_err, at_kvplanes, at_logm, at_tiles, at_segs, at_nsegs, at_nkeys, at_comp, at_ncomp,
+        at_rowmap;
     size_t at_end;
     size_t total;
 };
