@@ -145,7 +145,7 @@ def main():
     ap.add_argument("--workload", default="wan", choices=sorted(WORKLOADS))
     ap.add_argument("--rho", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows-stride", type=int, default=2)
+    ap.add_argument("--cpu-rows-stride", type=int, default=1)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()

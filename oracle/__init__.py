@@ -70,6 +70,8 @@ def lib():
             L.svgo_group_means.argtypes = [i32, i32, i32, _F64P, _I32P, _F64P]
             L.svgo_probe.argtypes = [i32, i32, i32, i32, _F64P, _I32P, _F64P, _F64P, _I32P, _F64P,
                                      _F64P, _I32P, _ptr_or_null(_F64P), _F64P]
+            L.svgo_probe_log.argtypes = [i32, i32, i32, i32, _F64P, _I32P, _F64P, _F64P, _I32P, _F64P,
+                                         _F64P, _I32P, _ptr_or_null(_F64P), _F64P]
             L.svgo_budget.argtypes = [f64, i32, i32]
             L.svgo_budget.restype = i64
             L.svgo_route.argtypes = [i32, i32, _F64P, _I32P, _I32P, i64, _U8P]
@@ -156,6 +158,20 @@ def probe(qbar, counts_q, K, V, labels_k, kbar, vbar, counts_k, want_eps: bool =
     return (ratio, eps) if want_eps else ratio
 
 
+def probe_log(qbar, counts_q, K, V, labels_k, kbar, vbar, counts_k, want_eps: bool = False):
+    """ln r[Cq, Ck] (and ln e[Cq, Nk] in key token order if ``want_eps``), the
+    larger exponential factored out so nothing overflows; -inf where r = 0."""
+    qbar, K, V, kbar, vbar = _f64(qbar), _f64(K), _f64(V), _f64(kbar), _f64(vbar)
+    Cq, d = qbar.shape
+    Nk = K.shape[0]
+    Ck = kbar.shape[0]
+    lr = np.empty((Cq, Ck), np.float64)
+    le = np.empty((Cq, Nk), np.float64) if want_eps else None
+    _check(lib().svgo_probe_log(Cq, Nk, Ck, d, qbar, _i32(counts_q), K, V, _i32(labels_k), kbar, vbar,
+                                _i32(counts_k), le, lr))
+    return (lr, le) if want_eps else lr
+
+
 def budget(rho: float, Nq: int, Nk: int) -> int:
     return int(lib().svgo_budget(float(rho), int(Nq), int(Nk)))
 
@@ -199,14 +215,19 @@ def forward_head(Q, K, V, init_q, init_k, Cq: int, Ck: int, rho: float, iters: i
     cq2, offq, permq, invq = permutation(lq, Cq)
     ck2, offk, permk, invk = permutation(lk, Ck)
     vbar = group_means(V, lk, Ck)
-    pr = probe(qbar, cq, K, V, lk, kbar, vbar, ck, want_eps=want_eps)
-    ratio, eps = pr if want_eps else (pr, None)
-    mask, used = route(ratio, cq, ck, rho, Nq, Nk)
+    pr = probe_log(qbar, cq, K, V, lk, kbar, vbar, ck, want_eps=want_eps)
+    log_ratio, log_eps = pr if want_eps else (pr, None)
+    # ln is increasing, so routing on ln r visits blocks in the order of r
+    mask, used = route(log_ratio, cq, ck, rho, Nq, Nk)
     O = hybrid(Q, K, V, lq, lk, kbar, vbar, ck, mask, rows)
+    with np.errstate(over="ignore"):
+        ratio = np.exp(log_ratio)
     out = dict(labels_q=lq, qbar=qbar, counts_q=cq, offsets_q=offq, perm_q=permq, inv_perm_q=invq,
                labels_k=lk, kbar=kbar, counts_k=ck, offsets_k=offk, perm_k=permk, inv_perm_k=invk,
-               vbar=vbar, ratio=ratio, mask=mask, sel_cost=np.int64(used),
+               vbar=vbar, log_ratio=log_ratio, ratio=ratio, mask=mask, sel_cost=np.int64(used),
                budget=np.int64(budget(rho, Nq, Nk)), O=O)
     if want_eps:
-        out["eps2"] = eps
+        out["log_eps2"] = log_eps
+        with np.errstate(over="ignore"):
+            out["eps2"] = np.exp(log_eps)
     return out

@@ -232,6 +232,78 @@ int svgo_probe(int Cq, int Nk, int Ck, int d, const double* qbar, const int32_t*
     return SVGO_OK;
 }
 
+/* The same probe in the log domain: ln r[c, g] (and ln e[c, j]).  The printed
+ * estimate multiplies raw exponentials e^{tau qbar.kbar} and e^{tau qbar.k_j},
+ * which overflow IEEE fp64 once tau qbar.k exceeds about 354 (heavy-tailed
+ * keys reach that).  Factoring the larger exponential out of the norm is exact
+ * algebra:
+ *     e = e^{2M} sum_t (e^{alpha-M} vbar_t - e^{beta-M} v_t)^2,
+ *     alpha = tau qbar.kbar_g, beta = tau qbar.k_j, M = max(alpha, beta),
+ * so ln e = 2M + ln(sum ...), still evaluated directly (not expanded).  The
+ * block value is ln r = ln(sum_{j in g} e_j) - ln m_g, the sum taken as a
+ * log-sum-exp over the keys of g; -inf when n_c m_g = 0 or every e_j is 0. */
+int svgo_probe_log(int Cq, int Nk, int Ck, int d, const double* qbar, const int32_t* counts_q,
+                   const double* K, const double* V, const int32_t* labels_k, const double* kbar,
+                   const double* vbar, const int32_t* counts_k, double* log_eps2,
+                   double* log_ratio)
+{
+    if (Cq <= 0 || Nk < 0 || Ck <= 0 || d <= 0 || !qbar || !counts_q || !K || !V || !labels_k ||
+        !kbar || !vbar || !counts_k || !log_ratio)
+        return SVGO_EARG;
+    const double tau = 1.0 / sqrt((double)d);
+    for (int j = 0; j < Nk; ++j)
+        if (labels_k[j] < 0 || labels_k[j] >= Ck) return SVGO_EARG;
+    int err = SVGO_OK;
+#pragma omp parallel
+    {
+        double* le = (double*)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
+        double* mx = (double*)malloc(sizeof(double) * (size_t)Ck);
+        double* sm = (double*)malloc(sizeof(double) * (size_t)Ck);
+        if (!le || !mx || !sm) {
+#pragma omp atomic write
+            err = SVGO_ENOMEM;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int c = 0; c < Cq; ++c) {
+                const double* qc = qbar + (size_t)c * d;
+                for (int j = 0; j < Nk; ++j) {
+                    const int g = labels_k[j];
+                    const double alpha = tau * dot(qc, kbar + (size_t)g * d, d);
+                    const double beta = tau * dot(qc, K + (size_t)j * d, d);
+                    const double M = alpha > beta ? alpha : beta;
+                    const double a = exp(alpha - M), b = exp(beta - M);
+                    double e = 0.0;
+                    for (int t = 0; t < d; ++t) {
+                        double u = a * vbar[(size_t)g * d + t] - b * V[(size_t)j * d + t];
+                        e += u * u;
+                    }
+                    le[j] = e > 0.0 ? 2.0 * M + log(e) : -INFINITY;
+                    if (log_eps2) log_eps2[(size_t)c * Nk + j] = le[j];
+                }
+                for (int g = 0; g < Ck; ++g) {
+                    mx[g] = -INFINITY;
+                    sm[g] = 0.0;
+                }
+                for (int j = 0; j < Nk; ++j)
+                    if (le[j] > mx[labels_k[j]]) mx[labels_k[j]] = le[j];
+                for (int j = 0; j < Nk; ++j) {
+                    const int g = labels_k[j];
+                    if (le[j] > -INFINITY) sm[g] += exp(le[j] - mx[g]);
+                }
+                double* row = log_ratio + (size_t)c * Ck;
+                for (int g = 0; g < Ck; ++g) {
+                    const int ok = counts_q[c] > 0 && counts_k[g] > 0 && sm[g] > 0.0;
+                    row[g] = ok ? mx[g] + log(sm[g]) - log((double)counts_k[g]) : -INFINITY;
+                }
+            }
+        }
+        free(le);
+        free(mx);
+        free(sm);
+    }
+    return err;
+}
+
 /* Density budget in (query, key) pairs: floor(rho * Nq * Nk), evaluated as
  * (rho * Nq) * Nk in fp64 ([R] step 3, "density budget rho"). */
 int64_t svgo_budget(double rho, int Nq, int Nk)

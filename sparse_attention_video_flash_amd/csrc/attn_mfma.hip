@@ -44,7 +44,7 @@ constexpr int K_PITCH = AT_D * 2 + 16;  // 272 B: 16 consecutive rows hit distin
 constexpr int V_PITCH = AT_D * 2 + 64;  // 320 B: transpose reads of 4 rows x 2 column groups
 constexpr int K_BUF = AT_BN * K_PITCH;  // 17408
 constexpr int V_BUF = AT_BN * V_PITCH;  // 20480
-constexpr int AT_LDS = 2 * K_BUF + 2 * V_BUF + AT_BN * 4 + 2 * AT_BN * 4 + 16;
+constexpr int AT_LDS = 2 * K_BUF + 2 * V_BUF + AT_BN * 4 + AT_BN * 4;
 constexpr int AT_XCD = 8;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -76,9 +76,10 @@ __global__ void k_comp_planes(const float* __restrict__ kbar, const float* __res
 // total length, and the list of compensated clusters (mask = 0, m_g > 0).
 __global__ __launch_bounds__(256) void k_seg_list(const uint8_t* __restrict__ mask,
                                                   const int32_t* __restrict__ offsets_k, int Cq,
-                                                  int Ck, int2* __restrict__ segs,
+                                                  int Ck, int Nk, int2* __restrict__ segs,
                                                   int* __restrict__ nsegs, int* __restrict__ nkeys,
-                                                  int* __restrict__ comp, int* __restrict__ ncomp)
+                                                  int* __restrict__ comp, int* __restrict__ ncomp,
+                                                  int* __restrict__ rowmap)
 {
     __shared__ int s_a[256], s_b[256];
     const int c = blockIdx.x, h = blockIdx.y;
@@ -126,6 +127,16 @@ __global__ __launch_bounds__(256) void k_seg_list(const uint8_t* __restrict__ ma
         nsegs[(size_t)h * Cq + c] = base;
         ncomp[(size_t)h * Cq + c] = cbase;
         nkeys[(size_t)h * Cq + c] = keys;
+    }
+    // Row map: list position -> reordered key row, segment after segment
+    // (the segment list above was written by this workgroup).
+    __syncthreads();
+    int* rm = rowmap + ((size_t)h * Cq + c) * Nk;
+    int pos = 0;
+    for (int si = 0; si < base; ++si) {
+        const int2 sg = out[si];
+        for (int k = threadIdx.x; k < sg.y; k += 256) rm[pos + k] = sg.x + k;
+        pos += sg.y;
     }
 }
 
@@ -182,6 +193,20 @@ __device__ __forceinline__ void stage_load(Stage& s, const bf16* __restrict__ K,
     }
 }
 
+// Same staging for the exact tiles: rows row[i] of this head's K and V read
+// through buffer descriptors (32-bit byte offsets; reads past the head's last
+// row return zero instead of faulting).
+__device__ __forceinline__ void stage_load_rows(Stage& s, __amdgpu_buffer_rsrc_t rk,
+                                                __amdgpu_buffer_rsrc_t rv, const int row[4], int kc)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int off = row[i] * (AT_D * 2) + kc * 16;
+        s.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+        s.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+    }
+}
+
 __device__ __forceinline__ void stage_store(const Stage& s, char* kbuf, char* vbuf, int tid)
 {
     const int kc = tid & 15, kr = tid >> 4;
@@ -228,7 +253,8 @@ __device__ __forceinline__ void tile_scores(f32x16_t acc[2], const char* kbuf, c
     acc[1] = a1;
 }
 
-// Online softmax with raw scores x (logit = x * scale2 + bias, base 2).
+// Online softmax with raw scores x (logit = x * scale2 + bias, base 2); the
+// accumulators are rescaled as soon as some lane's running max grows.
 // Returns the probabilities as PV B-operand fragments pf[kb * 2 + ks].
 __device__ __forceinline__ void softmax_update(Softmax& st, const f32x16_t x[2], float scale2,
                                                bf16x8_t pf[4])
@@ -307,29 +333,14 @@ __device__ __forceinline__ void mask_rows(f32x16_t x[2], int nvalid, int half)
         }
 }
 
-// Source rows of the exact tile starting at list position v0, for thread p < 64:
-// walk the routed segments from the cursor (si, off) = position v0.
-__device__ __forceinline__ int key_of(const int2* __restrict__ sl, int ns, int si, int off, int p,
-                                      int fallback)
-{
-    int o = off + p;
-    while (si < ns) {
-        const int2 sg = sl[si];
-        if (o < sg.y) return sg.x + o;
-        o -= sg.y;
-        ++si;
-    }
-    return fallback;
-}
-
 // ----------------------------------------------------------------------------- main kernel
 
 __global__ __launch_bounds__(AT_THREADS, 2) void k_attn_mfma(
     const bf16* __restrict__ Qp, const int32_t* __restrict__ offsets_q,
     const int32_t* __restrict__ perm_q, const bf16* __restrict__ Kp, const bf16* __restrict__ Vp,
     const bf16* __restrict__ kbh, const bf16* __restrict__ kbl, const bf16* __restrict__ vbh,
-    const bf16* __restrict__ vbl, const float* __restrict__ logm2, const int2* __restrict__ segs,
-    const int* __restrict__ nsegs, const int* __restrict__ nkeys, const int* __restrict__ comp,
+    const bf16* __restrict__ vbl, const float* __restrict__ logm2, const int* __restrict__ rowmap,
+    const int* __restrict__ nkeys, const int* __restrict__ comp,
     const int* __restrict__ ncomp, const int* __restrict__ tstart, int H, int Nq, int Nk, int Cq,
     int Ck, int tiles_per_head, int grid_per_xcd, float scale2, bf16* __restrict__ O)
 {
@@ -337,8 +348,7 @@ __global__ __launch_bounds__(AT_THREADS, 2) void k_attn_mfma(
     char* const kbuf0 = smem;
     char* const vbuf0 = smem + 2 * K_BUF;
     float* const s_bias = (float*)(smem + 2 * K_BUF + 2 * V_BUF);
-    int* const s_map = (int*)(smem + 2 * K_BUF + 2 * V_BUF + AT_BN * 4);  // [2][64]
-    int* const s_cur = s_map + 2 * AT_BN;                                  // cursor (si, off)
+    int* const s_map = (int*)(smem + 2 * K_BUF + 2 * V_BUF + AT_BN * 4);  // [64]
 #define KBUF(b) (kbuf0 + (b) * K_BUF)
 #define VBUF(b) (vbuf0 + (b) * V_BUF)
 
@@ -361,6 +371,7 @@ __global__ __launch_bounds__(AT_THREADS, 2) void k_attn_mfma(
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int qcol = lane & 31, half = lane >> 5;
+    const bool wact = wave * 32 < nrows;  // waves whose 32 query rows are all padding skip the math
 
     // Q^T fragments (B operand): query q0 + 32 wave + qcol, dims 16 s + 8 half + 0..7.
     bf16x8_t qf[8];
@@ -400,79 +411,68 @@ __global__ __launch_bounds__(AT_THREADS, 2) void k_attn_mfma(
             stage_store(sh, KBUF(0), VBUF(0), tid);
             stage_store(sl, KBUF(1), VBUF(1), tid);
             __syncthreads();
-            f32x16_t acc[2] = {f32x16_t{0}, f32x16_t{0}};
-            tile_scores(acc, KBUF(0), qf, lane);
-            tile_scores(acc, KBUF(1), qf, lane);
-            // logit = acc * scale2 + bias: fold the bias in as acc + bias / scale2
+            if (wact) {
+                f32x16_t acc[2] = {f32x16_t{0}, f32x16_t{0}};
+                tile_scores(acc, KBUF(0), qf, lane);
+                tile_scores(acc, KBUF(1), qf, lane);
+                // logit = acc * scale2 + bias: fold the bias in as acc + bias / scale2
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+                for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int kt = kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-                    acc[kb][i] = fmaf(s_bias[kt], 1.0f / scale2, acc[kb][i]);
-                }
-            bf16x8_t pf[4];
-            softmax_update(st, acc, scale2, pf);
-            tile_pv(st, VBUF(0), pf, lane);
-            tile_pv(st, VBUF(1), pf, lane);
+                    for (int i = 0; i < 16; ++i) {
+                        const int kt = kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+                        acc[kb][i] = fmaf(s_bias[kt], 1.0f / scale2, acc[kb][i]);
+                    }
+                bf16x8_t pf[4];
+                softmax_update(st, acc, scale2, pf);
+                tile_pv(st, VBUF(0), pf, lane);
+                tile_pv(st, VBUF(1), pf, lane);
+            }
             __syncthreads();
         }
     }
 
-    // 2. exact tiles (packed routed keys), double-buffered
+    // 2. exact tiles (packed routed keys), double-buffered, one barrier per
+    //    tile; the row map of tile it + 2 is fetched while tile it is computed.
     const int nk = nkeys[hc];
     if (nk > 0) {
-        const int ns = nsegs[hc];
-        const int2* sl = segs + hc * Ck;
-        const bf16* Kh = Kp + (size_t)h * Nk * AT_D;
-        const bf16* Vh = Vp + (size_t)h * Nk * AT_D;
-        const int first = sl[0].x;
+        const int* rm = rowmap + hc * Nk;
+        const size_t head_bytes = (size_t)Nk * AT_D * 2;
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(Kp + (size_t)h * Nk * AT_D), (short)0, (int)head_bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(Vp + (size_t)h * Nk * AT_D), (short)0, (int)head_bytes, 0x00020000);
+        const int kc = tid & 15, kr = tid >> 4;
         const int ntiles = (nk + AT_BN - 1) / AT_BN;
-        // maps of tiles 0 and 1, cursor at tile 2
-        if (tid < AT_BN) {
-            s_map[tid] = key_of(sl, ns, 0, 0, tid, first);
-            s_map[AT_BN + tid] = key_of(sl, ns, 0, 0, AT_BN + tid, first);
-        }
-        if (tid == 0) {
-            int si = 0, o = 2 * AT_BN;
-            while (si < ns && o >= sl[si].y) {
-                o -= sl[si].y;
-                ++si;
-            }
-            s_cur[0] = si;
-            s_cur[1] = o;
-        }
-        __syncthreads();
+        int row[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) row[i] = rm[min(kr + 16 * i, nk - 1)];
         Stage sbuf;
-        stage_load(sbuf, Kh, Vh, s_map, tid);
+        stage_load_rows(sbuf, rk, rv, row, kc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) row[i] = rm[min(AT_BN + kr + 16 * i, nk - 1)];
         stage_store(sbuf, KBUF(0), VBUF(0), tid);
         __syncthreads();
         for (int it = 0; it < ntiles; ++it) {
             const int buf = it & 1;
             const bool has_next = it + 1 < ntiles;
-            if (has_next) stage_load(sbuf, Kh, Vh, s_map + (buf ^ 1) * AT_BN, tid);
-            f32x16_t acc[2] = {f32x16_t{0}, f32x16_t{0}};
-            tile_scores(acc, KBUF(buf), qf, lane);
-            const int nvalid = nk - it * AT_BN;
-            if (nvalid < AT_BN) mask_rows(acc, nvalid, half);
-            bf16x8_t pf[4];
-            softmax_update(st, acc, scale2, pf);
-            tile_pv(st, VBUF(buf), pf, lane);
+            if (has_next) {
+                stage_load_rows(sbuf, rk, rv, row, kc);
+                const int v2 = (it + 2) * AT_BN + kr;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) row[i] = rm[min(v2 + 16 * i, nk - 1)];
+            }
+            if (wact) {
+                f32x16_t acc[2] = {f32x16_t{0}, f32x16_t{0}};
+                tile_scores(acc, KBUF(buf), qf, lane);
+                const int nvalid = nk - it * AT_BN;
+                if (nvalid < AT_BN) mask_rows(acc, nvalid, half);
+                bf16x8_t pf[4];
+                softmax_update(st, acc, scale2, pf);
+                tile_pv(st, VBUF(buf), pf, lane);
+            }
             if (!has_next) break;
             stage_store(sbuf, KBUF(buf ^ 1), VBUF(buf ^ 1), tid);
-            // map of tile it + 2 into the slot tile it used
-            const int si = s_cur[0], off = s_cur[1];
-            __syncthreads();
-            if (tid < AT_BN) s_map[buf * AT_BN + tid] = key_of(sl, ns, si, off, tid, first);
-            if (tid == 0) {
-                int s2 = si, o = off + AT_BN;
-                while (s2 < ns && o >= sl[s2].y) {
-                    o -= sl[s2].y;
-                    ++s2;
-                }
-                s_cur[0] = s2;
-                s_cur[1] = o;
-            }
             __syncthreads();
         }
     }
@@ -534,10 +534,11 @@ SVG_HIDDEN hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t st)
     int* nkeys = (int*)(s + L.at_nkeys);
     int* comp = (int*)(s + L.at_comp);
     int* ncomp = (int*)(s + L.at_ncomp);
+    int* rowmap = (int*)(s + L.at_rowmap);
     hipLaunchKernelGGL(k_comp_planes, dim3(a.Ck, a.H), dim3(AT_D), 0, st, a.kbar, a.vbar, a.counts_k,
                        a.Ck, kbh, kbl, vbh, vbl, logm2);
     hipLaunchKernelGGL(k_seg_list, dim3(a.Cq, a.H), dim3(256), 0, st, a.mask, a.offsets_k, a.Cq,
-                       a.Ck, segs, nsegs, nkeys, comp, ncomp);
+                       a.Ck, a.Nk, segs, nsegs, nkeys, comp, ncomp, rowmap);
     hipLaunchKernelGGL(k_tile_prefix, dim3(a.H), dim3(1024), 0, st, a.offsets_q, a.Cq, tstart);
     const int tiles_per_head = (a.Nq + AT_BM - 1) / AT_BM + a.Cq;
     const long total = (long)tiles_per_head * a.H;
@@ -545,7 +546,7 @@ SVG_HIDDEN hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t st)
     const float scale2 = (float)(1.4426950408889634 / sqrt((double)AT_D));
     hipLaunchKernelGGL(k_attn_mfma, dim3(per_xcd * AT_XCD), dim3(AT_THREADS), AT_LDS, st,
                        (const bf16*)a.Qp, a.offsets_q, a.perm_q, (const bf16*)a.Kp,
-                       (const bf16*)a.Vp, kbh, kbl, vbh, vbl, logm2, segs, nsegs, nkeys, comp, ncomp,
+                       (const bf16*)a.Vp, kbh, kbl, vbh, vbl, logm2, rowmap, nkeys, comp, ncomp,
                        tstart, a.H, a.Nq, a.Nk, a.Cq, a.Ck, tiles_per_head, per_xcd, scale2,
                        (bf16*)a.O);
     return hipGetLastError();

@@ -51,6 +51,23 @@ __device__ __forceinline__ unsigned long long fixed_bits(T x, double scale)
     return (unsigned long long)__double_as_longlong(fma((double)to_f32<T>(x), scale, kFixMagic));
 }
 
+// One probe term in log form: e = e^{2s} [em^2 P + 2 em Qd + R] with
+// s = sbar - D, em = expm1(D), P = ||vbar||^2, Qd = vbar.(vbar - v),
+// R = ||vbar - v||^2.  Returns x and f with e = e^x f.  For D > 0 the factor
+// e^{-2D} is moved inside the bracket (x = 2 sbar, and with y = e^{-D},
+// f = (1-y)^2 P + 2 y (1-y) Qd + y^2 R), so no intermediate overflows however
+// far a key lies from its centroid.
+__device__ __forceinline__ float probe_term(float sb, float dlt, float P, float Qd, float R, float& x)
+{
+    const bool pos = dlt > 0.f;
+    const float em = expm1f(pos ? -dlt : dlt);  // in (-1, 0]
+    const float y = 1.f + em;
+    const float c1 = pos ? -2.f * em * y : 2.f * em;
+    const float c2 = pos ? y * y : 1.f;
+    x = 2.f * (pos ? sb : sb - dlt);
+    return fmaxf(fmaf(em, em * P, fmaf(c1, Qd, c2 * R)), 0.f);
+}
+
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return f32_to_bf16(x); }

@@ -118,11 +118,9 @@ __global__ __launch_bounds__(256) void k_probe_generic(
 #pragma unroll 16
                 for (int t = 0; t < D; ++t) dot = fmaf(q[t], s_k[jj][t], dot);
                 const float dlt = tau * dot;   // sbar - s
-                const float s = sb - dlt;
-                const float em = expm1f(dlt);
                 const float2 kq = s_ks[jj];
-                const float f = fmaxf(fmaf(em, fmaf(em, P, 2.f * kq.x), kq.y), 0.f);
-                const float x = 2.f * s;
+                float x;
+                const float f = probe_term(sb, dlt, P, kq.x, kq.y, x);
                 if (log_eps2)
                     log_eps2[((size_t)h * Cq + c) * Nk + jb + jj] =
                         f > 0.f ? x + logf(f) : -__builtin_inff();

@@ -10,7 +10,8 @@
 // exactly 0 for a key equal to its centroid and small D keep their accuracy.
 // Then, as in the generic kernel,
 //     e = e^{2s} [expm1(D)^2 ||vbar_g||^2 + 2 expm1(D) vbar_g.delta_j + ||delta_j||^2],
-// s = sbar - D, is folded into a per-(c, g) running log-sum-exp.  Keys are the
+// s = sbar - D (in the overflow-free form of probe_term), is folded into a
+// per-(c, g) running log-sum-exp.  Keys are the
 // MFMA rows and query clusters the columns, so each lane owns one c and the
 // sums over keys stay in-lane until one exchange across the four row groups.
 // One wave handles one key cluster; the query-centroid planes of the head sit
@@ -125,11 +126,8 @@ __global__ __launch_bounds__(256) void k_probe_mfma(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     if (!kv[r]) continue;
-                    const float dlt = tau * acc[r];
-                    const float s = sb[cb] - dlt;
-                    const float em = expm1f(dlt);
-                    const float f = fmaxf(fmaf(em, fmaf(em, P, 2.f * kq[r].x), kq[r].y), 0.f);
-                    const float x = 2.f * s;
+                    float x;
+                    const float f = probe_term(sb[cb], tau * acc[r], P, kq[r].x, kq[r].y, x);
                     if (log_eps2 && c < Cq)
                         log_eps2[((size_t)h * Cq + c) * Nk + jb + 4 * grp + r] =
                             f > 0.f ? x + logf(f) : -__builtin_inff();

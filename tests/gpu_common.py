@@ -70,6 +70,65 @@ def oracle_head(w: Workload, data, hi: int, rho: float, rows=None, want_eps=Fals
     return oracle.forward_head(q, k, v, iq, ik, w.Cq, w.Ck, rho, iters=w.iters, rows=rows, want_eps=want_eps)
 
 
+def group_lse(L, labels, C: int):
+    """log-sum-exp of the columns of L [R, N] grouped by ``labels`` [N] -> [R, C]."""
+    L = np.asarray(L, np.float64)
+    M = np.full((L.shape[0], C), -np.inf)
+    np.maximum.at(M.T, labels, L.T)
+    S = np.zeros_like(M)
+    with np.errstate(invalid="ignore"):
+        np.add.at(S.T, labels, np.exp(L.T - M.T[labels]))
+    with np.errstate(divide="ignore"):
+        return np.where(np.isfinite(M), M + np.log(S), -np.inf)
+
+
+def probe_log_floors(qbar, kbar, vbar, K, V, labels_k, counts_k):
+    """ln of the comparison floors of the probe, 1e-4 times the scale of the two
+    terms whose difference is e:  per key  a^2 ||vbar||^2 + b^2 ||v_j||^2,  per
+    block the mean of that over the block's keys (a = e^{tau qbar.kbar},
+    b = e^{tau qbar.k_j}), all in the log domain."""
+    qbar, kbar, vbar, K, V = (np.asarray(x, np.float64) for x in (qbar, kbar, vbar, K, V))
+    tau = 1.0 / np.sqrt(qbar.shape[1])
+    C = kbar.shape[0]
+    with np.errstate(divide="ignore"):
+        la2 = 2 * tau * qbar @ kbar.T + np.log((vbar ** 2).sum(1))[None, :]    # [Cq, Ck]
+        lb2 = 2 * tau * qbar @ K.T + np.log((V ** 2).sum(1))[None, :]          # [Cq, Nk]
+        lmean = group_lse(lb2, labels_k, C) - np.log(np.maximum(counts_k, 1))[None, :]
+    f = np.log(1e-4)
+    return f + np.logaddexp(la2, lmean), f + np.logaddexp(la2[:, labels_k], lb2)
+
+
+def log_close(l_gpu, l_ref, l_floor, rtol=1e-3):
+    """|x_gpu - x_ref| <= rtol * max(x_ref, floor) for x = exp(l), evaluated in the
+    log domain; -inf (an exact zero) must be matched by -inf.  Returns (bad, dev)."""
+    l_gpu = np.asarray(l_gpu, np.float64)
+    l_ref = np.asarray(l_ref, np.float64)
+    lf = np.maximum(l_ref, l_floor)
+    with np.errstate(over="ignore", invalid="ignore"):
+        dev = np.abs(np.exp(l_gpu - lf) - np.exp(l_ref - lf))
+    both_zero = (l_ref == -np.inf) & (l_gpu == -np.inf)
+    bad = ~(both_zero | (dev <= rtol))
+    return bad, np.where(both_zero, 0.0, dev)
+
+
+def near_threshold_ok(mask_gpu, mask_ref, log_ratio):
+    """Mask mismatches are allowed only for blocks within 1e-5 relative of the
+    oracle's selection threshold (the ratio of the first unselected block):
+    |ln r - ln r_thr| <= 1e-5.  Returns the number of mismatches (asserts)."""
+    diff = mask_gpu != mask_ref
+    if not diff.any():
+        return 0
+    flat = np.asarray(log_ratio, np.float64).reshape(-1)
+    order = np.lexsort((np.arange(flat.size), -flat))
+    nsel = int(mask_ref.sum())
+    assert nsel < flat.size, "mask differs although every block is selected"
+    thr = flat[order[nsel]]
+    with np.errstate(invalid="ignore"):
+        near = (log_ratio == thr) | (np.abs(log_ratio - thr) <= 1e-5)
+    assert (~diff | near).all(), ("mask mismatch away from the threshold", int(diff.sum()))
+    return int(diff.sum())
+
+
 def rel_l2(a, b) -> float:
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)
@@ -86,4 +145,4 @@ def check_output(got, ref, dtype: str, what=""):
 
 
 __all__ = ["RAGGED", "WORKLOADS", "torch_gpu", "upload", "shape_of", "gpu_forward", "oracle_head", "rel_l2",
-           "check_output", "log", "TOL"]
+           "check_output", "log", "TOL", "group_lse", "probe_log_floors", "log_close", "near_threshold_ok"]

@@ -9,8 +9,8 @@ import pytest
 import oracle
 from sparse_attention_video_flash_amd import svgear as sv
 
-from gpu_common import (RAGGED, WORKLOADS, check_output, gpu_forward, log, oracle_head, shape_of,
-                        torch_gpu, upload)
+from gpu_common import (RAGGED, WORKLOADS, check_output, gpu_forward, log, log_close, near_threshold_ok,
+                        oracle_head, probe_log_floors, shape_of, torch_gpu, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -125,19 +125,6 @@ def _probe_inputs(w, data, refs):
                 Kp_h=Kp, Vp_h=Vp)
 
 
-def _ratio_close(lr_gpu, r_ref, floor):
-    """|r_gpu - r_ref| <= 1e-3 * max(r_ref, floor), evaluated in the log domain."""
-    lr_gpu = np.asarray(lr_gpu, np.float64)
-    with np.errstate(divide="ignore"):
-        lref = np.log(r_ref)
-        lf = np.log(np.maximum(r_ref, floor))
-    ok_zero = (r_ref == 0) & (lr_gpu == -np.inf)
-    with np.errstate(over="ignore", invalid="ignore"):
-        dev = np.abs(np.exp(lr_gpu - lf) - np.exp(lref - lf))
-    bad = ~(ok_zero | (dev <= 1e-3))
-    return bad, dev
-
-
 @pytest.mark.parametrize("case", ["tiny", "ragged", "small"])
 def test_probe_ratios_and_eps_match_oracle(case):
     torch = torch_gpu()
@@ -153,31 +140,20 @@ def test_probe_ratios_and_eps_match_oracle(case):
     le = torch.empty(H, w.Cq, w.N, device="cuda")
     sv.probe(shape, P["qbar"], P["counts_q"], P["Kp"], P["Vp"], P["kbar"], P["vbar"], P["counts_k"],
              P["offsets_k"], lr, ws, log_eps2=le, flags=sv.DEBUG_SYNC)
-    tau = 1.0 / np.sqrt(w.d)
     for h in range(H):
         r = refs[h]
         qbar32, kbar32, vbar32 = (r[x].astype(np.float32).astype(np.float64) for x in ("qbar", "kbar", "vbar"))
         k64 = data["host"][1][h].astype(np.float64)
         v64 = data["host"][2][h].astype(np.float64)
-        ratio, eps = oracle.probe(qbar32, r["counts_q"], k64, v64, r["labels_k"], kbar32, vbar32,
-                                  r["counts_k"], want_eps=True)
-        # floor: scale of the two terms whose difference is e, averaged over each block
-        lk = r["labels_k"]
-        a2 = np.exp(2 * tau * qbar32 @ kbar32.T)[:, lk] * (vbar32[lk] ** 2).sum(1)[None, :]
-        b2 = np.exp(2 * tau * qbar32 @ k64.T) * (v64 ** 2).sum(1)[None, :]
-        S = np.zeros_like(ratio)
-        for g in range(w.Ck):
-            sel = lk == g
-            if sel.any():
-                S[:, g] = (a2[:, sel] + b2[:, sel]).mean(1)
-        bad, dev = _ratio_close(lr[h].cpu().numpy(), ratio, 1e-4 * S)
+        lratio, leps = oracle.probe_log(qbar32, r["counts_q"], k64, v64, r["labels_k"], kbar32, vbar32,
+                                        r["counts_k"], want_eps=True)
+        lfloor_blk, lfloor_key = probe_log_floors(qbar32, kbar32, vbar32, k64, v64, r["labels_k"], r["counts_k"])
+        bad, dev = log_close(lr[h].cpu().numpy(), lratio, lfloor_blk)
         assert not bad.any(), (h, int(bad.sum()), float(dev[bad].max()))
         # per-key estimate, reordered key order
-        eps_p = eps[:, r["perm_k"]]
-        Sj = (a2 + b2)[:, r["perm_k"]]
-        badj, devj = _ratio_close(le[h].cpu().numpy(), eps_p, 1e-4 * Sj)
+        badj, devj = log_close(le[h].cpu().numpy(), leps[:, r["perm_k"]], lfloor_key[:, r["perm_k"]])
         assert not badj.any(), (h, int(badj.sum()), float(devj[badj].max()))
-        log("  head %d: max ratio dev %.2e, max eps dev %.2e" % (h, float(np.nanmax(dev)), float(np.nanmax(devj))))
+        log("  head %d: max ratio dev %.2e, max eps dev %.2e" % (h, float(dev.max()), float(devj.max())))
 
 
 def _route_gpu(w, H, lr, cq, ck, rho):
@@ -253,22 +229,6 @@ def test_attention_matches_oracle_given_routing(case, rho):
 
 # ----------------------------------------------------------------------------- end to end
 
-def _near_threshold_ok(mask_gpu, r, lr_gpu):
-    """Mask mismatches are allowed only for blocks within 1e-5 relative of the
-    oracle's selection threshold (the ratio of the first unselected block)."""
-    diff = mask_gpu != r["mask"]
-    if not diff.any():
-        return True, 0
-    ratio = r["ratio"]
-    order = sorted(range(ratio.size), key=lambda b: (-ratio.reshape(-1)[b], b))
-    nsel = int(r["mask"].sum())
-    if nsel >= ratio.size:
-        return False, int(diff.sum())
-    thr = ratio.reshape(-1)[order[nsel]]
-    near = np.abs(ratio - thr) <= 1e-5 * abs(thr)
-    return bool((~diff | near).all()), int(diff.sum())
-
-
 @pytest.mark.parametrize("case,rho", [("tiny", 0.25), ("tiny", 1.0), ("ragged", 0.3), ("small", 0.2)])
 def test_forward_end_to_end(case, rho):
     w = CASES[case]
@@ -280,8 +240,7 @@ def test_forward_end_to_end(case, rho):
         for key in ("labels_q", "counts_q", "offsets_q", "perm_q", "inv_perm_q", "labels_k", "counts_k",
                     "offsets_k", "perm_k", "inv_perm_k"):
             np.testing.assert_array_equal(out[key][h].numpy(), r[key], err_msg="%s head %d" % (key, h))
-        ok, nd = _near_threshold_ok(out["mask"][h].numpy(), r, out["log_ratio"][h].numpy())
-        assert ok, ("mask mismatch away from the threshold", h, nd)
+        nd = near_threshold_ok(out["mask"][h].numpy(), r["mask"], r["log_ratio"])
         if nd == 0:
             assert int(out["sel_cost"][h]) == int(r["sel_cost"])
         assert int(out["sel_cost"][h]) <= int(r["budget"])

@@ -115,6 +115,91 @@ def test_reparametrised_probe_algebra_equals_direct_form():
     np.testing.assert_allclose(e, r["eps2"], rtol=1e-9, atol=1e-300)
 
 
+def _piecewise_log_e(qbar, K, V, lk, kbar, vbar):
+    """ln e from the per-key scalars in the overflow-free piecewise form:
+    D = tau qbar.(kbar - k) <= 0:  x = 2(sbar - D),  f = em^2 P + 2 em Qd + R,  em = expm1(D);
+    D > 0:  x = 2 sbar,  f = (1-y)^2 P + 2y(1-y) Qd + y^2 R,  y = e^{-D}."""
+    tau = 1.0 / np.sqrt(K.shape[1])
+    sbar = tau * qbar @ kbar.T
+    D = (sbar[:, lk] - tau * qbar @ K.T)
+    delta = vbar[lk] - V
+    P = (vbar[lk] ** 2).sum(1)[None, :]
+    Qd = (vbar[lk] * delta).sum(1)[None, :]
+    R = (delta ** 2).sum(1)[None, :]
+    pos = D > 0
+    em = np.expm1(np.where(pos, -D, D))
+    y = 1 + em
+    f = em ** 2 * P + np.where(pos, -2 * em * y, 2 * em) * Qd + np.where(pos, y ** 2, 1.0) * R
+    x = 2 * np.where(pos, sbar[:, lk], sbar[:, lk] - D)
+    with np.errstate(divide="ignore"):
+        return np.where(f > 0, x + np.log(np.maximum(f, 0)), -np.inf)
+
+
+def test_piecewise_log_form_equals_log_probe_including_far_keys():
+    """The piecewise form equals the oracle's ln e on the tiny workload, and on
+    keys pushed far from their centroids (|D| up to hundreds, where e^{2s} and
+    expm1(D)^2 alone overflow fp64)."""
+    w, q, k, v, r = _clustered_tiny()
+    K, V = k.astype(np.float64), v.astype(np.float64)
+    lk, qbar, kbar, vbar = r["labels_k"], r["qbar"], r["kbar"], r["vbar"]
+    le = _piecewise_log_e(qbar, K, V, lk, kbar, vbar)
+    fin = np.isfinite(r["log_eps2"])
+    np.testing.assert_allclose(le[fin], r["log_eps2"][fin], rtol=1e-10, atol=1e-9)
+    assert (le[~fin] == -np.inf).all()
+    # far keys: scale the key offsets from their centroids by 100
+    K2 = kbar[lk] + 100.0 * (K - kbar[lk])
+    kbar2 = oracle.group_means(K2, lk, w.Ck)
+    vbar2 = oracle.group_means(V, lk, w.Ck)
+    _, le_ref = oracle.probe_log(qbar, r["counts_q"], K2, V, lk, kbar2, vbar2, r["counts_k"], want_eps=True)
+    tau = 1.0 / np.sqrt(K.shape[1])
+    assert np.abs(tau * qbar @ (kbar2[lk] - K2).T).max() > 360
+    le2 = _piecewise_log_e(qbar, K2, V, lk, kbar2, vbar2)
+    fin = np.isfinite(le_ref)
+    np.testing.assert_allclose(le2[fin], le_ref[fin], rtol=1e-10, atol=1e-8)
+
+
+def test_log_probe_equals_direct_probe():
+    """The log-domain evaluation (larger exponential factored out) equals the
+    logarithm of the printed direct form wherever the latter is finite, and
+    exact zeros map to -inf."""
+    w, q, k, v, r = _clustered_tiny()
+    K, V = k.astype(np.float64), v.astype(np.float64)
+    args = (r["qbar"], r["counts_q"], K, V, r["labels_k"], r["kbar"], r["vbar"], r["counts_k"])
+    ratio, eps = oracle.probe(*args, want_eps=True)
+    lratio, leps = oracle.probe_log(*args, want_eps=True)
+    assert np.isfinite(ratio).all() and (ratio > 0).any() and (ratio == 0).any()
+    with np.errstate(divide="ignore"):
+        np.testing.assert_allclose(lratio, np.log(ratio), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(leps, np.log(eps), rtol=0, atol=1e-12)
+    assert (lratio[ratio == 0] == -np.inf).all()
+
+
+def test_log_probe_shift_of_all_keys_beyond_fp64_range():
+    """Adding one vector u to every key (hence to every key centroid) adds
+    tau qbar_c.u to both exponents of row c, so e and r scale by
+    exp(2 tau qbar_c.u): ln r shifts by exactly that.  With a shift of a few
+    hundred the printed form overflows fp64; the log form does not."""
+    K, V, lab, init = _blocky_keys(5, G=5, per=6, d=16)
+    rng = np.random.default_rng(6)
+    K = K + 0.05 * rng.standard_normal(K.shape)          # keys no longer equal their centroid
+    lk, kbar, ck = oracle.kmeans(K, 5, init, iters=3)
+    vbar = oracle.group_means(V, lk, 5)
+    qbar = rng.standard_normal((4, 16))
+    cq = np.array([3, 0, 2, 5], np.int32)
+    u = 40.0 * qbar[0] / np.linalg.norm(qbar[0]) * 16   # tau qbar_0.u is several hundred
+    base = oracle.probe_log(qbar, cq, K, V, lk, kbar, vbar, ck)
+    shifted = oracle.probe_log(qbar, cq, K + u, V, lk, kbar + u, vbar, ck)
+    tau = 0.25
+    shift = 2 * tau * qbar @ u
+    assert shift.max() > 1000
+    with np.errstate(over="ignore", invalid="ignore"):
+        assert not np.isfinite(oracle.probe(qbar, cq, K + u, V, lk, kbar + u, vbar, ck)).all()
+    fin = np.isfinite(base)
+    assert (~fin == (cq[:, None] == 0) | (ck[None, :] == 0)).all()
+    np.testing.assert_allclose(shifted[fin], (base + shift[:, None])[fin], rtol=1e-12, atol=1e-8)
+    assert (shifted[~fin] == -np.inf).all()
+
+
 # ----------------------------------------------------------------------------- route
 
 @pytest.mark.parametrize("seed", range(6))
