@@ -8,14 +8,18 @@
 // v_mfma_f32_16x16x32_bf16 from bf16 hi/lo planes of both factors (products
 // hi.hi + hi.lo + lo.hi; the differences are formed in fp32 per key), so D is
 // exactly 0 for a key equal to its centroid and small D keep their accuracy.
-// Then, as in the generic kernel,
+// The estimate
 //     e = e^{2s} [expm1(D)^2 ||vbar_g||^2 + 2 expm1(D) vbar_g.delta_j + ||delta_j||^2],
-// s = sbar - D (in the overflow-free form of probe_term), is folded into a
-// per-(c, g) running log-sum-exp.  Keys are the
-// MFMA rows and query clusters the columns, so each lane owns one c and the
-// sums over keys stay in-lane until one exchange across the four row groups.
-// One wave handles one key cluster; the query-centroid planes of the head sit
-// in LDS for the whole workgroup.
+// s = sbar - D, is rewritten as e = e^{2 sbar} e^{u} f with u = 2 max(-D, 0)
+// and f the bracket with e^{-2D} moved inside when D > 0 (so f never
+// overflows); sum_j e^{u} f is accumulated per (c, g) against a shift on u
+// that moves only when some u outgrows it by 2^64.
+//
+// Work split: a workgroup (4 waves) takes one key cluster at a time and stages
+// the difference planes of 64 keys in LDS; wave w owns the query-centroid
+// column blocks cb = w, w + 4, ... whose bf16 hi/lo fragments stay in its
+// registers for the whole launch.  Keys are the MFMA rows, so each lane's
+// partial sums stay in-lane until one exchange across the four row groups.
 #include "internal.h"
 
 namespace svg {
@@ -26,11 +30,38 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int PR_D = 128;
 constexpr int PR_MAXCQ = 256;
-constexpr int PR_PITCH = PR_D * 2 + 16;  // bytes per query-centroid row of a plane
+constexpr int PR_KC = 64;                   // keys per staged chunk
+constexpr int PR_PITCH = PR_D * 2 + 16;     // bytes per key row of a plane (272)
+constexpr int PR_LDS = 2 * PR_KC * PR_PITCH + PR_KC * 8;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kShiftStep = 64.f;          // log2 headroom before the shift moves
 
 __device__ __forceinline__ bf16x8_t pr_as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-template <int NCB>
+// expm1(a) for a <= 0, given w = e^a: a degree-5 Taylor polynomial near 0
+// (truncation below 1.3e-9 relative for |a| <= 1/16), w - 1 elsewhere.
+__device__ __forceinline__ float expm1_nonpos(float a, float w)
+{
+    const float p =
+        a * fmaf(a, fmaf(a, fmaf(a, fmaf(a, 1.f / 120.f, 1.f / 24.f), 1.f / 6.f), 0.5f), 1.f);
+    return a > -0.0625f ? p : w - 1.f;
+}
+
+// Splits 8 fp32 values into packed bf16 hi and lo = bf16(x - hi) words.
+__device__ __forceinline__ void split8(const float x[8], u32x4_t& hi, u32x4_t& lo)
+{
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const bf16 h0 = f32_to_bf16(x[2 * k]), h1 = f32_to_bf16(x[2 * k + 1]);
+        const bf16 l0 = f32_to_bf16(x[2 * k] - bf16_to_f32(h0));
+        const bf16 l1 = f32_to_bf16(x[2 * k + 1] - bf16_to_f32(h1));
+        hi[k] = (unsigned)h0 | ((unsigned)h1 << 16);
+        lo[k] = (unsigned)l0 | ((unsigned)l1 << 16);
+    }
+}
+
+template <int NCBW>
 __global__ __launch_bounds__(256) void k_probe_mfma(
     const float* __restrict__ qbar, const int32_t* __restrict__ counts_q, const bf16* __restrict__ Kp,
     const float* __restrict__ kbar, const float* __restrict__ sbar, const float2* __restrict__ keys,
@@ -38,127 +69,157 @@ __global__ __launch_bounds__(256) void k_probe_mfma(
     float tau, float* __restrict__ log_ratio, float* __restrict__ log_eps2)
 {
     extern __shared__ __attribute__((aligned(16))) char smem[];
+    char* const a_hi = smem;
+    char* const a_lo = smem + PR_KC * PR_PITCH;
+    float2* const s_ks = (float2*)(smem + 2 * PR_KC * PR_PITCH);
     const int h = blockIdx.y;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    constexpr int ncb = NCB;            // 16-column blocks of query clusters
-    const int cqp = ncb * 16;
-    char* qhi = smem;
-    char* qlo = smem + (size_t)cqp * PR_PITCH;
+    const int col = lane & 15, grp = lane >> 4;   // A row / D column, and row group
+    const int ncb = (Cq + 15) / 16;
 
-    // Query-centroid planes of this head (rows past Cq are zero).
-    for (int k = tid; k < cqp * PR_D; k += 256) {
-        const int c = k / PR_D, t = k - c * PR_D;
-        const float v = c < Cq ? qbar[((size_t)h * Cq + c) * PR_D + t] : 0.f;
-        const bf16 vh = f32_to_bf16(v);
-        *(bf16*)(qhi + c * PR_PITCH + t * 2) = vh;
-        *(bf16*)(qlo + c * PR_PITCH + t * 2) = f32_to_bf16(v - bf16_to_f32(vh));
+    // B fragments of this wave's column blocks: centroid cb*16 + col, dims
+    // 32 ks + 8 grp + 0..7, split into bf16 hi and lo.
+    bf16x8_t bh[NCBW][4], bl[NCBW][4];
+#pragma unroll
+    for (int i = 0; i < NCBW; ++i) {
+        const int c = (wave + 4 * i) * 16 + col;
+        const bool cv = c < Cq;
+        const float* qp = qbar + ((size_t)h * Cq + (cv ? c : 0)) * PR_D + 8 * grp;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = cv ? qp[32 * ks + e] : 0.f;
+            u32x4_t hi, lo;
+            split8(x, hi, lo);
+            bh[i][ks] = pr_as_bf16x8(hi);
+            bl[i][ks] = pr_as_bf16x8(lo);
+        }
     }
-    __syncthreads();
 
-    const int col = lane & 15, grp = lane >> 4;   // MFMA column (query cluster) / row group
+    const int sch = tid & 15, srow = tid >> 4;   // staging: dims 8 sch.., rows srow + 16 i
     const int32_t* ok = offsets_k + (size_t)h * (Ck + 1);
-    for (int g = blockIdx.x * 4 + wave; g < Ck; g += gridDim.x * 4) {
+    for (int g = blockIdx.x; g < Ck; g += gridDim.x) {
         const int j0 = ok[g], j1 = ok[g + 1];
         const int mg = j1 - j0;
-        float* lr_out = log_ratio + (size_t)h * Cq * Ck + g;
         if (mg == 0) {
-            for (int c = lane; c < Cq; c += 64) lr_out[(size_t)c * Ck] = -__builtin_inff();
+            for (int c = tid; c < Cq; c += 256) log_ratio[((size_t)h * Cq + c) * Ck + g] = -__builtin_inff();
             continue;
         }
-        // k-bar_g for this lane's dims: 32 ks + 8 grp + 0..7, ks = 0..3
-        float kb[4][8];
-        const float* kbp = kbar + ((size_t)h * Ck + g) * PR_D + 8 * grp;
+        float kb8[8];
+        {
+            const float* kbp = kbar + ((size_t)h * Ck + g) * PR_D + 8 * sch;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) kb[ks][e] = kbp[32 * ks + e];
-        const float P = pg[(size_t)h * Ck + g];
-
-        float M[NCB], S[NCB], sb[NCB];
-#pragma unroll
-        for (int cb = 0; cb < ncb; ++cb) {
-            M[cb] = -__builtin_inff();
-            S[cb] = 0.f;
-            const int c = cb * 16 + col;
-            sb[cb] = c < Cq ? sbar[((size_t)h * Cq + c) * Ck + g] : 0.f;
+            for (int e = 0; e < 8; ++e) kb8[e] = kbp[e];
         }
-        for (int jb = j0; jb < j1; jb += 16) {
-            // A operand: differences kbar_g - k_j (row j = jb + col) as hi/lo planes
-            const int jr = jb + col;
-            const bool rv = jr < j1;
-            bf16x8_t ah[4], al[4];
-            const bf16* kp = Kp + ((size_t)h * Nk + (rv ? jr : j0)) * PR_D + 8 * grp;
+        const float P = pg[(size_t)h * Ck + g];
+        float sb[NCBW], sh[NCBW], S[NCBW];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const u32x4_t w = *(const u32x4_t*)(kp + 32 * ks);
+        for (int i = 0; i < NCBW; ++i) {
+            const int c = (wave + 4 * i) * 16 + col;
+            sb[i] = c < Cq ? sbar[((size_t)h * Cq + c) * Ck + g] : 0.f;
+            sh[i] = 0.f;
+            S[i] = 0.f;
+        }
+        for (int jc = j0; jc < j1; jc += PR_KC) {
+            const int nv = min(PR_KC, j1 - jc);
+            __syncthreads();   // the previous chunk's readers are done
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = srow + 16 * i;
+                const int j = jc + min(r, nv - 1);
+                const u32x4_t w = *(const u32x4_t*)(Kp + ((size_t)h * Nk + j) * PR_D + 8 * sch);
+                float df[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const unsigned bits = (e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16);
-                    const float df = rv ? kb[ks][e] - __uint_as_float(bits) : 0.f;
-                    const bf16 dh = f32_to_bf16(df);
-                    ah[ks][e] = __builtin_bit_cast(__bf16, dh);
-                    al[ks][e] = __builtin_bit_cast(__bf16, f32_to_bf16(df - bf16_to_f32(dh)));
+                    df[e] = kb8[e] - __uint_as_float(bits);
                 }
+                u32x4_t hi, lo;
+                split8(df, hi, lo);
+                *(u32x4_t*)(a_hi + r * PR_PITCH + sch * 16) = hi;
+                *(u32x4_t*)(a_lo + r * PR_PITCH + sch * 16) = lo;
             }
-            // per-key scalars for this lane's rows jb + 4 grp + r
-            float2 kq[4];
-            bool kv[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int j = jb + 4 * grp + r;
-                kv[r] = j < j1;
-                kq[r] = kv[r] ? keys[(size_t)h * Nk + j] : make_float2(0.f, 0.f);
-            }
-#pragma unroll
-            for (int cb = 0; cb < ncb; ++cb) {
-                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-                const char* bh = qhi + (cb * 16 + col) * PR_PITCH + 16 * grp;
-                const char* bl = qlo + (cb * 16 + col) * PR_PITCH + 16 * grp;
+            if (tid < PR_KC) s_ks[tid] = tid < nv ? keys[(size_t)h * Nk + jc + tid] : make_float2(0.f, 0.f);
+            __syncthreads();
+
+            const int ntile = (nv + 15) / 16;
+            for (int kt = 0; kt < ntile; ++kt) {
+                bf16x8_t ah[4], al[4];
+                const int arow = kt * 16 + col;
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
-                    const bf16x8_t qh = pr_as_bf16x8(*(const u32x4_t*)(bh + 64 * ks));
-                    const bf16x8_t ql = pr_as_bf16x8(*(const u32x4_t*)(bl + 64 * ks));
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ks], qh, acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ks], ql, acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[ks], qh, acc, 0, 0, 0);
+                    ah[ks] = pr_as_bf16x8(*(const u32x4_t*)(a_hi + arow * PR_PITCH + (32 * ks + 8 * grp) * 2));
+                    al[ks] = pr_as_bf16x8(*(const u32x4_t*)(a_lo + arow * PR_PITCH + (32 * ks + 8 * grp) * 2));
                 }
-                const int c = cb * 16 + col;
+                const int kr0 = kt * 16 + 4 * grp;   // this lane's rows kr0 .. kr0 + 3
+                float2 kq[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if (!kv[r]) continue;
-                    float x;
-                    const float f = probe_term(sb[cb], tau * acc[r], P, kq[r].x, kq[r].y, x);
-                    if (log_eps2 && c < Cq)
-                        log_eps2[((size_t)h * Cq + c) * Nk + jb + 4 * grp + r] =
-                            f > 0.f ? x + logf(f) : -__builtin_inff();
-                    if (f > 0.f) {
-                        if (x > M[cb]) {
-                            S[cb] = fmaf(S[cb], __expf(M[cb] - x), f);
-                            M[cb] = x;
-                        } else {
-                            S[cb] = fmaf(f, __expf(x - M[cb]), S[cb]);
-                        }
+                for (int r = 0; r < 4; ++r) kq[r] = s_ks[kr0 + r];
+#pragma unroll
+                for (int i = 0; i < NCBW; ++i) {
+                    if (wave + 4 * i >= ncb) continue;   // wave-uniform
+                    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ks], bh[i][ks], acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ks], bl[i][ks], acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[ks], bh[i][ks], acc, 0, 0, 0);
+                    }
+                    float f[4], u[4];
+                    float umax = 0.f;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float D = tau * acc[r];
+                        const float ad = fabsf(D);
+                        const float w = __builtin_amdgcn_exp2f(-ad * kLog2e);   // e^{-|D|}
+                        const float em = expm1_nonpos(-ad, w);
+                        const bool pos = D > 0.f;
+                        const float c1 = pos ? -2.f * em * w : 2.f * em;
+                        const float c2 = pos ? w * w : 1.f;
+                        const float fr = fmaxf(fmaf(em, em * P, fmaf(c1, kq[r].x, c2 * kq[r].y)), 0.f);
+                        f[r] = kr0 + r < nv ? fr : 0.f;
+                        // log2 e^{2|D|} for D <= 0; 0 where the term vanishes, so no
+                        // exponent of a zero term can overflow
+                        u[r] = (pos || !(f[r] > 0.f)) ? 0.f : (2.f * kLog2e) * ad;
+                        umax = fmaxf(umax, u[r]);
+                    }
+                    if (__any(umax > sh[i] + kShiftStep)) {
+                        const float ns = fmaxf(sh[i], umax);
+                        S[i] *= __builtin_amdgcn_exp2f(sh[i] - ns);
+                        sh[i] = ns;
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) S[i] = fmaf(f[r], __builtin_amdgcn_exp2f(u[r] - sh[i]), S[i]);
+                    if (log_eps2) {
+                        const int c = (wave + 4 * i) * 16 + col;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (c < Cq && kr0 + r < nv)
+                                log_eps2[((size_t)h * Cq + c) * Nk + jc + kr0 + r] =
+                                    f[r] > 0.f ? 2.f * sb[i] + kLn2 * u[r] + logf(f[r]) : -__builtin_inff();
                     }
                 }
             }
         }
         // combine the four row groups (lanes col, col + 16, col + 32, col + 48)
 #pragma unroll
-        for (int cb = 0; cb < ncb; ++cb) {
-            float m = M[cb], sacc = S[cb];
+        for (int i = 0; i < NCBW; ++i) {
+            if (wave + 4 * i >= ncb) continue;
+            float m = sh[i], s = S[i];
 #pragma unroll
             for (int o = 16; o <= 32; o <<= 1) {
-                const float om = __shfl_xor(m, o), os = __shfl_xor(sacc, o);
+                const float om = __shfl_xor(m, o), os = __shfl_xor(s, o);
                 const float mn = fmaxf(m, om);
-                if (mn == -__builtin_inff()) continue;
-                sacc = sacc * __expf(m - mn) + os * __expf(om - mn);
+                s = s * __builtin_amdgcn_exp2f(m - mn) + os * __builtin_amdgcn_exp2f(om - mn);
                 m = mn;
             }
-            const int c = cb * 16 + col;
+            const int c = (wave + 4 * i) * 16 + col;
             if (grp == 0 && c < Cq) {
                 float lr = -__builtin_inff();
-                if (counts_q[(size_t)h * Cq + c] > 0 && sacc > 0.f) lr = m + logf(sacc) - logf((float)mg);
-                lr_out[(size_t)c * Ck] = lr;
+                if (counts_q[(size_t)h * Cq + c] > 0 && s > 0.f)
+                    lr = 2.f * sb[i] + kLn2 * (m + __log2f(s)) - logf((float)mg);
+                log_ratio[((size_t)h * Cq + c) * Ck + g] = lr;
             }
         }
     }
@@ -172,23 +233,19 @@ SVG_HIDDEN bool probe_mfma_supported(const ProbeArgs& a)
 SVG_HIDDEN hipError_t launch_probe_mfma(const ProbeArgs& a, const float* sbar, const float2* keys,
                                         const float* pg, hipStream_t st)
 {
-    const int cqp = ((a.Cq + 15) / 16) * 16;
-    const size_t lds = 2 * (size_t)cqp * PR_PITCH;
-    int blocks = (a.Ck + 3) / 4;
-    if (blocks > 64) blocks = 64;
+    const int ncbw = ((a.Cq + 15) / 16 + 3) / 4;   // column blocks per wave
+    int gx = (1024 + a.H - 1) / a.H;
+    if (gx > a.Ck) gx = a.Ck;
     float* eps = (a.flags & SVGEAR_DEBUG_EPS) ? a.log_eps2 : nullptr;
     const float tau = 1.0f / sqrtf((float)PR_D);
 #define SVG_PROBE_CASE(n)                                                                          \
     case n:                                                                                        \
-        hipLaunchKernelGGL(k_probe_mfma<n>, dim3(blocks, a.H), dim3(256), lds, st, a.qbar,         \
+        hipLaunchKernelGGL(k_probe_mfma<n>, dim3(gx, a.H), dim3(256), PR_LDS, st, a.qbar,         \
                            a.counts_q, (const bf16*)a.Kp, a.kbar, sbar, keys, pg, a.offsets_k,     \
                            a.Nk, a.Cq, a.Ck, tau, a.log_ratio, eps);                               \
         break;
-    switch (cqp / 16) {
+    switch (ncbw) {
         SVG_PROBE_CASE(1) SVG_PROBE_CASE(2) SVG_PROBE_CASE(3) SVG_PROBE_CASE(4)
-        SVG_PROBE_CASE(5) SVG_PROBE_CASE(6) SVG_PROBE_CASE(7) SVG_PROBE_CASE(8)
-        SVG_PROBE_CASE(9) SVG_PROBE_CASE(10) SVG_PROBE_CASE(11) SVG_PROBE_CASE(12)
-        SVG_PROBE_CASE(13) SVG_PROBE_CASE(14) SVG_PROBE_CASE(15) SVG_PROBE_CASE(16)
     default: return hipErrorInvalidValue;
     }
 #undef SVG_PROBE_CASE
