@@ -62,6 +62,13 @@ SVG_HIDDEN Layout make_layout(const svgear_shape& s)
     L.cl_perm = take(H * N * 4);
     L.cl_sums = take(H * C * d * 8);
     L.cl_resid = take(H * C * 4);
+    L.cl_labprev = take(H * N * 4);
+    L.cl_bounds = take(3 * H * N * 4);
+    L.cl_changed = take(H * C * 4);
+    L.cl_moved = take(H * C * 4);
+    L.cl_mlist = take(H * C * 4);
+    L.cl_mpos = take(H * C * 4);
+    L.cl_mcount = take(H * 4);
     L.cl_end = off;
 
     off = 0;

@@ -18,6 +18,16 @@
 // the oracle's exact arithmetic (sum of (x_t - c_t)^2 in coordinate order,
 // lowest index on ties).  The labels therefore equal those of a direct fp64
 // evaluation.
+//
+// Later iterations.  Every settled token keeps rigorous bounds (in the same
+// ||c||^2 - 2 x.c units) on its true distance to its own centroid (upper and
+// lower) and on the distance to every other centroid (lower).  A centroid that
+// the last update left bit-identical keeps all its distances, so iteration
+// t > 0 screens every token against the moved centroids only
+// (k_assign_partial): the own centroid's bounds are refreshed if it moved, the
+// moved others give fresh bounds, and the label is decided when one candidate's
+// upper bound lies below every other lower bound; any other token goes to the
+// exact recheck, which also refreshes its bounds exactly.
 #include "internal.h"
 
 namespace svg {
@@ -35,6 +45,30 @@ constexpr int KM_LDS = 2 * KM_BUF;
 constexpr int KM_TOK = 256;                     // tokens per workgroup (4 waves x 64)
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// Outward rounding of fp32 bounds (covers the rounding of the one or two fp32
+// operations that formed them); infinities stay.
+__device__ __forceinline__ float bound_up(float x)
+{
+    return __builtin_isinf(x) ? x : x + (fabsf(x) * 0x1p-22f + 0x1p-100f);
+}
+__device__ __forceinline__ float bound_dn(float x)
+{
+    return __builtin_isinf(x) ? x : x - (fabsf(x) * 0x1p-22f + 0x1p-100f);
+}
+
+// The partial screen is used for a head when at most a quarter of its
+// centroids moved: with more, a full screen costs about the same and its fresh
+// bounds save exact rechecks (bounds folded over many moved centroids are loose).
+__device__ __forceinline__ bool km_partial_pays(int moved, int C) { return 4 * moved <= C; }
+
+// Screen error bound E(x) for a token of norm nx (see the file comment).
+__device__ __forceinline__ float screen_error(float nx, float R, float cmax)
+{
+    const float u = 5.9604645e-8f;  // 2^-24
+    const float xn = nx * 1.0001f;
+    return 1.01f * (2.f * xn * R + 64.f * u * xn * cmax + 2.f * u * (cmax * cmax + 2.f * xn * cmax));
+}
 
 // Per centroid: bf16 hi/lo planes, ||c||^2 (fp32 and fp64); per head: R and ||c||max
 // (as float bits, via integer max of non-negative floats).
@@ -108,14 +142,43 @@ __device__ __forceinline__ void km_store(const KmStage& s, char* buf, int tid)
     if (tid < KM_CB) ((float*)(buf + 2 * KM_PLANE))[tid] = s.cn;
 }
 
+// acc[tb] = (hi + lo rows of a 32-centroid block) x (token block tb)^T; the
+// fragment reads are issued two k-steps ahead of their MFMAs, which bounds the
+// registers they occupy.
+__device__ __forceinline__ void km_tile(f32x16_t acc[2], const char* rh, const bf16x8_t xf[2][8])
+{
+    const char* rl = rh + KM_PLANE;
+    acc[0] = acc[1] = f32x16_t{0};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        const bf16x8_t ah = as_bf16x8(*(const u32x4_t*)(rh + s * 32));
+        const bf16x8_t al = as_bf16x8(*(const u32x4_t*)(rl + s * 32));
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xf[tb][s], acc[tb], 0, 0, 0);
+            acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xf[tb][s], acc[tb], 0, 0, 0);
+        }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int s = 0; s < 6; ++s) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+}
+
 // Screen: labels = screen argmin; near-ties appended to flags[h, *] (token ids).
 __global__ __launch_bounds__(256, 2) void k_assign_mfma(
     const bf16* __restrict__ X, const bf16* __restrict__ hi, const bf16* __restrict__ lo,
     const float* __restrict__ cn32, const unsigned* __restrict__ stats, int N, int C,
-    int32_t* __restrict__ labels, int32_t* __restrict__ flags, int* __restrict__ nflag)
+    int32_t* __restrict__ labels, int32_t* __restrict__ flags, int* __restrict__ nflag,
+    float* __restrict__ ub_own, float* __restrict__ lb_own, float* __restrict__ lb_rest,
+    const int* __restrict__ mcount)
 {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int h = blockIdx.y;
+    if (mcount && km_partial_pays(mcount[h], C)) return;   // k_assign_partial takes this head
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int tcol = lane & 31, half = lane >> 5;
     const bf16* Xh = X + (size_t)h * N * KM_D;
@@ -169,19 +232,8 @@ __global__ __launch_bounds__(256, 2) void k_assign_mfma(
         const float* s_cn = (const float*)(buf + 2 * KM_PLANE);
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
-            f32x16_t acc[2] = {f32x16_t{0}, f32x16_t{0}};
-            const char* rh = buf + (cb * 32 + tcol) * KM_PITCH + half * 16;
-            const char* rl = rh + KM_PLANE;
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const bf16x8_t ah = as_bf16x8(*(const u32x4_t*)(rh + s * 32));
-                const bf16x8_t al = as_bf16x8(*(const u32x4_t*)(rl + s * 32));
-#pragma unroll
-                for (int tb = 0; tb < 2; ++tb) {
-                    acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xf[tb][s], acc[tb], 0, 0, 0);
-                    acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xf[tb][s], acc[tb], 0, 0, 0);
-                }
-            }
+            f32x16_t acc[2];
+            km_tile(acc, buf + (cb * 32 + tcol) * KM_PITCH + half * 16, xf);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int r = cb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
@@ -205,7 +257,6 @@ __global__ __launch_bounds__(256, 2) void k_assign_mfma(
 
     const float R = __uint_as_float(stats[4 * h + 0]);
     const float cmax = __uint_as_float(stats[4 * h + 1]);
-    const float u = 5.9604645e-8f;  // 2^-24
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
         // merge with the partner half-wave (other centroid rows, same token)
@@ -216,11 +267,168 @@ __global__ __launch_bounds__(256, 2) void k_assign_mfma(
         const int ni1 = take ? pi1 : i1[tb];
         const float nb2 = fminf(fminf(b2[tb], pb2), fmaxf(b1[tb], pb1));
         if (half == 0 && tok[tb] < N) {
-            const float xn = nx[tb] * 1.0001f;
-            const float E = 1.01f * (2.f * xn * R + 64.f * u * xn * cmax +
-                                     2.f * u * (cmax * cmax + 2.f * xn * cmax));
-            labels[(size_t)h * N + tok[tb]] = ni1;
+            const float E = screen_error(nx[tb], R, cmax);
+            const size_t t = (size_t)h * N + tok[tb];
+            labels[t] = ni1;
             if (!(nb2 - nb1 > 2.f * E)) {
+                const int pos = atomicAdd(nflag + h, 1);
+                flags[(size_t)h * N + pos] = tok[tb];
+            } else {
+                ub_own[t] = bound_up(nb1 + E);
+                lb_own[t] = bound_dn(nb1 - E);
+                lb_rest[t] = bound_dn(nb2 - E);
+            }
+        }
+    }
+}
+
+// The moved centroids (list mlist[h, 0 .. mcount)) staged like km_load; rows
+// past the list get ||c||^2 = +inf.
+__device__ __forceinline__ void km_load_list(KmStage& s, const bf16* __restrict__ hi,
+                                             const bf16* __restrict__ lo,
+                                             const float* __restrict__ cn,
+                                             const int* __restrict__ ml, int k0, int cnt, int tid)
+{
+    const int ch = tid & 15, r = tid >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int k = k0 + r + 16 * i;
+        const bool ok = k < cnt;
+        const int m = ok ? ml[k] : 0;
+        s.v[i] = ok ? *(const u32x4_t*)(hi + (size_t)m * KM_D + ch * 8) : u32x4_t{0, 0, 0, 0};
+        s.v[4 + i] = ok ? *(const u32x4_t*)(lo + (size_t)m * KM_D + ch * 8) : u32x4_t{0, 0, 0, 0};
+    }
+    const bool okc = tid < KM_CB && k0 + tid < cnt;
+    s.cn = okc ? cn[ml[k0 + tid]] : __builtin_inff();
+}
+
+// Iterations after the first: screen against the moved centroids only and
+// decide from the stored bounds (file comment); undecided tokens are queued for
+// the exact recheck.
+__global__ __launch_bounds__(256, 2) void k_assign_partial(
+    const bf16* __restrict__ X, const bf16* __restrict__ hi, const bf16* __restrict__ lo,
+    const float* __restrict__ cn32, const unsigned* __restrict__ stats, const int* __restrict__ mlist,
+    const int* __restrict__ mpos, const int* __restrict__ mcount, int N, int C,
+    int32_t* __restrict__ labels,
+    int32_t* __restrict__ flags, int* __restrict__ nflag, float* __restrict__ ub_own,
+    float* __restrict__ lb_own, float* __restrict__ lb_rest)
+{
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int h = blockIdx.y;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tcol = lane & 31, half = lane >> 5;
+    const bf16* Xh = X + (size_t)h * N * KM_D;
+    const bf16* hih = hi + (size_t)h * C * KM_D;
+    const bf16* loh = lo + (size_t)h * C * KM_D;
+    const float* cnh = cn32 + (size_t)h * C;
+    const int* ml = mlist + (size_t)h * C;
+    const int cnt = mcount[h];
+    if (!km_partial_pays(cnt, C)) return;   // k_assign_mfma takes this head
+
+    bf16x8_t xf[2][8];
+    float nx[2];
+    int tok[2], own[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+        tok[tb] = blockIdx.x * KM_TOK + wave * 64 + tb * 32 + tcol;
+        const int row = tok[tb] < N ? tok[tb] : N - 1;
+        own[tb] = mpos[(size_t)h * C + labels[(size_t)h * N + row]];   // list position or -1
+        const bf16* xp = Xh + (size_t)row * KM_D + half * 8;
+        float ss = 0.f;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const u32x4_t w = *(const u32x4_t*)(xp + 16 * s);
+            xf[tb][s] = as_bf16x8(w);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float a = __uint_as_float(w[e] << 16), b = __uint_as_float(w[e] & 0xFFFF0000u);
+                ss = fmaf(a, a, ss);
+                ss = fmaf(b, b, ss);
+            }
+        }
+        ss += __shfl_xor(ss, 32);
+        nx[tb] = sqrtf(ss);
+    }
+
+    // per lane and token block: the own centroid's screen value (if it moved),
+    // and the two smallest over the other moved centroids, list position of the first
+    float od[2], b1[2], b2[2];
+    int i1[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+        od[tb] = b1[tb] = b2[tb] = __builtin_inff();
+        i1[tb] = 0;
+    }
+
+    // Single-buffered chunks (the moved list is short after the first few
+    // iterations; this keeps the kernel within 256 VGPRs).
+    const int nchunk = (cnt + KM_CB - 1) / KM_CB;
+    for (int k = 0; k < nchunk; ++k) {
+        char* const buf = smem;
+        {
+            KmStage stg;
+            km_load_list(stg, hih, loh, cnh, ml, k * KM_CB, cnt, tid);
+            __syncthreads();   // the previous chunk's readers are done
+            km_store(stg, buf, tid);
+            __syncthreads();
+        }
+        {
+            const float* s_cn = (const float*)(buf + 2 * KM_PLANE);
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+                f32x16_t acc[2];
+                km_tile(acc, buf + (cb * 32 + tcol) * KM_PITCH + half * 16, xf);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int r = cb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+                    const float cnv = s_cn[r];  // +inf past the list
+                    const int m = k * KM_CB + r;   // list position
+#pragma unroll
+                    for (int tb = 0; tb < 2; ++tb) {
+                        const float d = fmaf(-2.f, acc[tb][i], cnv);
+                        const bool is_own = m == own[tb];
+                        od[tb] = is_own ? d : od[tb];
+                        const float dd = is_own ? __builtin_inff() : d;
+                        const float u = fmaxf(b1[tb], dd);
+                        i1[tb] = dd < b1[tb] ? m : i1[tb];
+                        b1[tb] = fminf(b1[tb], dd);
+                        b2[tb] = fminf(b2[tb], u);
+                    }
+                }
+            }
+        }
+    }
+
+    const float R = __uint_as_float(stats[4 * h + 0]);
+    const float cmax = __uint_as_float(stats[4 * h + 1]);
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+        const float pb1 = __shfl_xor(b1[tb], 32), pb2 = __shfl_xor(b2[tb], 32);
+        const int pi1 = __shfl_xor(i1[tb], 32);
+        const float pod = __shfl_xor(od[tb], 32);
+        const bool take = pb1 < b1[tb] || (pb1 == b1[tb] && pi1 < i1[tb]);
+        const float nb1 = take ? pb1 : b1[tb];
+        const int ni1 = take ? pi1 : i1[tb];
+        const float nb2 = fminf(fminf(b2[tb], pb2), fmaxf(b1[tb], pb1));
+        const float nod = fminf(od[tb], pod);   // at most one half saw the own centroid
+        if (half == 0 && tok[tb] < N) {
+            const float E = screen_error(nx[tb], R, cmax);
+            const size_t t = (size_t)h * N + tok[tb];
+            const bool own_moved = nod < __builtin_inff();
+            const float UBa = own_moved ? bound_up(nod + E) : ub_own[t];
+            const float LBa = own_moved ? bound_dn(nod - E) : lb_own[t];
+            const float LBr = lb_rest[t];
+            const float LBo1 = bound_dn(nb1 - E), UBo1 = bound_up(nb1 + E), LBo2 = bound_dn(nb2 - E);
+            if (UBa < fminf(LBr, LBo1)) {
+                ub_own[t] = UBa;
+                lb_own[t] = LBa;
+                lb_rest[t] = fminf(LBr, LBo1);
+            } else if (UBo1 < fminf(fminf(LBr, LBa), LBo2)) {
+                labels[t] = ml[ni1];
+                ub_own[t] = UBo1;
+                lb_own[t] = LBo1;
+                lb_rest[t] = fminf(fminf(LBr, LBa), LBo2);
+            } else {
                 const int pos = atomicAdd(nflag + h, 1);
                 flags[(size_t)h * N + pos] = tok[tb];
             }
@@ -241,7 +449,10 @@ __global__ __launch_bounds__(256) void k_recheck(const bf16* __restrict__ X,
                                                  const unsigned* __restrict__ stats, int N, int C,
                                                  const int32_t* __restrict__ flags,
                                                  const int* __restrict__ nflag,
-                                                 int32_t* __restrict__ labels)
+                                                 int32_t* __restrict__ labels,
+                                                 float* __restrict__ ub_own,
+                                                 float* __restrict__ lb_own,
+                                                 float* __restrict__ lb_rest)
 {
 #pragma clang fp contract(off)
     __shared__ double s_x[KM_D];
@@ -250,7 +461,7 @@ __global__ __launch_bounds__(256) void k_recheck(const bf16* __restrict__ X,
     __shared__ int s_ri[4];
     __shared__ double s_c[RC_ROWS][KM_D];
     __shared__ int s_cand[RC_MAXCAND];
-    __shared__ int s_nc;
+    __shared__ int s_nc, s_win;
     const int h = blockIdx.y;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int cnt = nflag[h];
@@ -340,19 +551,30 @@ __global__ __launch_bounds__(256) void k_recheck(const bf16* __restrict__ X,
                     bi = s_ri[w];
                 }
             labels[(size_t)h * N + token] = bi;
+            s_win = bi;
+        }
+        __syncthreads();
+        // Bounds for the later partial screens: the winner's exact distance
+        // (shifted by ||x||^2 into the screen's units), and the smallest dot-form
+        // value of the others; both widened by tol, which exceeds their errors.
+        const int win = s_win;
+        double second = __builtin_inf();
+        for (int m = tid; m < C; m += 256)
+            if (m != win) second = fmin(second, s_d[m]);
+        for (int o = 32; o >= 1; o >>= 1) second = fmin(second, __shfl_xor(second, o));
+        __syncthreads();
+        if (lane == 0) s_rb[wave] = second;
+        __syncthreads();
+        if (tid == 0) {
+            second = fmin(fmin(s_rb[0], s_rb[1]), fmin(s_rb[2], s_rb[3]));
+            const double own = best - xx;
+            const size_t t = (size_t)h * N + token;
+            ub_own[t] = __double2float_ru(own + tol);
+            lb_own[t] = __double2float_rd(own - tol);
+            lb_rest[t] = __double2float_rd(second - tol);
         }
     }
 }
-
-struct KmPlanes {
-    bf16* hi;
-    bf16* lo;
-    float* cn32;
-    double* cn64;
-    unsigned* stats;
-    int32_t* flags;
-    int* nflag;
-};
 
 SVG_HIDDEN KmPlanes km_planes(const ClusterArgs& a)
 {
@@ -366,6 +588,13 @@ SVG_HIDDEN KmPlanes km_planes(const ClusterArgs& a)
     P.stats = (unsigned*)(s + L.cl_stats);
     P.flags = (int32_t*)(s + L.cl_flag);
     P.nflag = (int*)(s + L.cl_nflag);
+    P.mlist = (int*)(s + L.cl_mlist);
+    P.mpos = (int*)(s + L.cl_mpos);
+    P.mcount = (int*)(s + L.cl_mcount);
+    const size_t HN = (size_t)a.H * a.N;
+    P.ub_own = (float*)(s + L.cl_bounds);
+    P.lb_own = P.ub_own + HN;
+    P.lb_rest = P.lb_own + HN;
     return P;
 }
 
@@ -383,13 +612,20 @@ SVG_HIDDEN hipError_t launch_km_prep(const ClusterArgs& a, const double* cent64,
 }
 
 SVG_HIDDEN hipError_t launch_assign_mfma(const ClusterArgs& a, const double* cent64,
-                                         const KmPlanes& P, hipStream_t st)
+                                         const KmPlanes& P, bool partial, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_assign_mfma, dim3((a.N + KM_TOK - 1) / KM_TOK, a.H), dim3(256), KM_LDS, st,
-                       (const bf16*)a.X, P.hi, P.lo, P.cn32, P.stats, a.N, a.C, a.labels, P.flags,
-                       P.nflag);
+    // With `partial`, both screens are launched and each head runs in the one
+    // its moved-centroid count selects (decided on the device).
+    const dim3 grid((a.N + KM_TOK - 1) / KM_TOK, a.H);
+    hipLaunchKernelGGL(k_assign_mfma, grid, dim3(256), KM_LDS, st, (const bf16*)a.X, P.hi, P.lo,
+                       P.cn32, P.stats, a.N, a.C, a.labels, P.flags, P.nflag, P.ub_own, P.lb_own,
+                       P.lb_rest, partial ? (const int*)P.mcount : (const int*)nullptr);
+    if (partial)
+        hipLaunchKernelGGL(k_assign_partial, grid, dim3(256), KM_BUF, st, (const bf16*)a.X, P.hi,
+                           P.lo, P.cn32, P.stats, P.mlist, P.mpos, P.mcount, a.N, a.C, a.labels,
+                           P.flags, P.nflag, P.ub_own, P.lb_own, P.lb_rest);
     hipLaunchKernelGGL(k_recheck, dim3(64, a.H), dim3(256), 0, st, (const bf16*)a.X, cent64, P.cn64,
-                       P.stats, a.N, a.C, P.flags, P.nflag, a.labels);
+                       P.stats, a.N, a.C, P.flags, P.nflag, a.labels, P.ub_own, P.lb_own, P.lb_rest);
     return hipGetLastError();
 }
 

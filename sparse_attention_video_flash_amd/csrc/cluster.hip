@@ -223,7 +223,8 @@ __global__ __launch_bounds__(256) void k_cluster_chunks(const T* __restrict__ X,
                                                         const int32_t* __restrict__ perm,
                                                         const int32_t* __restrict__ offsets, int N,
                                                         int C, int shift,
-                                                        unsigned long long* __restrict__ sums)
+                                                        unsigned long long* __restrict__ sums,
+                                                        const int* __restrict__ changed)
 {
     constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
     constexpr int CPR = D / EPC;               // chunks per row
@@ -246,9 +247,11 @@ __global__ __launch_bounds__(256) void k_cluster_chunks(const T* __restrict__ X,
         if (oh[mid + 1] > p0) hi_c = mid; else lo_c = mid + 1;
     }
     __syncthreads();
+    const int* chh = changed ? changed + (size_t)h * C : nullptr;
     for (int m = lo_c; m < C && oh[m] < p1; ++m) {
         const int a0 = max(oh[m], p0) - p0, a1 = min(oh[m + 1], p1) - p0;
         if (a1 <= a0) continue;
+        if (chh && !chh[m]) continue;   // membership unchanged: its mean is unchanged
         unsigned long long acc[EPC];
 #pragma unroll
         for (int e = 0; e < EPC; ++e) acc[e] = 0;
@@ -292,12 +295,16 @@ __global__ __launch_bounds__(256) void k_cluster_chunks(const T* __restrict__ X,
 // zero (plain means).  Optionally writes an fp32 copy; with PLANES also the
 // bf16 hi/lo planes, ||c||^2 (fp32, fp64) and the split residual norm that the
 // MFMA screen of the next assignment needs.  Clears the sums for the next pass.
+// With `changed`, only clusters whose membership changed are recomputed (the
+// others' sums are zero and their centroids stand); `moved` records whether
+// a recomputed centroid differs from its previous value in any bit.
 template <int D, bool PLANES>
 __global__ __launch_bounds__(256) void k_cluster_finalize(
     const int32_t* __restrict__ counts, int C, int shift, int zero_empty,
     unsigned long long* __restrict__ sums, double* __restrict__ cent64, float* __restrict__ cent_out,
     bf16* __restrict__ hi, bf16* __restrict__ lo, float* __restrict__ cn32,
-    double* __restrict__ cn64, float* __restrict__ resid)
+    double* __restrict__ cn64, float* __restrict__ resid, const int* __restrict__ changed,
+    int* __restrict__ moved)
 {
     constexpr int EPL = D / 64;
     const int h = blockIdx.y;
@@ -305,14 +312,17 @@ __global__ __launch_bounds__(256) void k_cluster_finalize(
     const double inv_scale = ldexp(1.0, -shift);
     for (int m = blockIdx.x * 4 + wave; m < C; m += gridDim.x * 4) {
         const size_t row = (size_t)h * C + m;
+        if (changed && !changed[row]) continue;   // wave-uniform
         const int n = counts[row];
         double a2 = 0.0, r2s = 0.0;
+        bool mv = false;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
             const size_t i = row * D + lane * EPL + e;
             double c;
             if (n > 0) {
                 c = ((double)(long long)sums[i] * inv_scale) / (double)n;
+                mv |= c != cent64[i];
                 cent64[i] = c;
                 sums[i] = 0ull;
             } else if (zero_empty) {
@@ -333,6 +343,10 @@ __global__ __launch_bounds__(256) void k_cluster_finalize(
                 r2s = fma(r2, r2, r2s);
             }
         }
+        if (moved) {
+            const bool any = __any(mv);
+            if (lane == 0) moved[row] = any ? 1 : 0;
+        }
         if constexpr (PLANES) {
             for (int o = 32; o >= 1; o >>= 1) {
                 a2 += __shfl_xor(a2, o);
@@ -345,6 +359,63 @@ __global__ __launch_bounds__(256) void k_cluster_finalize(
             }
         }
     }
+}
+
+// Label changes of one assignment: both clusters of every token whose label
+// changed are marked (their members, hence their means, changed); the labels are
+// then kept for the next comparison.  With mark == 0 only the copy is made.
+__global__ __launch_bounds__(256) void k_label_diff(const int32_t* __restrict__ labels,
+                                                    int32_t* __restrict__ prev, int N, int C,
+                                                    int mark, int* __restrict__ changed)
+{
+    const int h = blockIdx.y;
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= N) return;
+    const size_t t = (size_t)h * N + i;
+    const int now = labels[t];
+    if (mark) {
+        const int was = prev[t];
+        if (now != was) {
+            if (was >= 0 && was < C) changed[(size_t)h * C + was] = 1;
+            if (now >= 0 && now < C) changed[(size_t)h * C + now] = 1;
+        }
+    }
+    prev[t] = now;
+}
+
+// Per head: the ascending list of moved centroids (the only ones the next
+// assignment has to evaluate) and each centroid's position in it (-1 if it did
+// not move); both flag arrays are then cleared for the next round.
+__global__ __launch_bounds__(1024) void k_moved_list(int C, int* __restrict__ changed,
+                                                     int* __restrict__ moved, int* __restrict__ mlist,
+                                                     int* __restrict__ mpos, int* __restrict__ mcount)
+{
+    __shared__ int s_part[1024];
+    const int h = blockIdx.x;
+    int* mv = moved + (size_t)h * C;
+    int* ch = changed + (size_t)h * C;
+    int base = 0;
+    for (int m0 = 0; m0 < C; m0 += 1024) {
+        const int m = m0 + threadIdx.x;
+        const int f = (m < C) ? mv[m] : 0;
+        s_part[threadIdx.x] = f;
+        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {
+            const int v = threadIdx.x >= off ? s_part[threadIdx.x - off] : 0;
+            __syncthreads();
+            s_part[threadIdx.x] += v;
+            __syncthreads();
+        }
+        if (f) mlist[(size_t)h * C + base + s_part[threadIdx.x] - 1] = m;
+        if (m < C) {
+            mpos[(size_t)h * C + m] = f ? base + s_part[threadIdx.x] - 1 : -1;
+            mv[m] = 0;
+            ch[m] = 0;
+        }
+        base += s_part[1023];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) mcount[h] = base;
 }
 
 // Per-head maxima, over all clusters, of the split residual and of ||c|| (the
@@ -425,21 +496,6 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ lab
 
 // ----------------------------------------------------------------------------- driver
 
-struct KmPlanes {
-    bf16* hi;
-    bf16* lo;
-    float* cn32;
-    double* cn64;
-    unsigned* stats;
-    int32_t* flags;
-    int* nflag;
-};
-SVG_HIDDEN KmPlanes km_planes(const ClusterArgs& a);
-SVG_HIDDEN hipError_t launch_km_prep(const ClusterArgs& a, const double* cent64, const KmPlanes& P,
-                                     hipStream_t st);
-SVG_HIDDEN hipError_t launch_assign_mfma(const ClusterArgs& a, const double* cent64,
-                                         const KmPlanes& P, hipStream_t st);
-SVG_HIDDEN bool assign_mfma_supported(const ClusterArgs& a);
 
 template <typename T, int D>
 static hipError_t run_cluster(const ClusterArgs& a, hipStream_t st)
@@ -463,10 +519,11 @@ static hipError_t run_cluster(const ClusterArgs& a, hipStream_t st)
     // plain mean pass (no planes)
     auto mean_pass = [&](const T* src, const int32_t* order, int zero_empty, float* out) {
         hipLaunchKernelGGL((k_cluster_chunks<T, D>), gchunks, dim3(256), 0, st, src, order, a.offsets,
-                           N, C, a.shift, sums);
+                           N, C, a.shift, sums, (const int*)nullptr);
         hipLaunchKernelGGL((k_cluster_finalize<D, false>), gfin, dim3(256), 0, st, a.counts, C,
                            a.shift, zero_empty, sums, cent64, out, (bf16*)nullptr, (bf16*)nullptr,
-                           (float*)nullptr, (double*)nullptr, (float*)nullptr);
+                           (float*)nullptr, (double*)nullptr, (float*)nullptr, (const int*)nullptr,
+                           (int*)nullptr);
     };
 
     // counting-sort front half: tile histograms, per-label tile prefixes, counts, offsets
@@ -487,9 +544,20 @@ static hipError_t run_cluster(const ClusterArgs& a, hipStream_t st)
             hipError_t e = launch_km_prep(a, cent64, P, st);
             if (e != hipSuccess) return e;
         }
+        // With the MFMA screen, iteration 0 evaluates every centroid; later
+        // iterations only the centroids that moved in the last update, against
+        // per-token bounds on the distances to all others (see assign_mfma.hip).
+        // Updates recompute only the clusters whose membership changed.
+        int* changed = (int*)(s + L.cl_changed);
+        int* moved = (int*)(s + L.cl_moved);
+        int32_t* labprev = (int32_t*)(s + L.cl_labprev);
+        if (mfma) {
+            zero_words(changed, (size_t)H * C * 4, st);
+            zero_words(moved, (size_t)H * C * 4, st);
+        }
         for (int it = 0; it < a.iters; ++it) {
             if (mfma) {
-                hipError_t e = launch_assign_mfma(a, cent64, P, st);
+                hipError_t e = launch_assign_mfma(a, cent64, P, it > 0, st);
                 if (e != hipSuccess) return e;
             } else {
                 hipLaunchKernelGGL((k_assign_exact<T, D>), dim3((N + 255) / 256, H), dim3(256), 0,
@@ -497,17 +565,23 @@ static hipError_t run_cluster(const ClusterArgs& a, hipStream_t st)
             }
             if (it == a.iters - 1) break;
             // update: unstable bucket order + exact per-cluster means (and next planes)
+            if (mfma)
+                hipLaunchKernelGGL(k_label_diff, dim3((N + 255) / 256, H), dim3(256), 0, st, a.labels,
+                                   labprev, N, C, it > 0 ? 1 : 0, changed);
             sort_front(nullptr, mfma ? P.nflag : nullptr);
             hipLaunchKernelGGL(k_bucket, gtiles, dim3(256), (size_t)C * 4, st, a.labels, N, C,
                                ntiles, hist, a.offsets, pwork);
             if (mfma && D == 128) {
+                const int* chg = it > 0 ? changed : nullptr;
                 hipLaunchKernelGGL((k_cluster_chunks<T, D>), gchunks, dim3(256), 0, st, X, pwork,
-                                   a.offsets, N, C, a.shift, sums);
+                                   a.offsets, N, C, a.shift, sums, chg);
                 hipLaunchKernelGGL((k_cluster_finalize<D, D == 128>), gfin, dim3(256), 0, st, a.counts,
                                    C, a.shift, 0, sums, cent64, (float*)nullptr, P.hi, P.lo, P.cn32,
-                                   P.cn64, resid);
+                                   P.cn64, resid, chg, moved);
                 hipLaunchKernelGGL(k_plane_stats, dim3(H), dim3(256), 0, st, C, P.cn64, resid,
                                    P.stats);
+                hipLaunchKernelGGL(k_moved_list, dim3(H), dim3(1024), 0, st, C, changed, moved,
+                                   P.mlist, P.mpos, P.mcount);
             } else {
                 mean_pass(X, pwork, 0, (float*)nullptr);
             }

@@ -101,7 +101,8 @@ struct Layout {
     size_t scratch;  // start of the per-stage scratch
     // cluster scratch (relative to scratch)
     size_t cl_err, cl_cent64, cl_hi, cl_lo, cl_cnorm, cl_cn64, cl_stats, cl_flag, cl_nflag,
-        cl_hist, cl_perm, cl_sums, cl_resid;
+        cl_hist, cl_perm, cl_sums, cl_resid, cl_labprev, cl_bounds, cl_changed, cl_moved,
+        cl_mlist, cl_mpos, cl_mcount;
     size_t cl_end;
     // probe scratch (relative to scratch)
     size_t pr_err, pr_qplanes, pr_sbar, pr_keys, pr_pg;
@@ -136,6 +137,29 @@ struct ClusterArgs {
     const Layout* L;
 };
 SVG_HIDDEN hipError_t launch_cluster(const ClusterArgs& a, hipStream_t st);
+
+// State of the MFMA k-means assignment (cluster scratch).
+struct KmPlanes {
+    bf16* hi;            // [H, C, d] bf16 hi plane of the fp64 centroids
+    bf16* lo;            // [H, C, d] bf16 plane of the remainder
+    float* cn32;         // [H, C] ||c||^2
+    double* cn64;        // [H, C] ||c||^2
+    unsigned* stats;     // [H, 4] split residual and ||c|| maxima (float bits)
+    int32_t* flags;      // [H, N] tokens queued for the exact recheck
+    int* nflag;          // [H]
+    int* mlist;          // [H, C] centroids moved by the last update, ascending
+    int* mpos;           // [H, C] position of a centroid in mlist, -1 if it did not move
+    int* mcount;         // [H]
+    float* ub_own;       // [H, N] upper bound of the distance to the own centroid
+    float* lb_own;       // [H, N] lower bound of the same
+    float* lb_rest;      // [H, N] lower bound of the distance to every other centroid
+};
+SVG_HIDDEN KmPlanes km_planes(const ClusterArgs& a);
+SVG_HIDDEN hipError_t launch_km_prep(const ClusterArgs& a, const double* cent64, const KmPlanes& P,
+                                     hipStream_t st);
+SVG_HIDDEN hipError_t launch_assign_mfma(const ClusterArgs& a, const double* cent64,
+                                         const KmPlanes& P, bool partial, hipStream_t st);
+SVG_HIDDEN bool assign_mfma_supported(const ClusterArgs& a);
 
 struct ProbeArgs {
     int H, Nk, d, Cq, Ck, dtype, flags;
