@@ -230,6 +230,7 @@ struct Softmax {
 __device__ __forceinline__ void tile_scores(f32x16_t acc[2], const char* kbuf, const bf16x8_t qf[8],
                                             int lane)
 {
+    __builtin_amdgcn_s_setprio(1);
     const int row = lane & 31, half = lane >> 5;
     const char* kr0 = kbuf + row * K_PITCH + half * 16;
     const char* kr1 = kr0 + 32 * K_PITCH;
@@ -251,6 +252,21 @@ __device__ __forceinline__ void tile_scores(f32x16_t acc[2], const char* kbuf, c
     __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
     acc[0] = a0;
     acc[1] = a1;
+    __builtin_amdgcn_s_setprio(0);
+}
+
+// Lane l and lane l ^ 32 hold the two halves of one query column: after
+// v_permlane32_swap the pair of results is {own value, partner's value} in
+// every lane, so symmetric combinations need no LDS round trip.
+__device__ __forceinline__ float pair_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Online softmax with raw scores x (logit = x * scale2 + bias, base 2); the
@@ -264,7 +280,7 @@ __device__ __forceinline__ void softmax_update(Softmax& st, const f32x16_t x[2],
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, x[kb][i]);
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * scale2;
+    mloc = pair_max(mloc) * scale2;
     const float mnew = fmaxf(st.m, mloc);
     const float muse = mnew == -__builtin_inff() ? 0.f : mnew;
     if (__any(mnew > st.m)) {
@@ -296,6 +312,7 @@ __device__ __forceinline__ void softmax_update(Softmax& st, const f32x16_t x[2],
 // the transpose reads scheduled ahead of the MFMAs.
 __device__ __forceinline__ void tile_pv(Softmax& st, const char* vbuf, const bf16x8_t pf[4], int lane)
 {
+    __builtin_amdgcn_s_setprio(1);
     const int j = lane & 15, grp = lane >> 4;
     const int half = grp >> 1;
     // row 4 half + j / 4 (+16 kk, +8 for the second load), column 16 (grp & 1) + 4 (j & 3)
@@ -319,6 +336,7 @@ __device__ __forceinline__ void tile_pv(Softmax& st, const char* vbuf, const bf1
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+    __builtin_amdgcn_s_setprio(0);
 }
 
 // Tile rows past nvalid get -inf.
@@ -478,7 +496,7 @@ __global__ __launch_bounds__(AT_THREADS, 2) void k_attn_mfma(
     }
 
     // 3. normalise, stage the tile in LDS as [query][d], store rows in token order
-    const float ltot = st.l + __shfl_xor(st.l, 32);
+    const float ltot = pair_sum(st.l);
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     __syncthreads();
     char* ost = smem;  // 128 rows x K_PITCH bytes = 2 K buffers
