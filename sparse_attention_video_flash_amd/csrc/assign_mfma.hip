@@ -624,7 +624,7 @@ SVG_HIDDEN hipError_t launch_assign_mfma(const ClusterArgs& a, const double* cen
         hipLaunchKernelGGL(k_assign_partial, grid, dim3(256), KM_BUF, st, (const bf16*)a.X, P.hi,
                            P.lo, P.cn32, P.stats, P.mlist, P.mpos, P.mcount, a.N, a.C, a.labels,
                            P.flags, P.nflag, P.ub_own, P.lb_own, P.lb_rest);
-    hipLaunchKernelGGL(k_recheck, dim3(64, a.H), dim3(256), 0, st, (const bf16*)a.X, cent64, P.cn64,
+    hipLaunchKernelGGL(k_recheck, dim3(256, a.H), dim3(256), 0, st, (const bf16*)a.X, cent64, P.cn64,
                        P.stats, a.N, a.C, P.flags, P.nflag, a.labels, P.ub_own, P.lb_own, P.lb_rest);
     return hipGetLastError();
 }

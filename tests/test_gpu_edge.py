@@ -1,0 +1,102 @@
+"""GPU parity on the edges of the supported shapes, through svgear_forward:
+different query and key lengths, every element type / head size pairing (the
+bf16 d = 128 path runs the MFMA kernels, the others the generic ones), a
+single key cluster, one cluster per key, and the density extremes rho = 0 and
+rho = 1.  Bars as in the main parity tests: integer outputs bit-exact, the mask
+exact up to near-threshold blocks, outputs within the dtype's tolerance."""
+import numpy as np
+import pytest
+
+import oracle
+from sparse_attention_video_flash_amd import svgear as sv
+from sparse_attention_video_flash_amd.inputs import Mixture, Workload, generate_head
+
+from gpu_common import check_output, log, near_threshold_ok, torch_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _workload(dtype, d, Cq, Ck, seed=11):
+    return Workload("edge", 2, (3, 20, 23), d, dtype, Cq, Ck, 10, (0.3,), seed,
+                    (Mixture((0, 2), 24, (2, 3, 4), 0.25, "normal", 0.08, 2.0, "add"),))
+
+
+def _run(w, Nq, Nk, rho, iters=None):
+    torch = torch_gpu()
+    iters = w.iters if iters is None else iters
+    et = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    parts = [generate_head(w, h, Nq, Nk) for h in range(w.H)]
+    q, k, v, iq, ik = (np.stack([p[i] for p in parts]) for i in range(5))
+    dev = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(dt)  # noqa: E731
+    shape = sv.make_shape(w.H, Nq, Nk, w.d, w.Cq, w.Ck, iters, sv.BF16 if w.dtype == "bf16" else sv.F32)
+    ws = sv.alloc_workspace(shape)
+    im = sv.alloc_intermediates(shape)
+    Q, K, V = dev(q, et), dev(k, et), dev(v, et)
+    O = torch.empty_like(Q)
+    sv.forward(shape, rho, Q, K, V, dev(iq, torch.int32), dev(ik, torch.int32), O, ws, im)
+    torch.cuda.synchronize()
+    out = {key: t.cpu() for key, t in im.items()}
+    return out, O.float().cpu().numpy(), (q, k, v, iq, ik)
+
+
+def _check(w, Nq, Nk, rho, out, O, host, iters=None):
+    iters = w.iters if iters is None else iters
+    q, k, v, iq, ik = host
+    for h in range(w.H):
+        r = oracle.forward_head(q[h], k[h], v[h], iq[h], ik[h], w.Cq, w.Ck, rho, iters=iters)
+        for key in ("labels_q", "counts_q", "offsets_q", "perm_q", "inv_perm_q", "labels_k", "counts_k",
+                    "offsets_k", "perm_k", "inv_perm_k"):
+            np.testing.assert_array_equal(out[key][h].numpy(), r[key], err_msg="%s head %d" % (key, h))
+        nd = near_threshold_ok(out["mask"][h].numpy(), r["mask"], r["log_ratio"])
+        if nd == 0:
+            assert int(out["sel_cost"][h]) == int(r["sel_cost"])
+        assert int(out["sel_cost"][h]) <= int(r["budget"])
+        check_output(O[h], r["O"], w.dtype, "head %d O" % h)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("fp32", 128), ("fp32", 64)])
+def test_forward_unequal_query_and_key_lengths(dtype, d):
+    w = _workload(dtype, d, 9, 41)
+    Nq, Nk = 611, 1380
+    log("unequal lengths %s d=%d Nq=%d Nk=%d" % (dtype, d, Nq, Nk))
+    out, O, host = _run(w, Nq, Nk, 0.3)
+    _check(w, Nq, Nk, 0.3, out, O, host)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_forward_single_key_cluster(dtype):
+    """Ck = 1: one key cluster holding every key (rho decides all or nothing)."""
+    w = _workload(dtype, 128, 5, 1)
+    for rho in (0.0, 0.5, 1.0):
+        log("single key cluster %s rho=%g" % (dtype, rho))
+        out, O, host = _run(w, 400, 500, rho, iters=3)
+        _check(w, 400, 500, rho, out, O, host, iters=3)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_forward_one_cluster_per_key(dtype):
+    """Ck = Nk: every key is its own centroid, so compensation is exact and the
+    output equals dense attention for every rho."""
+    w = _workload(dtype, 128, 4, 160)
+    for rho in (0.0, 0.2):
+        log("singleton key clusters %s rho=%g" % (dtype, rho))
+        out, O, host = _run(w, 200, 160, rho, iters=2)
+        _check(w, 200, 160, rho, out, O, host, iters=2)
+        q, k, v = host[:3]
+        for h in range(w.H):
+            s = q[h].astype(np.float64) @ k[h].astype(np.float64).T / np.sqrt(w.d)
+            p = np.exp(s - s.max(1, keepdims=True))
+            dense = (p / p.sum(1, keepdims=True)) @ v[h].astype(np.float64)
+            check_output(O[h], dense, dtype, "head %d vs dense" % h)
+
+
+@pytest.mark.parametrize("rho", [0.0, 1.0])
+def test_forward_density_extremes(rho):
+    w = _workload("bf16", 128, 13, 37)
+    log("density extreme rho=%g" % rho)
+    out, O, host = _run(w, 1380, 1380, rho)
+    for h in range(w.H):
+        cost = int(out["sel_cost"][h])
+        assert cost == (0 if rho == 0.0 else 1380 * 1380)
+    _check(w, 1380, 1380, rho, out, O, host)
+
