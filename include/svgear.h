@@ -68,7 +68,8 @@ typedef struct {
 enum {
     SVGEAR_LABELS_GIVEN = 1, /* svgear_cluster: skip k-means, reorder by the labels passed in */
     SVGEAR_DEBUG_EPS = 2,    /* svgear_probe: also write ln(e[c, j]) per key              */
-    SVGEAR_DEBUG_SYNC = 4    /* synchronise the stream before returning, report faults    */
+    SVGEAR_DEBUG_SYNC = 4,   /* synchronise the stream before returning, report faults    */
+    SVGEAR_PROBE_LOGIT = 8   /* svgear_probe: logit-only estimate (no values), see below  */
 };
 
 /* Per-call pointers of svgear_forward's intermediate results.  Any member may be
@@ -135,7 +136,13 @@ int svgear_cluster(const svgear_shape* shape, int side, const void* X, const voi
  * Kp, Vp are the reordered keys/values [H, Nk, d] and offsets_k their cluster
  * ranges, as written by svgear_cluster.  With SVGEAR_DEBUG_EPS, log_eps2
  * [H, Cq, Nk] (reordered key order) receives ln e[c, j]; otherwise it may be
- * NULL.  Logits never go to device memory.  Errors as svgear_cluster. */
+ * NULL.  Logits never go to device memory.
+ * With SVGEAR_PROBE_LOGIT the estimate ignores the values ([R] step 2 labels
+ * the printed formula the value-aware version; the German summary 2B describes
+ * the probe as a logit difference):
+ *     e[c, j] = ( exp(tau qbar_c . kbar_g) - exp(tau qbar_c . k_j) )^2,
+ * block ratio and output as above; Vp and vbar are then not read (they must
+ * still be valid pointers).  Errors as svgear_cluster. */
 int svgear_probe(const svgear_shape* shape, const float* qbar, const int32_t* counts_q,
                  const void* Kp, const void* Vp, const float* kbar, const float* vbar,
                  const int32_t* counts_k, const int32_t* offsets_k, int flags, float* log_ratio,

@@ -71,7 +71,7 @@ def lib():
             L.svgo_probe.argtypes = [i32, i32, i32, i32, _F64P, _I32P, _F64P, _F64P, _I32P, _F64P,
                                      _F64P, _I32P, _ptr_or_null(_F64P), _F64P]
             L.svgo_probe_log.argtypes = [i32, i32, i32, i32, _F64P, _I32P, _F64P, _F64P, _I32P, _F64P,
-                                         _F64P, _I32P, _ptr_or_null(_F64P), _F64P]
+                                         _F64P, _I32P, _ptr_or_null(_F64P), _F64P, i32]
             L.svgo_budget.argtypes = [f64, i32, i32]
             L.svgo_budget.restype = i64
             L.svgo_route.argtypes = [i32, i32, _F64P, _I32P, _I32P, i64, _U8P]
@@ -158,9 +158,11 @@ def probe(qbar, counts_q, K, V, labels_k, kbar, vbar, counts_k, want_eps: bool =
     return (ratio, eps) if want_eps else ratio
 
 
-def probe_log(qbar, counts_q, K, V, labels_k, kbar, vbar, counts_k, want_eps: bool = False):
+def probe_log(qbar, counts_q, K, V, labels_k, kbar, vbar, counts_k, want_eps: bool = False,
+              logit_only: bool = False):
     """ln r[Cq, Ck] (and ln e[Cq, Nk] in key token order if ``want_eps``), the
-    larger exponential factored out so nothing overflows; -inf where r = 0."""
+    larger exponential factored out so nothing overflows; -inf where r = 0.
+    ``logit_only``: the estimate without values, (e^{tau qbar.kbar} - e^{tau qbar.k})^2."""
     qbar, K, V, kbar, vbar = _f64(qbar), _f64(K), _f64(V), _f64(kbar), _f64(vbar)
     Cq, d = qbar.shape
     Nk = K.shape[0]
@@ -168,7 +170,7 @@ def probe_log(qbar, counts_q, K, V, labels_k, kbar, vbar, counts_k, want_eps: bo
     lr = np.empty((Cq, Ck), np.float64)
     le = np.empty((Cq, Nk), np.float64) if want_eps else None
     _check(lib().svgo_probe_log(Cq, Nk, Ck, d, qbar, _i32(counts_q), K, V, _i32(labels_k), kbar, vbar,
-                                _i32(counts_k), le, lr))
+                                _i32(counts_k), le, lr, 1 if logit_only else 0))
     return (lr, le) if want_eps else lr
 
 

@@ -241,11 +241,15 @@ int svgo_probe(int Cq, int Nk, int Ck, int d, const double* qbar, const int32_t*
  *     alpha = tau qbar.kbar_g, beta = tau qbar.k_j, M = max(alpha, beta),
  * so ln e = 2M + ln(sum ...), still evaluated directly (not expanded).  The
  * block value is ln r = ln(sum_{j in g} e_j) - ln m_g, the sum taken as a
- * log-sum-exp over the keys of g; -inf when n_c m_g = 0 or every e_j is 0. */
+ * log-sum-exp over the keys of g; -inf when n_c m_g = 0 or every e_j is 0.
+ * With logit_only the estimate is the logit-difference variant that the
+ * pages name but do not print ([R] step 2 calls the printed formula the
+ * value-aware version; [DE] 2B speaks of a logit difference), read as
+ * e = (exp(tau qbar.kbar_g) - exp(tau qbar.k_j))^2. */
 int svgo_probe_log(int Cq, int Nk, int Ck, int d, const double* qbar, const int32_t* counts_q,
                    const double* K, const double* V, const int32_t* labels_k, const double* kbar,
                    const double* vbar, const int32_t* counts_k, double* log_eps2,
-                   double* log_ratio)
+                   double* log_ratio, int logit_only)
 {
     if (Cq <= 0 || Nk < 0 || Ck <= 0 || d <= 0 || !qbar || !counts_q || !K || !V || !labels_k ||
         !kbar || !vbar || !counts_k || !log_ratio)
@@ -273,9 +277,14 @@ int svgo_probe_log(int Cq, int Nk, int Ck, int d, const double* qbar, const int3
                     const double M = alpha > beta ? alpha : beta;
                     const double a = exp(alpha - M), b = exp(beta - M);
                     double e = 0.0;
-                    for (int t = 0; t < d; ++t) {
-                        double u = a * vbar[(size_t)g * d + t] - b * V[(size_t)j * d + t];
-                        e += u * u;
+                    if (logit_only) {
+                        /* the logit-difference estimate: the values drop out */
+                        e = (a - b) * (a - b);
+                    } else {
+                        for (int t = 0; t < d; ++t) {
+                            double u = a * vbar[(size_t)g * d + t] - b * V[(size_t)j * d + t];
+                            e += u * u;
+                        }
                     }
                     le[j] = e > 0.0 ? 2.0 * M + log(e) : -INFINITY;
                     if (log_eps2) log_eps2[(size_t)c * Nk + j] = le[j];

@@ -288,7 +288,7 @@ SVG_API int svgear_probe(const svgear_shape* shape, const float* qbar, const int
 {
     int rc = check_shape(shape);
     if (rc) return rc;
-    if (flags & ~(SVGEAR_DEBUG_EPS | SVGEAR_DEBUG_SYNC)) return SVGEAR_E_ARG;
+    if (flags & ~(SVGEAR_DEBUG_EPS | SVGEAR_DEBUG_SYNC | SVGEAR_PROBE_LOGIT)) return SVGEAR_E_ARG;
     rc = check_ptrs({qbar, counts_q, Kp, Vp, kbar, vbar, counts_k, offsets_k, log_ratio});
     if (rc) return rc;
     if (flags & SVGEAR_DEBUG_EPS) {

@@ -16,13 +16,22 @@ namespace svg {
 
 // Per key (reordered order): (vbar_g.delta_j, ||delta_j||^2), and per key
 // cluster ||vbar_g||^2.  One block per key cluster; 16 lanes per key row.
+// With logit_only the values drop out: (0, 0) per key and 1 per cluster, which
+// turns the bracket into expm1(D)^2, i.e. e = (e^sbar - e^s)^2.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_key_scalars(const T* __restrict__ Vp,
                                                      const float* __restrict__ vbar,
                                                      const int32_t* __restrict__ offsets_k, int Nk,
                                                      int Ck, float2* __restrict__ keys,
-                                                     float* __restrict__ pg)
+                                                     float* __restrict__ pg, int logit_only)
 {
+    if (logit_only) {
+        const int g = blockIdx.x, h = blockIdx.y;
+        if (threadIdx.x == 0) pg[(size_t)h * Ck + g] = 1.f;
+        const int j0 = offsets_k[(size_t)h * (Ck + 1) + g], j1 = offsets_k[(size_t)h * (Ck + 1) + g + 1];
+        for (int j = j0 + (int)threadIdx.x; j < j1; j += 256) keys[(size_t)h * Nk + j] = make_float2(0.f, 0.f);
+        return;
+    }
     constexpr int EPT = D / 16;  // elements per thread
     const int g = blockIdx.x, h = blockIdx.y;
     const int sub = threadIdx.x & 15, row = threadIdx.x >> 4;
@@ -157,7 +166,7 @@ static hipError_t run_probe(const ProbeArgs& a, hipStream_t st)
     float* pg = (float*)(a.scratch + L.pr_pg);
     const float tau = 1.0f / sqrtf((float)D);
     hipLaunchKernelGGL((k_key_scalars<T, D>), dim3(a.Ck, a.H), dim3(256), 0, st, (const T*)a.Vp,
-                       a.vbar, a.offsets_k, a.Nk, a.Ck, keys, pg);
+                       a.vbar, a.offsets_k, a.Nk, a.Ck, keys, pg, (a.flags & SVGEAR_PROBE_LOGIT) ? 1 : 0);
     hipLaunchKernelGGL((k_sbar<D>), dim3(a.Cq, (a.Ck + 255) / 256, a.H), dim3(256), 0, st, a.qbar,
                        a.kbar, a.Cq, a.Ck, 1.0 / sqrt((double)D), sbar);
     if (probe_mfma_supported(a)) return launch_probe_mfma(a, sbar, keys, pg, st);

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(PKG, "libsvgear.so")
 
 OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_WORKSPACE, E_RHO, E_HIP, E_ARG = 0, -1, -2, -3, -4, -5, -6, -7, -8
 F32, BF16 = 0, 1
-LABELS_GIVEN, DEBUG_EPS, DEBUG_SYNC = 1, 2, 4
+LABELS_GIVEN, DEBUG_EPS, DEBUG_SYNC, PROBE_LOGIT = 1, 2, 4, 8
 
 EXPORTS = ("svgear_workspace_bytes", "svgear_cluster", "svgear_probe", "svgear_route",
            "svgear_attention", "svgear_forward", "svgear_status_string", "svgear_version")

@@ -156,6 +156,46 @@ def test_probe_ratios_and_eps_match_oracle(case):
         log("  head %d: max ratio dev %.2e, max eps dev %.2e" % (h, float(dev.max()), float(devj.max())))
 
 
+@pytest.mark.parametrize("case", ["tiny", "ragged", "small"])
+def test_probe_logit_only_matches_oracle(case):
+    """The logit-only estimate (SVGEAR_PROBE_LOGIT) against the oracle's, with the
+    floor built from unit values (the estimate has no value terms)."""
+    torch = torch_gpu()
+    w = CASES[case]
+    log("probe logit-only %s" % case)
+    data = upload(w)
+    refs = _oracle_all(w, data, w.rhos[0])
+    H = len(refs)
+    shape = shape_of(w, H)
+    ws = sv.alloc_workspace(shape)
+    P = _probe_inputs(w, data, refs)
+    lr = torch.empty(H, w.Cq, w.Ck, device="cuda")
+    le = torch.empty(H, w.Cq, w.N, device="cuda")
+    sv.probe(shape, P["qbar"], P["counts_q"], P["Kp"], P["Vp"], P["kbar"], P["vbar"], P["counts_k"],
+             P["offsets_k"], lr, ws, log_eps2=le, flags=sv.DEBUG_SYNC | sv.PROBE_LOGIT)
+    for h in range(H):
+        r = refs[h]
+        qbar32, kbar32, vbar32 = (r[x].astype(np.float32).astype(np.float64) for x in ("qbar", "kbar", "vbar"))
+        k64 = data["host"][1][h].astype(np.float64)
+        v64 = data["host"][2][h].astype(np.float64)
+        lratio, leps = oracle.probe_log(qbar32, r["counts_q"], k64, v64, r["labels_k"], kbar32, vbar32,
+                                        r["counts_k"], want_eps=True, logit_only=True)
+        unit_c = np.zeros_like(vbar32)
+        unit_c[:, 0] = 1.0
+        unit_k = np.zeros_like(v64)
+        unit_k[:, 0] = 1.0
+        lfb, lfk = probe_log_floors(qbar32, kbar32, unit_c, k64, unit_k, r["labels_k"], r["counts_k"])
+        # Without value terms, e = a^2 expm1(D)^2 carries the absolute error of D
+        # itself (the split-bf16 products are good to about 2^-16 of
+        # tau sum_t |qbar_t delta_t|), squared-amplified where D is small: the bar
+        # is 3e-3 for block means and 1e-2 per key (1e-3 for the value-aware probe).
+        bad, dev = log_close(lr[h].cpu().numpy(), lratio, lfb, rtol=3e-3)
+        assert not bad.any(), (h, int(bad.sum()), float(dev[bad].max()))
+        badj, devj = log_close(le[h].cpu().numpy(), leps[:, r["perm_k"]], lfk[:, r["perm_k"]], rtol=1e-2)
+        assert not badj.any(), (h, int(badj.sum()), float(devj[badj].max()))
+        log("  head %d: max ratio dev %.2e, max eps dev %.2e" % (h, float(dev.max()), float(devj.max())))
+
+
 def _route_gpu(w, H, lr, cq, ck, rho):
     torch = torch_gpu()
     shape = shape_of(w, H)

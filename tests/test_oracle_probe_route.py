@@ -200,6 +200,49 @@ def test_log_probe_shift_of_all_keys_beyond_fp64_range():
     assert (shifted[~fin] == -np.inf).all()
 
 
+def test_logit_only_probe_equals_brute_force():
+    """Logit-only estimate (no values): ln of the block mean of
+    (e^{tau qbar.kbar_g} - e^{tau qbar.k_j})^2, written out in numpy."""
+    w, q, k, v, r = _clustered_tiny()
+    K, V = k.astype(np.float64), v.astype(np.float64)
+    lk, qbar, kbar, vbar = r["labels_k"], r["qbar"], r["kbar"], r["vbar"]
+    tau = 1.0 / np.sqrt(K.shape[1])
+    a = np.exp(tau * qbar @ kbar.T)[:, lk]
+    b = np.exp(tau * qbar @ K.T)
+    e = (a - b) ** 2
+    ref = np.zeros(r["ratio"].shape)
+    for g in range(w.Ck):
+        sel = lk == g
+        if sel.any():
+            ref[:, g] = e[:, sel].mean(axis=1)
+    ref[r["counts_q"] == 0] = 0.0
+    lr, le = oracle.probe_log(qbar, r["counts_q"], K, V, lk, kbar, vbar, r["counts_k"], want_eps=True,
+                              logit_only=True)
+    with np.errstate(divide="ignore"):
+        np.testing.assert_allclose(lr, np.log(ref), rtol=0, atol=1e-11)
+        np.testing.assert_allclose(le, np.log(e), rtol=0, atol=1e-11)
+
+
+def test_logit_only_probe_ignores_values_and_vanishes_for_identical_keys():
+    K, V, lab, init = _blocky_keys(7)
+    lk, kbar, ck = oracle.kmeans(K, 6, init, iters=3)
+    vbar = oracle.group_means(V, lk, 6)
+    rng = np.random.default_rng(8)
+    qbar = rng.standard_normal((4, 16))
+    cq = np.array([3, 1, 2, 7], np.int32)
+    # keys equal to their centroids: every logit difference is zero (up to the
+    # rounding of the fp64 centroid mean)
+    lr = oracle.probe_log(qbar, cq, K, V, lk, kbar, vbar, ck, logit_only=True)
+    assert (np.exp(lr) <= 1e-24).all()
+    # perturbed keys: the result does not depend on V or vbar at all
+    K2 = K + 0.1 * rng.standard_normal(K.shape)
+    kbar2 = oracle.group_means(K2, lk, 6)
+    a = oracle.probe_log(qbar, cq, K2, V, lk, kbar2, vbar, ck, logit_only=True)
+    b = oracle.probe_log(qbar, cq, K2, 5.0 * V[::-1].copy(), lk, kbar2, -vbar, ck, logit_only=True)
+    np.testing.assert_array_equal(a, b)
+    assert np.isfinite(a).all()
+
+
 # ----------------------------------------------------------------------------- route
 
 @pytest.mark.parametrize("seed", range(6))
