@@ -69,7 +69,8 @@ enum {
     SVGEAR_LABELS_GIVEN = 1, /* svgear_cluster: skip k-means, reorder by the labels passed in */
     SVGEAR_DEBUG_EPS = 2,    /* svgear_probe: also write ln(e[c, j]) per key              */
     SVGEAR_DEBUG_SYNC = 4,   /* synchronise the stream before returning, report faults    */
-    SVGEAR_PROBE_LOGIT = 8   /* svgear_probe: logit-only estimate (no values), see below  */
+    SVGEAR_PROBE_LOGIT = 8,  /* svgear_probe: logit-only estimate (no values), see below  */
+    SVGEAR_PROBE_SCORE = 16  /* svgear_probe: attention-score comparator, see below       */
 };
 
 /* Per-call pointers of svgear_forward's intermediate results.  Any member may be
@@ -142,7 +143,16 @@ int svgear_cluster(const svgear_shape* shape, int side, const void* X, const voi
  * the probe as a logit difference):
  *     e[c, j] = ( exp(tau qbar_c . kbar_g) - exp(tau qbar_c . k_j) )^2,
  * block ratio and output as above; Vp and vbar are then not read (they must
- * still be valid pointers).  Errors as svgear_cluster. */
+ * still be valid pointers).
+ * With SVGEAR_PROBE_SCORE the ratio is the attention-score rule that the pages
+ * argue against ([R] novelty paragraph; [DE] 1 and 2B), read as the centroid
+ * estimate of the attention mass of block (c, g) per pair of the block:
+ *     ln r[c, g] = tau qbar_c . kbar_g
+ *                  - ln sum_{g': m_g' > 0} m_g' exp(tau qbar_c . kbar_g'),
+ * -inf where n_c m_g = 0.  Only qbar, kbar and the counts are read (the other
+ * pointers must still be valid); it cannot be combined with
+ * SVGEAR_PROBE_LOGIT or SVGEAR_DEBUG_EPS (SVGEAR_E_ARG).
+ * Errors as svgear_cluster. */
 int svgear_probe(const svgear_shape* shape, const float* qbar, const int32_t* counts_q,
                  const void* Kp, const void* Vp, const float* kbar, const float* vbar,
                  const int32_t* counts_k, const int32_t* offsets_k, int flags, float* log_ratio,
@@ -158,6 +168,17 @@ int svgear_probe(const svgear_shape* shape, const float* qbar, const int32_t* co
 int svgear_route(const svgear_shape* shape, double rho, const float* log_ratio,
                  const int32_t* counts_q, const int32_t* counts_k, uint8_t* mask,
                  int64_t* sel_cost, void* ws, size_t ws_bytes, void* stream);
+
+/* The other reading of the density budget ([R] future-work paragraph: the
+ * same budget for every query cluster): each query cluster c selects within its
+ * own row, B_c = floor((rho * counts_q[c]) * Nk) pairs (fp64), greedily in
+ * descending ratio order (equal log_ratio: lower key-cluster index first), the
+ * longest prefix whose total cost counts_q[c] * counts_k[g] is <= B_c.  Same
+ * arguments, outputs and errors as svgear_route; sel_cost[h] is the total over
+ * the head's rows.  Not used by svgear_forward (which routes per head). */
+int svgear_route_rows(const svgear_shape* shape, double rho, const float* log_ratio,
+                      const int32_t* counts_q, const int32_t* counts_k, uint8_t* mask,
+                      int64_t* sel_cost, void* ws, size_t ws_bytes, void* stream);
 
 /* Step 4 of [R] (also [DE] 2A, [IT] 2A): hybrid attention.  For each reordered
  * query row of cluster c (rows offsets_q[c] .. offsets_q[c+1] of Qp), one

@@ -72,6 +72,7 @@ def lib():
                                      _F64P, _I32P, _ptr_or_null(_F64P), _F64P]
             L.svgo_probe_log.argtypes = [i32, i32, i32, i32, _F64P, _I32P, _F64P, _F64P, _I32P, _F64P,
                                          _F64P, _I32P, _ptr_or_null(_F64P), _F64P, i32]
+            L.svgo_score_log.argtypes = [i32, i32, i32, _F64P, _I32P, _F64P, _I32P, _F64P]
             L.svgo_budget.argtypes = [f64, i32, i32]
             L.svgo_budget.restype = i64
             L.svgo_route.argtypes = [i32, i32, _F64P, _I32P, _I32P, i64, _U8P]
@@ -174,6 +175,17 @@ def probe_log(qbar, counts_q, K, V, labels_k, kbar, vbar, counts_k, want_eps: bo
     return (lr, le) if want_eps else lr
 
 
+def score_log(qbar, counts_q, kbar, counts_k):
+    """Attention-score comparator, ln r[Cq, Ck]: the centroid-estimated attention
+    mass of block (c, g) per pair of the block, -inf where the block is empty."""
+    qbar, kbar = _f64(qbar), _f64(kbar)
+    Cq, d = qbar.shape
+    Ck = kbar.shape[0]
+    lr = np.empty((Cq, Ck), np.float64)
+    _check(lib().svgo_score_log(Cq, Ck, d, qbar, _i32(counts_q), kbar, _i32(counts_k), lr))
+    return lr
+
+
 def budget(rho: float, Nq: int, Nk: int) -> int:
     return int(lib().svgo_budget(float(rho), int(Nq), int(Nk)))
 
@@ -192,6 +204,24 @@ def route(ratio, counts_q, counts_k, rho: Optional[float] = None, Nq: Optional[i
     return mask, int(used)
 
 
+def route_rows(ratio, counts_q, counts_k, rho: float, Nk: int):
+    """Per-query-cluster budgets (the review page's future-work reading of the
+    density budget: one budget per query cluster).  Row c is routed on its own
+    with the greedy rule of ``route`` and the budget floor((rho * n_c) * Nk),
+    i.e. the head budget formula with the row's query count.  Returns
+    (mask[Cq, Ck] uint8, total selected cost over the rows)."""
+    ratio = _f64(ratio)
+    Cq, Ck = ratio.shape
+    cq = _i32(counts_q)
+    mask = np.empty((Cq, Ck), np.uint8)
+    total = 0
+    for c in range(Cq):
+        m, used = route(ratio[c:c + 1], cq[c:c + 1], counts_k, budget_pairs=budget(rho, int(cq[c]), Nk))
+        mask[c] = m[0]
+        total += used
+    return mask, total
+
+
 def hybrid(Q, K, V, labels_q, labels_k, kbar, vbar, counts_k, mask, rows=None):
     """Hybrid attention output for query tokens ``rows`` (default: all), token order."""
     Q, K, V, kbar, vbar = _f64(Q), _f64(K), _f64(V), _f64(kbar), _f64(vbar)
@@ -208,8 +238,14 @@ def hybrid(Q, K, V, labels_q, labels_k, kbar, vbar, counts_k, mask, rows=None):
 
 
 def forward_head(Q, K, V, init_q, init_k, Cq: int, Ck: int, rho: float, iters: int = 10,
-                 rows: Optional[Sequence[int]] = None, want_eps: bool = False) -> Dict[str, np.ndarray]:
-    """All five steps for one head; returns every intermediate and the output."""
+                 rows: Optional[Sequence[int]] = None, want_eps: bool = False, ratio_mode: str = "error",
+                 per_row: bool = False) -> Dict[str, np.ndarray]:
+    """All five steps for one head; returns every intermediate and the output.
+    ``ratio_mode``: "error" (the value-aware probe), "logit" (its logit-only
+    variant) or "score" (the attention-score comparator); ``per_row`` routes
+    with one budget per query cluster instead of one per head."""
+    if ratio_mode not in ("error", "logit", "score"):
+        raise ValueError("ratio_mode must be error, logit or score")
     Q, K, V = _f64(Q), _f64(K), _f64(V)
     Nq, Nk = Q.shape[0], K.shape[0]
     lq, qbar, cq = kmeans(Q, Cq, init_q, iters)
@@ -217,10 +253,17 @@ def forward_head(Q, K, V, init_q, init_k, Cq: int, Ck: int, rho: float, iters: i
     cq2, offq, permq, invq = permutation(lq, Cq)
     ck2, offk, permk, invk = permutation(lk, Ck)
     vbar = group_means(V, lk, Ck)
-    pr = probe_log(qbar, cq, K, V, lk, kbar, vbar, ck, want_eps=want_eps)
-    log_ratio, log_eps = pr if want_eps else (pr, None)
+    if ratio_mode == "score":
+        log_ratio, log_eps = score_log(qbar, cq, kbar, ck), None
+        want_eps = False
+    else:
+        pr = probe_log(qbar, cq, K, V, lk, kbar, vbar, ck, want_eps=want_eps, logit_only=ratio_mode == "logit")
+        log_ratio, log_eps = pr if want_eps else (pr, None)
     # ln is increasing, so routing on ln r visits blocks in the order of r
-    mask, used = route(log_ratio, cq, ck, rho, Nq, Nk)
+    if per_row:
+        mask, used = route_rows(log_ratio, cq, ck, rho, Nk)
+    else:
+        mask, used = route(log_ratio, cq, ck, rho, Nq, Nk)
     O = hybrid(Q, K, V, lq, lk, kbar, vbar, ck, mask, rows)
     with np.errstate(over="ignore"):
         ratio = np.exp(log_ratio)

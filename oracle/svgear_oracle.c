@@ -313,6 +313,44 @@ int svgo_probe_log(int Cq, int Nk, int Ck, int d, const double* qbar, const int3
     return err;
 }
 
+/* Attention-score comparator: the selection rule the pages argue against
+ * ([R] novelty paragraph: score-based selection is misaligned with the output
+ * error once a compensation branch exists; [DE] 1 and 2B; [IT] 1).  The pages
+ * give no formula for the score; read here as the centroid estimate of the
+ * attention mass that query cluster c puts on key cluster g,
+ *     P[c, g] = m_g e^{tau qbar_c.kbar_g} / sum_{g'} m_g' e^{tau qbar_c.kbar_g'}
+ * (each key of g stands in as its centroid), with the value-to-cost rule of
+ * the error-aware router: block value n_c P[c, g], cost n_c m_g, so
+ *     ln r[c, g] = tau qbar_c.kbar_g - ln sum_{g'} m_g' e^{tau qbar_c.kbar_g'},
+ * the sum over non-empty clusters, taken as a log-sum-exp; -inf where
+ * n_c m_g = 0. */
+int svgo_score_log(int Cq, int Ck, int d, const double* qbar, const int32_t* counts_q,
+                   const double* kbar, const int32_t* counts_k, double* log_ratio)
+{
+    if (Cq <= 0 || Ck <= 0 || d <= 0 || !qbar || !counts_q || !kbar || !counts_k || !log_ratio)
+        return SVGO_EARG;
+    const double tau = 1.0 / sqrt((double)d);
+    double* sb = (double*)malloc(sizeof(double) * (size_t)Ck);
+    if (!sb) return SVGO_ENOMEM;
+    for (int c = 0; c < Cq; ++c) {
+        double mx = -INFINITY;
+        for (int g = 0; g < Ck; ++g) {
+            double s = 0.0;
+            for (int t = 0; t < d; ++t) s += qbar[(size_t)c * d + t] * kbar[(size_t)g * d + t];
+            sb[g] = tau * s;
+            if (counts_k[g] > 0 && sb[g] + log((double)counts_k[g]) > mx) mx = sb[g] + log((double)counts_k[g]);
+        }
+        double sum = 0.0;
+        for (int g = 0; g < Ck; ++g)
+            if (counts_k[g] > 0) sum += exp(sb[g] + log((double)counts_k[g]) - mx);
+        const double lse = mx + log(sum);
+        for (int g = 0; g < Ck; ++g)
+            log_ratio[(size_t)c * Ck + g] = (counts_q[c] > 0 && counts_k[g] > 0) ? sb[g] - lse : -INFINITY;
+    }
+    free(sb);
+    return SVGO_OK;
+}
+
 /* Density budget in (query, key) pairs: floor(rho * Nq * Nk), evaluated as
  * (rho * Nq) * Nk in fp64 ([R] step 3, "density budget rho"). */
 int64_t svgo_budget(double rho, int Nq, int Nk)

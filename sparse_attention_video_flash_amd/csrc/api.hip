@@ -107,7 +107,6 @@ SVG_HIDDEN int read_device_error(const int* err, hipStream_t st)
     return v;
 }
 
-SVG_HIDDEN void zero_words(void* p, size_t bytes, hipStream_t st);
 
 }  // namespace svg
 
@@ -288,7 +287,10 @@ SVG_API int svgear_probe(const svgear_shape* shape, const float* qbar, const int
 {
     int rc = check_shape(shape);
     if (rc) return rc;
-    if (flags & ~(SVGEAR_DEBUG_EPS | SVGEAR_DEBUG_SYNC | SVGEAR_PROBE_LOGIT)) return SVGEAR_E_ARG;
+    if (flags & ~(SVGEAR_DEBUG_EPS | SVGEAR_DEBUG_SYNC | SVGEAR_PROBE_LOGIT | SVGEAR_PROBE_SCORE))
+        return SVGEAR_E_ARG;
+    if ((flags & SVGEAR_PROBE_SCORE) && (flags & (SVGEAR_PROBE_LOGIT | SVGEAR_DEBUG_EPS)))
+        return SVGEAR_E_ARG;
     rc = check_ptrs({qbar, counts_q, Kp, Vp, kbar, vbar, counts_k, offsets_k, log_ratio});
     if (rc) return rc;
     if (flags & SVGEAR_DEBUG_EPS) {
@@ -330,6 +332,32 @@ SVG_API int svgear_route(const svgear_shape* shape, double rho, const float* log
     a.mask = mask;
     a.sel_cost = sel_cost;
     return finish(launch_route(a, (hipStream_t)stream), 0, (hipStream_t)stream, nullptr);
+}
+
+SVG_API int svgear_route_rows(const svgear_shape* shape, double rho, const float* log_ratio,
+                              const int32_t* counts_q, const int32_t* counts_k, uint8_t* mask,
+                              int64_t* sel_cost, void* ws, size_t ws_bytes, void* stream)
+{
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    if (!(rho >= 0.0 && rho <= 1.0)) return SVGEAR_E_RHO;
+    rc = check_ptrs({log_ratio, counts_q, counts_k, mask, sel_cost});
+    if (rc) return rc;
+    Layout L;
+    rc = check_ws(shape, ws, ws_bytes, &L);
+    if (rc) return rc;
+    RouteArgs a;
+    a.H = shape->H;
+    a.Cq = shape->Cq;
+    a.Ck = shape->Ck;
+    a.budget = 0;
+    a.log_ratio = log_ratio;
+    a.counts_q = counts_q;
+    a.counts_k = counts_k;
+    a.mask = mask;
+    a.sel_cost = sel_cost;
+    return finish(launch_route_rows(a, rho, shape->Nk, (hipStream_t)stream), 0, (hipStream_t)stream,
+                  nullptr);
 }
 
 static int attention_impl(const svgear_shape* shape, const void* Qp, const int32_t* offsets_q,

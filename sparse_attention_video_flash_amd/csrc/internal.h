@@ -188,6 +188,8 @@ struct RouteArgs {
     int64_t* sel_cost;
 };
 SVG_HIDDEN hipError_t launch_route(const RouteArgs& a, hipStream_t st);
+SVG_HIDDEN hipError_t launch_route_rows(const RouteArgs& a, double rho, int Nk, hipStream_t st);
+SVG_HIDDEN void zero_words(void* p, size_t bytes, hipStream_t st);
 
 struct AttnArgs {
     int H, Nq, Nk, d, Cq, Ck, dtype;

@@ -84,6 +84,45 @@ __global__ __launch_bounds__(256) void k_sbar(const float* __restrict__ qbar,
     sbar[((size_t)h * Cq + c) * Ck + g] = (float)(tau * s);
 }
 
+// Attention-score comparator: row c of ln r is sbar[c, g] minus the row's
+// log-sum-exp of sbar[c, g'] + ln m_g' over non-empty key clusters, so
+// m_g e^{ln r} is the centroid estimate of the attention mass on block (c, g).
+// One workgroup per (c, h); max and sum are block reductions in fp32.
+__global__ __launch_bounds__(256) void k_score_ratio(const float* __restrict__ sbar,
+                                                     const int32_t* __restrict__ counts_q,
+                                                     const int32_t* __restrict__ counts_k, int Cq,
+                                                     int Ck, float* __restrict__ log_ratio)
+{
+    __shared__ float s_red[256];
+    const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+    const float* sb = sbar + ((size_t)h * Cq + c) * Ck;
+    const int32_t* ck = counts_k + (size_t)h * Ck;
+    float mx = -INFINITY;
+    for (int g = tid; g < Ck; g += 256)
+        if (ck[g] > 0) mx = fmaxf(mx, sb[g] + logf((float)ck[g]));
+    s_red[tid] = mx;
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+        if (tid < off) s_red[tid] = fmaxf(s_red[tid], s_red[tid + off]);
+        __syncthreads();
+    }
+    mx = s_red[0];
+    __syncthreads();
+    float sum = 0.0f;
+    for (int g = tid; g < Ck; g += 256)
+        if (ck[g] > 0) sum += expf(sb[g] + logf((float)ck[g]) - mx);
+    s_red[tid] = sum;
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+        if (tid < off) s_red[tid] += s_red[tid + off];
+        __syncthreads();
+    }
+    const float lse = mx + logf(s_red[0]);
+    const bool row_ok = counts_q[(size_t)h * Cq + c] > 0;
+    float* out = log_ratio + ((size_t)h * Cq + c) * Ck;
+    for (int g = tid; g < Ck; g += 256) out[g] = (row_ok && ck[g] > 0) ? sb[g] - lse : -INFINITY;
+}
+
 // Generic probe: one block per key cluster g, one thread per query cluster c.
 // The differences kbar_g - k_j of the cluster's keys are staged in LDS 32 at a
 // time, so D = tau qbar.(kbar_g - k_j) is formed directly: it is exactly zero
@@ -165,6 +204,13 @@ static hipError_t run_probe(const ProbeArgs& a, hipStream_t st)
     float2* keys = (float2*)(a.scratch + L.pr_keys);
     float* pg = (float*)(a.scratch + L.pr_pg);
     const float tau = 1.0f / sqrtf((float)D);
+    if (a.flags & SVGEAR_PROBE_SCORE) {
+        hipLaunchKernelGGL((k_sbar<D>), dim3(a.Cq, (a.Ck + 255) / 256, a.H), dim3(256), 0, st, a.qbar,
+                           a.kbar, a.Cq, a.Ck, 1.0 / sqrt((double)D), sbar);
+        hipLaunchKernelGGL(k_score_ratio, dim3(a.Cq, a.H), dim3(256), 0, st, sbar, a.counts_q,
+                           a.counts_k, a.Cq, a.Ck, a.log_ratio);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL((k_key_scalars<T, D>), dim3(a.Ck, a.H), dim3(256), 0, st, (const T*)a.Vp,
                        a.vbar, a.offsets_k, a.Nk, a.Ck, keys, pg, (a.flags & SVGEAR_PROBE_LOGIT) ? 1 : 0);
     hipLaunchKernelGGL((k_sbar<D>), dim3(a.Cq, (a.Ck + 255) / 256, a.H), dim3(256), 0, st, a.qbar,

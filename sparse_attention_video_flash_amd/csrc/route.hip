@@ -149,4 +149,95 @@ SVG_HIDDEN hipError_t launch_route(const RouteArgs& a, hipStream_t st)
     return hipGetLastError();
 }
 
+// ----------------------------------------------------------------------------- per-cluster budgets
+//
+// The other reading of the budget ([R] future-work paragraph: one density
+// budget for every query cluster): query cluster c may spend
+// B_c = floor((rho * n_c) * Nk) pairs on its own row of blocks, chosen greedily
+// in descending ratio order (equal ratios: lower key-cluster index first), the
+// longest prefix that fits.  One workgroup per (head, row): the row's order
+// keys are sorted in LDS (bitonic, 64-bit keys = descending order key, then
+// index), then an inclusive cost scan marks the prefix.  The row's selected
+// cost is added to sel_cost[h] (integer atomics, exact).
+constexpr int kRowThreads = 256;
+constexpr int kRowMax = 4096;
+
+__global__ __launch_bounds__(kRowThreads) void k_route_rows(const float* __restrict__ log_ratio,
+                                                            const int32_t* __restrict__ counts_q,
+                                                            const int32_t* __restrict__ counts_k,
+                                                            int Cq, int Ck, int Nk, double rho,
+                                                            uint8_t* __restrict__ mask,
+                                                            unsigned long long* __restrict__ sel_cost)
+{
+    __shared__ unsigned long long s_key[kRowMax];
+    __shared__ long long s_part[kRowThreads];
+    const int c = blockIdx.x, h = blockIdx.y;
+    const int tid = threadIdx.x;
+    int n = 1;
+    while (n < Ck) n <<= 1;
+    const float* lr = log_ratio + ((size_t)h * Cq + c) * Ck;
+    for (int i = tid; i < n; i += kRowThreads)
+        s_key[i] = i < Ck ? ((unsigned long long)(~order_key(lr[i])) << 32) | (unsigned)i : ~0ull;
+    __syncthreads();
+    for (int k = 2; k <= n; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = tid; i < n; i += kRowThreads) {
+                const int l = i ^ j;
+                if (l > i) {
+                    const unsigned long long a = s_key[i], b = s_key[l];
+                    const bool up = (i & k) == 0;
+                    if ((a > b) == up) {
+                        s_key[i] = b;
+                        s_key[l] = a;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    // costs in sorted order, thread-contiguous runs, then a block scan of the runs
+    const long long nc = counts_q[(size_t)h * Cq + c];
+    const int32_t* ck = counts_k + (size_t)h * Ck;
+    const long long budget = (long long)floor((rho * (double)nc) * (double)Nk);
+    const int per = (Ck + kRowThreads - 1) / kRowThreads;
+    const int p0 = tid * per;
+    long long run = 0;
+    for (int k = 0; k < per && p0 + k < Ck; ++k) run += nc * ck[(int)(s_key[p0 + k] & 0xffffffffu)];
+    s_part[tid] = run;
+    __syncthreads();
+    for (int off = 1; off < kRowThreads; off <<= 1) {
+        const long long v = tid >= off ? s_part[tid - off] : 0;
+        __syncthreads();
+        s_part[tid] += v;
+        __syncthreads();
+    }
+    long long cum = s_part[tid] - run;
+    long long mine = 0;
+    uint8_t* mrow = mask + ((size_t)h * Cq + c) * Ck;
+    for (int k = 0; k < per && p0 + k < Ck; ++k) {
+        const int g = (int)(s_key[p0 + k] & 0xffffffffu);
+        const long long w = nc * ck[g];
+        cum += w;
+        const bool take = cum <= budget;
+        mrow[g] = take ? 1 : 0;
+        if (take) mine += w;
+    }
+    s_part[tid] = mine;
+    __syncthreads();
+    if (tid == 0) {
+        long long tot = 0;
+        for (int k = 0; k < kRowThreads; ++k) tot += s_part[k];
+        atomicAdd(sel_cost + h, (unsigned long long)tot);
+    }
+}
+
+SVG_HIDDEN hipError_t launch_route_rows(const RouteArgs& a, double rho, int Nk, hipStream_t st)
+{
+    zero_words(a.sel_cost, (size_t)a.H * 8, st);
+    hipLaunchKernelGGL(k_route_rows, dim3(a.Cq, a.H), dim3(kRowThreads), 0, st, a.log_ratio,
+                       a.counts_q, a.counts_k, a.Cq, a.Ck, Nk, rho, a.mask,
+                       (unsigned long long*)a.sel_cost);
+    return hipGetLastError();
+}
+
 }  // namespace svg

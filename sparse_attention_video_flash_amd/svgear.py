@@ -15,9 +15,9 @@ LIB_PATH = os.path.join(PKG, "libsvgear.so")
 
 OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_WORKSPACE, E_RHO, E_HIP, E_ARG = 0, -1, -2, -3, -4, -5, -6, -7, -8
 F32, BF16 = 0, 1
-LABELS_GIVEN, DEBUG_EPS, DEBUG_SYNC, PROBE_LOGIT = 1, 2, 4, 8
+LABELS_GIVEN, DEBUG_EPS, DEBUG_SYNC, PROBE_LOGIT, PROBE_SCORE = 1, 2, 4, 8, 16
 
-EXPORTS = ("svgear_workspace_bytes", "svgear_cluster", "svgear_probe", "svgear_route",
+EXPORTS = ("svgear_workspace_bytes", "svgear_cluster", "svgear_probe", "svgear_route", "svgear_route_rows",
            "svgear_attention", "svgear_forward", "svgear_status_string", "svgear_version")
 
 
@@ -59,6 +59,7 @@ def load():
                                      vp, sz, vp]
         L.svgear_probe.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
         L.svgear_route.argtypes = [sp, f64, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.svgear_route_rows.argtypes = [sp, f64, vp, vp, vp, vp, vp, vp, sz, vp]
         L.svgear_attention.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.svgear_forward.argtypes = [sp, f64, vp, vp, vp, vp, vp, vp, ctypes.POINTER(Intermediates),
                                      vp, sz, vp]
@@ -143,6 +144,14 @@ def route(shape: Shape, rho: float, log_ratio, counts_q, counts_k, mask, sel_cos
     rc = load().svgear_route(ctypes.byref(shape), float(rho), _ptr(log_ratio), _ptr(counts_q), _ptr(counts_k),
                              _ptr(mask), _ptr(sel_cost), _ptr(ws), ws.numel(), _stream(stream))
     _check(rc, "svgear_route")
+
+
+def route_rows(shape: Shape, rho: float, log_ratio, counts_q, counts_k, mask, sel_cost, ws, stream=None):
+    """Route with one budget per query cluster (same arguments as ``route``)."""
+    rc = load().svgear_route_rows(ctypes.byref(shape), float(rho), _ptr(log_ratio), _ptr(counts_q),
+                                  _ptr(counts_k), _ptr(mask), _ptr(sel_cost), _ptr(ws), ws.numel(),
+                                  _stream(stream))
+    _check(rc, "svgear_route_rows")
 
 
 def attention(shape: Shape, Qp, offsets_q, perm_q, Kp, Vp, kbar, vbar, counts_k, offsets_k, mask, O, ws,

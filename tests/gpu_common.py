@@ -111,10 +111,10 @@ def log_close(l_gpu, l_ref, l_floor, rtol=1e-3):
     return bad, np.where(both_zero, 0.0, dev)
 
 
-def near_threshold_ok(mask_gpu, mask_ref, log_ratio):
-    """Mask mismatches are allowed only for blocks within 1e-5 relative of the
+def near_threshold_ok(mask_gpu, mask_ref, log_ratio, tol=1e-5):
+    """Mask mismatches are allowed only for blocks within ``tol`` relative of the
     oracle's selection threshold (the ratio of the first unselected block):
-    |ln r - ln r_thr| <= 1e-5.  Returns the number of mismatches (asserts)."""
+    |ln r - ln r_thr| <= tol.  Returns the number of mismatches (asserts)."""
     diff = mask_gpu != mask_ref
     if not diff.any():
         return 0
@@ -124,7 +124,7 @@ def near_threshold_ok(mask_gpu, mask_ref, log_ratio):
     assert nsel < flat.size, "mask differs although every block is selected"
     thr = flat[order[nsel]]
     with np.errstate(invalid="ignore"):
-        near = (log_ratio == thr) | (np.abs(log_ratio - thr) <= 1e-5)
+        near = (log_ratio == thr) | (np.abs(log_ratio - thr) <= tol)
     assert (~diff | near).all(), ("mask mismatch away from the threshold", int(diff.sum()))
     return int(diff.sum())
 

@@ -236,6 +236,41 @@ def test_route_mask_bit_exact_given_ratios(case):
     del Nq, Nk
 
 
+@pytest.mark.parametrize("Cq,Ck,N", [(8, 16, 256), (13, 37, 1380), (64, 256, 8192), (3, 4096, 8192)])
+def test_route_rows_bit_exact_given_ratios(Cq, Ck, N):
+    """Per-query-cluster budgets: mask and total cost bit-exact against the
+    oracle on continuous, tied and partly -inf ratios, from rho = 0 to 1,
+    including the largest key-cluster count (4096)."""
+    torch = torch_gpu()
+    log("route_rows Cq=%d Ck=%d" % (Cq, Ck))
+    rng = np.random.default_rng(Cq * 1000 + Ck)
+    H = 2
+    cq = rng.integers(0, 2 * N // Cq + 1, (H, Cq)).astype(np.int32)
+    ck = rng.integers(0, 2 * N // Ck + 1, (H, Ck)).astype(np.int32)
+    cq[:, 0] = 0
+    ck[:, 1] = 0
+    variants = {
+        "continuous": rng.standard_normal((H, Cq, Ck)).astype(np.float32) * 5,
+        "ties": rng.integers(-3, 3, (H, Cq, Ck)).astype(np.float32),
+        "with_-inf": np.where(rng.random((H, Cq, Ck)) < 0.2, -np.inf,
+                              rng.standard_normal((H, Cq, Ck))).astype(np.float32),
+    }
+    shape = sv.make_shape(H, N, N, 128, Cq, Ck, 10, sv.BF16)
+    ws = sv.alloc_workspace(shape)
+    mask = torch.empty(H, Cq, Ck, dtype=torch.uint8, device="cuda")
+    sel = torch.empty(H, dtype=torch.int64, device="cuda")
+    for name, lr in variants.items():
+        for rho in (0.0, 0.05, 0.3, 0.5, 1.0):
+            sv.route_rows(shape, rho, _dev(lr, torch.float32), _dev(cq, torch.int32), _dev(ck, torch.int32),
+                          mask, sel, ws)
+            torch.cuda.synchronize()
+            m, st = mask.cpu().numpy(), sel.cpu().numpy()
+            for h in range(H):
+                ref, used = oracle.route_rows(lr[h].astype(np.float64), cq[h], ck[h], rho, N)
+                np.testing.assert_array_equal(m[h], ref, err_msg="%s rho=%s head %d" % (name, rho, h))
+                assert st[h] == used
+
+
 # ----------------------------------------------------------------------------- step 4
 
 @pytest.mark.parametrize("case", ["tiny", "ragged", "small"])

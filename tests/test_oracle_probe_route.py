@@ -245,6 +245,52 @@ def test_logit_only_probe_ignores_values_and_vanishes_for_identical_keys():
 
 # ----------------------------------------------------------------------------- route
 
+def _dense_cluster_mass(q, K, labels, Ck, tau):
+    """Softmax of one query over every key, summed per key cluster (fp64)."""
+    s = tau * (K @ q)
+    p = np.exp(s - s.max())
+    p /= p.sum()
+    return np.bincount(labels, weights=p, minlength=Ck)
+
+
+@pytest.mark.parametrize("scale", [1.0, 40.0])
+def test_score_ratio_equals_dense_attention_mass_when_keys_sit_on_centroids(scale):
+    """When every key equals its cluster's centroid, the centroid estimate of
+    the block attention mass is the exact softmax mass over the real keys; at
+    scale 40 the logits reach several hundred (beyond a raw e^x in fp64)."""
+    rng = np.random.default_rng(21)
+    d, Cq, Ck = 32, 5, 7
+    kbar = rng.standard_normal((Ck, d)) * scale
+    ck = np.array([3, 0, 1, 5, 2, 4, 6], np.int32)        # one empty key cluster
+    labels = np.repeat(np.arange(Ck), ck).astype(np.int32)
+    K = kbar[labels]
+    qbar = rng.standard_normal((Cq, d)) * scale
+    cq = np.array([4, 1, 0, 2, 9], np.int32)               # one empty query cluster
+    lr = oracle.score_log(qbar, cq, kbar, ck)
+    tau = 1.0 / np.sqrt(d)
+    for c in range(Cq):
+        if cq[c] == 0:
+            assert np.all(lr[c] == -np.inf)
+            continue
+        mass = _dense_cluster_mass(qbar[c], K, labels, Ck, tau)
+        got = np.where(ck > 0, np.exp(lr[c]) * ck, 0.0)
+        np.testing.assert_allclose(got, mass, rtol=1e-12, atol=1e-300)
+        assert lr[c, 1] == -np.inf
+        assert abs(got.sum() - 1.0) < 1e-12
+
+
+def test_score_ratio_orders_blocks_by_centroid_logit_within_a_row():
+    """Within one row the ratio is the centroid logit minus a row constant, so
+    the order of blocks in a row is that of tau qbar.kbar, whatever the sizes."""
+    rng = np.random.default_rng(5)
+    d, Cq, Ck = 16, 3, 9
+    qbar, kbar = rng.standard_normal((Cq, d)), rng.standard_normal((Ck, d))
+    ck = rng.integers(1, 50, Ck).astype(np.int32)
+    lr = oracle.score_log(qbar, np.ones(Cq, np.int32), kbar, ck)
+    diff = lr - (qbar @ kbar.T) / np.sqrt(d)
+    np.testing.assert_allclose(diff, diff[:, :1].repeat(Ck, 1), rtol=0, atol=1e-12)
+
+
 @pytest.mark.parametrize("seed", range(6))
 def test_greedy_equals_enumerated_optimum_for_equal_costs(seed):
     """All clusters of equal size: every block costs the same, and greedy by
@@ -332,6 +378,44 @@ def test_route_invariants():
         if prev is not None:
             assert (prev <= mask).all(), "masks nest as the density grows"
         prev = mask
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_route_rows_matches_naive_per_row_selection(seed):
+    """Per-query-cluster budgets: every row is the greedy prefix of its own
+    descending order under floor(rho * n_c * Nk), computed here with exact
+    rational arithmetic; the rows' total never exceeds the per-head budget."""
+    from fractions import Fraction
+    rng = np.random.default_rng(300 + seed)
+    Cq, Ck = 6, 8
+    cq = rng.integers(0, 9, Cq).astype(np.int32)
+    ck = rng.integers(0, 7, Ck).astype(np.int32)
+    ratio = rng.integers(0, 5, (Cq, Ck)).astype(np.float64)
+    Nq, Nk = int(cq.sum()), int(ck.sum())
+    for rho in (0.0, 0.125, 0.3, 0.5, 1.0):
+        mask, total = oracle.route_rows(ratio, cq, ck, rho, Nk)
+        got_total = 0
+        for c in range(Cq):
+            Bc = int(Fraction(rho) * int(cq[c]) * Nk)
+            ref, used = _naive_route(ratio[c:c + 1], cq[c:c + 1], ck, Bc)
+            np.testing.assert_array_equal(mask[c], ref[0], err_msg="row %d rho %g" % (c, rho))
+            assert used <= Bc
+            got_total += used
+        assert total == got_total <= oracle.budget(rho, Nq, Nk)
+        if rho == 1.0:
+            assert mask.all()
+
+
+def test_route_rows_single_query_cluster_is_head_route():
+    """With one query cluster the row budget is the head budget."""
+    rng = np.random.default_rng(7)
+    ck = rng.integers(1, 9, 20).astype(np.int32)
+    cq = np.array([37], np.int32)
+    ratio = rng.standard_normal((1, 20))
+    Nk = int(ck.sum())
+    for rho in (0.1, 0.4, 0.9):
+        np.testing.assert_array_equal(oracle.route_rows(ratio, cq, ck, rho, Nk)[0],
+                                      oracle.route(ratio, cq, ck, rho, 37, Nk)[0])
 
 
 GOLDEN_BUDGETS = "tests/golden/budgets.txt"
