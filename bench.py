@@ -137,15 +137,79 @@ def traffic_entry(kernel_file):
     return rec.get("bytes_per_launch")
 
 
+VARIANTS = (("error", False), ("logit", False), ("score", False), ("error", True), ("score", True))
+
+
+def quality(w, torch, dev, row_stride):
+    """Output error of the routing variants against dense attention at equal
+    density: one clustering (svgear_forward), then per variant and rho the
+    variant's probe, route and hybrid attention through the per-stage entry
+    points.  Dense attention is evaluated in fp32 (torch, on the GPU) on every
+    row_stride-th query of every head.  Also times each variant's probe and
+    route stages (HIP events on the library's stream)."""
+    torch.backends.cuda.matmul.allow_tf32 = False
+    Q, K, V, iq, ik = upload(w, torch, dev)
+    shape = sv.make_shape(w.H, w.N, w.N, w.d, w.Cq, w.Ck, w.iters, sv.BF16 if w.dtype == "bf16" else sv.F32)
+    ws = sv.alloc_workspace(shape, dev)
+    im = sv.alloc_intermediates(shape, dev)
+    O = torch.empty_like(Q)
+    sv.forward(shape, w.rhos[0], Q, K, V, iq, ik, O, ws, im)
+    rows = torch.arange(0, w.N, row_stride, device=dev)
+    tau = 1.0 / np.sqrt(w.d)
+    dense = torch.empty(w.H, rows.numel(), w.d, device=dev)
+    for h in range(w.H):
+        s = (Q[h, rows].float() @ K[h].float().T.contiguous()) * tau
+        dense[h] = torch.softmax(s, dim=1) @ V[h].float()
+    torch.cuda.synchronize()
+    log("quality: clustering and dense reference ready")
+    flags = {"error": 0, "logit": sv.PROBE_LOGIT, "score": sv.PROBE_SCORE}
+    head_groups = [("all", list(range(w.H)))]
+    if w.name == "stress":
+        head_groups += [("mixture heads 0-7", list(range(8))), ("student-t heads 8-15", list(range(8, 16)))]
+    table = []
+    for mode, per_row in VARIANTS:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        for rho in w.rhos:
+            ev[0].record()
+            sv.probe(shape, im["qbar"], im["counts_q"], im["Kp"], im["Vp"], im["kbar"], im["vbar"],
+                     im["counts_k"], im["offsets_k"], im["log_ratio"], ws, flags=flags[mode])
+            ev[1].record()
+            (sv.route_rows if per_row else sv.route)(shape, rho, im["log_ratio"], im["counts_q"],
+                                                    im["counts_k"], im["mask"], im["sel_cost"], ws)
+            ev[2].record()
+            sv.attention(shape, im["Qp"], im["offsets_q"], im["perm_q"], im["Kp"], im["Vp"], im["kbar"],
+                         im["vbar"], im["counts_k"], im["offsets_k"], im["mask"], O, ws)
+            torch.cuda.synchronize()
+            diff = (O[:, rows].float() - dense).pow(2).sum(dim=(1, 2))
+            ref = dense.pow(2).sum(dim=(1, 2))
+            density = float(im["sel_cost"].double().sum()) / (float(w.N) * w.N * w.H)
+            entry = {"variant": mode + (" per-row budget" if per_row else ""), "rho": rho,
+                     "density": round(density, 5), "probe_ms": round(ev[0].elapsed_time(ev[1]), 4),
+                     "route_ms": round(ev[1].elapsed_time(ev[2]), 4)}
+            for name, hs in head_groups:
+                entry["rel_l2 " + name] = float(np.sqrt(float(diff[hs].sum()) / float(ref[hs].sum())))
+            table.append(entry)
+            log("quality %s" % json.dumps(entry))
+    return {"experiment": "routing quality at equal density vs dense attention",
+            "workload": "%s: %d heads x %d tokens, d=%d, Cq=%d, Ck=%d" % (w.name, w.H, w.N, w.d, w.Cq, w.Ck),
+            "rows": "every %dth query row of every head (%d per head), dense attention in fp32"
+                    % (row_stride, rows.numel()),
+            "results": table}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="wan", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default=None, choices=sorted(WORKLOADS),
+                    help="default: wan (stress with --quality)")
     ap.add_argument("--rho", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows-stride", type=int, default=1)
+    ap.add_argument("--quality", action="store_true",
+                    help="compare the routing variants' output error against dense attention and exit")
+    ap.add_argument("--quality-row-stride", type=int, default=16)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -169,8 +233,12 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     sv.load()
     dev = torch.device("cuda:0")
-    w = WORKLOADS[args.workload]
+    w = WORKLOADS[args.workload or "wan"]
     rho = w.rhos[0] if args.rho is None else args.rho
+    if args.quality:
+        wq = WORKLOADS[args.workload or "stress"]
+        print(json.dumps(quality(wq, torch, dev, args.quality_row_stride)), flush=True)
+        return
     t = time.perf_counter()
     Q, K, V, iq, ik = upload(w, torch, dev)
     torch.cuda.synchronize()

@@ -73,6 +73,9 @@ def lib():
             L.svgo_probe_log.argtypes = [i32, i32, i32, i32, _F64P, _I32P, _F64P, _F64P, _I32P, _F64P,
                                          _F64P, _I32P, _ptr_or_null(_F64P), _F64P, i32]
             L.svgo_score_log.argtypes = [i32, i32, i32, _F64P, _I32P, _F64P, _I32P, _F64P]
+            L.svgo_route_optimal.argtypes = [i32, i32, _F64P, _I32P, _I32P, i64, _U8P,
+                                             ctypes.POINTER(ctypes.c_double)]
+            L.svgo_route_optimal.restype = i64
             L.svgo_budget.argtypes = [f64, i32, i32]
             L.svgo_budget.restype = i64
             L.svgo_route.argtypes = [i32, i32, _F64P, _I32P, _I32P, i64, _U8P]
@@ -202,6 +205,32 @@ def route(ratio, counts_q, counts_k, rho: Optional[float] = None, Nq: Optional[i
     if used < 0:
         raise ValueError("oracle route rejected its arguments (code %d)" % used)
     return mask, int(used)
+
+
+def route_optimal(log_ratio, counts_q, counts_k, budget_pairs: int):
+    """Exact 0-1 knapsack selection (dynamic programming over integer costs):
+    (mask, selected cost, value) with value = sum over selected blocks of
+    cost * e^{ln r - max ln r}; greedy's value on the same scale is
+    ``knapsack_value(mask, ...)``."""
+    lr = _f64(log_ratio)
+    Cq, Ck = lr.shape
+    mask = np.empty((Cq, Ck), np.uint8)
+    val = ctypes.c_double(0.0)
+    used = lib().svgo_route_optimal(Cq, Ck, lr, _i32(counts_q), _i32(counts_k), int(budget_pairs), mask,
+                                    ctypes.byref(val))
+    if used < 0:
+        raise ValueError("oracle knapsack rejected its arguments (code %d)" % used)
+    return mask, int(used), float(val.value)
+
+
+def knapsack_value(mask, log_ratio, counts_q, counts_k) -> float:
+    """sum over selected blocks of cost * e^{ln r - max finite ln r}."""
+    lr = np.asarray(log_ratio, np.float64)
+    shift = lr[np.isfinite(lr)].max() if np.isfinite(lr).any() else 0.0
+    cost = np.outer(np.asarray(counts_q, np.float64), np.asarray(counts_k, np.float64))
+    with np.errstate(under="ignore"):
+        v = np.where(np.isfinite(lr), cost * np.exp(lr - shift), 0.0)
+    return float(v[np.asarray(mask, bool)].sum())
 
 
 def route_rows(ratio, counts_q, counts_k, rho: float, Nk: int):

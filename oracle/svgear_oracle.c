@@ -404,6 +404,66 @@ int64_t svgo_route(int Cq, int Ck, const double* ratio, const int32_t* counts_q,
     return used;
 }
 
+/* Exact 0-1 knapsack over the blocks, the optimum that the greedy rule
+ * approximates ([R] weaknesses paragraph: greedy selection is an approximate
+ * 0-1 knapsack; dynamic programming is named as the exact alternative).
+ * Block b = c*Ck+g has integer weight w_b = counts_q[c] * counts_k[g] and value
+ * val_b = w_b * e^{log_ratio_b - shift}, shift = the largest finite log_ratio
+ * (a common factor, so the optimum is that of the unscaled values; blocks with
+ * log_ratio = -inf have value 0).  Classic DP over capacities 0..budget:
+ * best[w] = max(best[w], best[w - w_b] + val_b) item by item, with one bit per
+ * (item, capacity) recording a take, then a backward walk from capacity
+ * budget.  Of several optimal sets the walk returns one; the value is unique.
+ * Returns the selected weight and writes mask and *value (in the shifted
+ * scale), or a negative error code; SVGO_ENOMEM also when the bit table
+ * (blocks x (budget + 1) bits) exceeds 2^33 bits. */
+int64_t svgo_route_optimal(int Cq, int Ck, const double* log_ratio, const int32_t* counts_q,
+                           const int32_t* counts_k, int64_t budget, uint8_t* mask, double* value)
+{
+    if (Cq <= 0 || Ck <= 0 || !log_ratio || !counts_q || !counts_k || !mask || budget < 0)
+        return SVGO_EARG;
+    const size_t nb = (size_t)Cq * Ck, cap = (size_t)budget + 1;
+    if ((double)nb * (double)cap > 8589934592.0) return SVGO_ENOMEM;
+    double shift = -INFINITY;
+    for (size_t b = 0; b < nb; ++b)
+        if (isfinite(log_ratio[b]) && log_ratio[b] > shift) shift = log_ratio[b];
+    const size_t row_bytes = (cap + 7) / 8;
+    uint8_t* take = (uint8_t*)calloc(nb, row_bytes);
+    double* best = (double*)calloc(cap, sizeof(double));
+    if (!take || !best) {
+        free(take);
+        free(best);
+        return SVGO_ENOMEM;
+    }
+    for (size_t b = 0; b < nb; ++b) {
+        const int64_t wb = (int64_t)counts_q[b / Ck] * (int64_t)counts_k[b % Ck];
+        const double vb = isfinite(log_ratio[b]) ? (double)wb * exp(log_ratio[b] - shift) : 0.0;
+        if (wb > budget) continue;
+        uint8_t* tb = take + b * row_bytes;
+        for (int64_t w = budget; w >= wb; --w) {
+            const double cand = best[w - wb] + vb;
+            if (cand > best[w]) {
+                best[w] = cand;
+                tb[w >> 3] |= (uint8_t)(1u << (w & 7));
+            }
+        }
+    }
+    memset(mask, 0, nb);
+    int64_t w = budget, used = 0;
+    for (size_t b = nb; b-- > 0;) {
+        if (take[b * row_bytes + (w >> 3)] & (1u << (w & 7))) {
+            const int64_t wb = (int64_t)counts_q[b / Ck] * (int64_t)counts_k[b % Ck];
+            mask[b] = 1;
+            used += wb;
+            w -= wb;
+        }
+    }
+    *value = best[budget];
+    free(take);
+    free(best);
+    return used;
+}
+
 /* Hybrid attention output ([R] step 4; [DE] 2A).  For query i of cluster
  * c = labels_q[i], one softmax runs over
  *   exact terms        tau*q_i.k_j                for keys j with mask[c, labels_k[j]] = 1,

@@ -418,6 +418,46 @@ def test_route_rows_single_query_cluster_is_head_route():
                                       oracle.route(ratio, cq, ck, rho, 37, Nk)[0])
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_knapsack_optimum_equals_enumeration(seed):
+    """The DP optimum against every subset of a 3 x 4 grid (4096 subsets), with
+    ties, empty clusters and -inf ratios; the greedy value never exceeds it."""
+    rng = np.random.default_rng(500 + seed)
+    Cq, Ck = 3, 4
+    cq = rng.integers(0, 6, Cq).astype(np.int32)
+    ck = rng.integers(0, 6, Ck).astype(np.int32)
+    lr = rng.integers(-2, 3, (Cq, Ck)).astype(np.float64) * 0.7
+    lr[rng.random((Cq, Ck)) < 0.15] = -np.inf
+    cost = np.outer(cq, ck).astype(np.int64).reshape(-1)
+    for rho in (0.1, 0.3, 0.6):
+        B = oracle.budget(rho, int(cq.sum()), int(ck.sum()))
+        mask, used, val = oracle.route_optimal(lr, cq, ck, B)
+        best = 0.0
+        for bits in itertools.product((0, 1), repeat=Cq * Ck):
+            sel = np.array(bits, bool)
+            if cost[sel].sum() <= B:
+                best = max(best, oracle.knapsack_value(sel.reshape(Cq, Ck), lr, cq, ck))
+        assert val == pytest.approx(best, rel=1e-12, abs=1e-300)
+        assert used == int(cost[mask.reshape(-1) == 1].sum()) <= B
+        assert oracle.knapsack_value(mask, lr, cq, ck) == pytest.approx(val, rel=1e-12, abs=1e-300)
+        gmask, _ = oracle.route(lr, cq, ck, budget_pairs=B)
+        assert oracle.knapsack_value(gmask, lr, cq, ck) <= val * (1 + 1e-12)
+
+
+def test_knapsack_beats_greedy_where_a_large_block_blocks_the_prefix():
+    """Budget 10, costs 6, 5, 5, ratios 1.0, 0.9, 0.9: greedy takes the cost-6
+    block and stops (value 6); the optimum takes both cost-5 blocks (value 9)."""
+    cq = np.array([1], np.int32)
+    ck = np.array([6, 5, 5], np.int32)
+    lr = np.log(np.array([[1.0, 0.9, 0.9]]))
+    gmask, gused = oracle.route(lr, cq, ck, budget_pairs=10)
+    assert gmask.tolist() == [[1, 0, 0]] and gused == 6
+    mask, used, val = oracle.route_optimal(lr, cq, ck, 10)
+    assert mask.tolist() == [[0, 1, 1]] and used == 10
+    assert val == pytest.approx(9.0, rel=1e-15)
+    assert oracle.knapsack_value(gmask, lr, cq, ck) == pytest.approx(6.0, rel=1e-15)
+
+
 GOLDEN_BUDGETS = "tests/golden/budgets.txt"
 
 
