@@ -17,9 +17,10 @@
 //   1. compensation tiles: the centroids of the key clusters that are skipped
 //      for c and non-empty, split into bf16 hi + lo planes (k-bar and v-bar are
 //      fp32), with logit tau q.kbar_g + ln m_g;
-//   2. exact tiles: the keys of every routed key cluster, K and V
-//      double-buffered in LDS, the next tile's global loads in flight during
-//      the current tile's math.
+//   2. exact tiles: the keys of every routed key cluster, gathered by row
+//      index straight from global memory into LDS (buffer loads with the lds
+//      flag), two buffers, the next tile's loads in flight during the current
+//      tile's math.
 // One online softmax (base-2 exponent) covers both kinds of terms.
 //
 // Workgroups are ordered so that the query tiles of one cluster run
@@ -36,18 +37,32 @@ typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
-constexpr int AT_BM = 128;
+constexpr int AT_WAVES = 4;                  // 32 query rows per wave
+constexpr int AT_BM = 32 * AT_WAVES;
 constexpr int AT_BN = 64;
 constexpr int AT_D = 128;
-constexpr int AT_THREADS = 256;
-constexpr int K_PITCH = AT_D * 2 + 16;  // 272 B: 16 consecutive rows hit distinct banks (b128)
-constexpr int V_PITCH = AT_D * 2 + 64;  // 320 B: transpose reads of 4 rows x 2 column groups
-constexpr int K_BUF = AT_BN * K_PITCH;  // 17408
-constexpr int V_BUF = AT_BN * V_PITCH;  // 20480
-constexpr int AT_LDS = 2 * K_BUF + 2 * V_BUF + AT_BN * 4 + AT_BN * 4;
+constexpr int AT_THREADS = 64 * AT_WAVES;
+constexpr int ST_STEP = AT_THREADS / 16;     // rows staged per pass (16 lanes x 16 B per row)
+constexpr int ST_ROWS = AT_BN / ST_STEP;     // rows of a 64-row tile per thread
+// Key and value tiles: 64 rows of 256 B, unpadded, the 16-B chunks of each row
+// XOR-swizzled so that the score reads (16 rows, one chunk) and the transpose
+// reads (4 rows, 4 chunks) hit distinct banks.  The exact tiles are written
+// straight from global memory into LDS (one buffer load with the lds flag
+// fills 4 rows of one operand), two buffers deep.
+constexpr int ROW_B = AT_D * 2;          // 256
+constexpr int T_BUF = AT_BN * ROW_B;     // 16384
+constexpr int AT_NBUF = 2;
+constexpr int K_PITCH = AT_D * 2 + 16;   // output staging rows (272 B)
+constexpr int AT_LDS = AT_NBUF * 2 * T_BUF + AT_BN * 4 + AT_BN * 4;
+static_assert(AT_BM * K_PITCH <= AT_NBUF * 2 * T_BUF, "output staging fits the tile buffers");
+static_assert(ST_ROWS * ST_STEP == AT_BN, "staging covers a tile");
 constexpr int AT_XCD = 8;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// LDS chunk position of 16-B chunk c of tile row r (an involution in c).
+__device__ __forceinline__ int k_pos(int r, int c) { return c ^ (r & 15); }
+__device__ __forceinline__ int v_pos(int r, int c) { return c ^ ((r & 3) << 2); }
 
 // ----------------------------------------------------------------------------- prep kernels
 
@@ -177,8 +192,8 @@ __global__ __launch_bounds__(1024) void k_tile_prefix(const int32_t* __restrict_
 // source row map[r] (always a valid row: rows past the list are clamped and
 // masked out later).
 struct Stage {
-    u32x4_t k[4];
-    u32x4_t v[4];
+    u32x4_t k[ST_ROWS];
+    u32x4_t v[ST_ROWS];
 };
 
 __device__ __forceinline__ void stage_load(Stage& s, const bf16* __restrict__ K,
@@ -186,24 +201,10 @@ __device__ __forceinline__ void stage_load(Stage& s, const bf16* __restrict__ K,
 {
     const int kc = tid & 15, kr = tid >> 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const size_t row = (size_t)map[kr + 16 * i];
+    for (int i = 0; i < ST_ROWS; ++i) {
+        const size_t row = (size_t)map[kr + ST_STEP * i];
         s.k[i] = *(const u32x4_t*)(K + row * AT_D + kc * 8);
         s.v[i] = *(const u32x4_t*)(V + row * AT_D + kc * 8);
-    }
-}
-
-// Same staging for the exact tiles: rows row[i] of this head's K and V read
-// through buffer descriptors (32-bit byte offsets; reads past the head's last
-// row return zero instead of faulting).
-__device__ __forceinline__ void stage_load_rows(Stage& s, __amdgpu_buffer_rsrc_t rk,
-                                                __amdgpu_buffer_rsrc_t rv, const int row[4], int kc)
-{
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int off = row[i] * (AT_D * 2) + kc * 16;
-        s.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
-        s.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
     }
 }
 
@@ -211,9 +212,10 @@ __device__ __forceinline__ void stage_store(const Stage& s, char* kbuf, char* vb
 {
     const int kc = tid & 15, kr = tid >> 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        *(u32x4_t*)(kbuf + (kr + 16 * i) * K_PITCH + kc * 16) = s.k[i];
-        *(u32x4_t*)(vbuf + (kr + 16 * i) * V_PITCH + kc * 16) = s.v[i];
+    for (int i = 0; i < ST_ROWS; ++i) {
+        const int r = kr + ST_STEP * i;
+        *(u32x4_t*)(kbuf + r * ROW_B + k_pos(r, kc) * 16) = s.k[i];
+        *(u32x4_t*)(vbuf + r * ROW_B + v_pos(r, kc) * 16) = s.v[i];
     }
 }
 
@@ -232,13 +234,14 @@ __device__ __forceinline__ void tile_scores(f32x16_t acc[2], const char* kbuf, c
 {
     __builtin_amdgcn_s_setprio(1);
     const int row = lane & 31, half = lane >> 5;
-    const char* kr0 = kbuf + row * K_PITCH + half * 16;
-    const char* kr1 = kr0 + 32 * K_PITCH;
+    const char* kr0 = kbuf + row * ROW_B;
+    const char* kr1 = kr0 + 32 * ROW_B;   // row + 32: same swizzle
     f32x16_t a0 = acc[0], a1 = acc[1];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-        const bf16x8_t k0 = as_bf16x8(*(const u32x4_t*)(kr0 + s * 32));
-        const bf16x8_t k1 = as_bf16x8(*(const u32x4_t*)(kr1 + s * 32));
+        const int off = k_pos(row, 2 * s + half) * 16;
+        const bf16x8_t k0 = as_bf16x8(*(const u32x4_t*)(kr0 + off));
+        const bf16x8_t k1 = as_bf16x8(*(const u32x4_t*)(kr1 + off));
         a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[s], a0, 0, 0, 0);
         a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[s], a1, 0, 0, 0);
     }
@@ -316,14 +319,17 @@ __device__ __forceinline__ void tile_pv(Softmax& st, const char* vbuf, const bf1
     const int j = lane & 15, grp = lane >> 4;
     const int half = grp >> 1;
     // row 4 half + j / 4 (+16 kk, +8 for the second load), column 16 (grp & 1) + 4 (j & 3)
-    const char* base = vbuf + (4 * half + (j >> 2)) * V_PITCH + (16 * (grp & 1) + 4 * (j & 3)) * 2;
+    // + 32 db elements: chunk 2 (grp & 1) + (j & 3) / 2 + 4 db, whose swizzled
+    // position is the same chunk with db replaced by db ^ ((j >> 2) & 3).
+    const int jr = (j >> 2) & 3;
+    const char* base = vbuf + (4 * half + (j >> 2)) * ROW_B + (2 * (grp & 1) + ((j >> 1) & 1)) * 16 + (j & 1) * 8;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-            const char* a = base + (16 * kk) * V_PITCH + (32 * db) * 2;
+            const char* a = base + (16 * kk) * ROW_B + (db ^ jr) * 64;
             const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a);
-            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a + 8 * V_PITCH));
+            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a + 8 * ROW_B));
             const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
             const bf16x8_t vf = as_bf16x8(u32x4_t{l2[0], l2[1], h2[0], h2[1]});
             st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], st.o[db], 0, 0, 0);
@@ -351,6 +357,101 @@ __device__ __forceinline__ void mask_rows(f32x16_t x[2], int nvalid, int half)
         }
 }
 
+// ----------------------------------------------------------------------------- exact tiles
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Workgroup barrier without the LDS release fence of __syncthreads (which
+// would also wait for every load-to-LDS still in flight, including the tiles
+// requested for later steps).  Every wave has already waited for its own loads
+// of the tile the barrier publishes, and all reads of the tile being retired
+// fed MFMAs before the barrier; the empty asm statements and the scheduling
+// barriers keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void tile_barrier()
+{
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+constexpr int FILL_ROWS = AT_BN / AT_WAVES;   // tile rows each wave fills
+constexpr int FILL_N = FILL_ROWS / 4;          // 4-row instructions per operand and wave
+
+// Fill tile buffer b (K rows at b, V rows at b + T_BUF): wave w writes rows
+// FILL_ROWS w .. FILL_ROWS (w + 1) - 1, one 4-row instruction per operand and
+// step; lane l writes LDS chunk l & 15 of its row and so reads the global
+// chunk that the swizzle places there.
+__device__ __forceinline__ void tile_fill(char* b, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                          int wv, const int r[FILL_N], const int kx[FILL_N], int vx)
+{
+    char* kb = b + FILL_ROWS * wv * ROW_B;
+    char* vb = b + T_BUF + FILL_ROWS * wv * ROW_B;
+#pragma unroll
+    for (int i = 0; i < FILL_N; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)(kb + 4 * i * ROW_B), 16, r[i] * ROW_B + kx[i], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < FILL_N; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)(vb + 4 * i * ROW_B), 16, r[i] * ROW_B + vx, 0, 0, 0);
+}
+
+// The exact tiles of one query tile: the routed keys (row map rm, nk keys) in
+// 64-key tiles through two LDS buffers.  Each step requests the row indices of
+// tile t + 2, then the rows of tile t + 1 straight into the other buffer, then
+// computes tile t; the loads land during the math.  The two buffers are
+// distinct restrict-qualified pointers and the loop is unrolled by two, so
+// the compiler sees that the loads in flight never alias the buffer being
+// read and adds no wait of its own before the reads; the explicit wait before
+// each barrier covers this wave's loads and the barrier publishes every
+// wave's rows.  Loads past the last tile use clamped rows into a buffer no
+// one reads; all loads drain before returning.
+__device__ __forceinline__ void exact_tiles(char* __restrict__ b0, char* __restrict__ b1, Softmax& st,
+                                            const bf16x8_t qf[8], __amdgpu_buffer_rsrc_t rk,
+                                            __amdgpu_buffer_rsrc_t rv, const int* __restrict__ rm, int nk,
+                                            int wave, int lane, bool wact, float scale2)
+{
+    const int ntiles = (nk + AT_BN - 1) / AT_BN;
+    const int half = lane >> 5;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int lr = FILL_ROWS * wv + (lane >> 4), p = lane & 15;
+    int kx[FILL_N];
+#pragma unroll
+    for (int i = 0; i < FILL_N; ++i) kx[i] = k_pos(lr + 4 * i, p) * 16;
+    const int vx = v_pos(lr, p) * 16;   // rows lr + 4 i share it
+    int ra[FILL_N], rb[FILL_N];
+#define ROWS(SET, T)                                                                          \
+    _Pragma("unroll") for (int i = 0; i < FILL_N; ++i)                                        \
+        SET[i] = rm[min((T) * AT_BN + lr + 4 * i, nk - 1)];
+    ROWS(ra, 0)
+    ROWS(rb, 1)
+    tile_fill(b0, rk, rv, wv, ra, kx, vx);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | 0);
+    tile_barrier();
+#define EXACT_STEP(T, CUR, NXT, RT, RN)                                                       \
+    {                                                                                         \
+        ROWS(RT, (T) + 2)                /* rows of tile T + 2 (set of tile T, now free) */   \
+        tile_fill(NXT, rk, rv, wv, RN, kx, vx);   /* tile T + 1 */                            \
+        if (wact && (T) < ntiles) {                                                           \
+            f32x16_t acc[2] = {f32x16_t{0}, f32x16_t{0}};                                     \
+            tile_scores(acc, CUR, qf, lane);                                                  \
+            const int nvalid = nk - (T) * AT_BN;                                              \
+            if (nvalid < AT_BN) mask_rows(acc, nvalid, half);                                 \
+            bf16x8_t pf[4];                                                                   \
+            softmax_update(st, acc, scale2, pf);                                              \
+            tile_pv(st, CUR + T_BUF, pf, lane);                                               \
+        }                                                                                     \
+        __builtin_amdgcn_s_waitcnt(0x0F70 | 0);   /* tile T + 1 and rows of T + 2 landed */   \
+        tile_barrier();                                                                       \
+    }
+    for (int t = 0; t < ntiles; t += 2) {
+        EXACT_STEP(t, b0, b1, ra, rb)
+        EXACT_STEP(t + 1, b1, b0, rb, ra)
+    }
+#undef EXACT_STEP
+#undef ROWS
+}
+
 // ----------------------------------------------------------------------------- main kernel
 
 __global__ __launch_bounds__(AT_THREADS, 2) void k_attn_mfma(
@@ -363,12 +464,10 @@ __global__ __launch_bounds__(AT_THREADS, 2) void k_attn_mfma(
     int Ck, int tiles_per_head, int grid_per_xcd, float scale2, bf16* __restrict__ O)
 {
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    char* const kbuf0 = smem;
-    char* const vbuf0 = smem + 2 * K_BUF;
-    float* const s_bias = (float*)(smem + 2 * K_BUF + 2 * V_BUF);
-    int* const s_map = (int*)(smem + 2 * K_BUF + 2 * V_BUF + AT_BN * 4);  // [64]
-#define KBUF(b) (kbuf0 + (b) * K_BUF)
-#define VBUF(b) (vbuf0 + (b) * V_BUF)
+    float* const s_bias = (float*)(smem + AT_NBUF * 2 * T_BUF);
+    int* const s_map = (int*)(smem + AT_NBUF * 2 * T_BUF + AT_BN * 4);  // [64]
+#define KBUF(b) (smem + (b) * 2 * T_BUF)
+#define VBUF(b) (smem + (b) * 2 * T_BUF + T_BUF)
 
     // XCD-aware order: logical tile = XCD-major position of this workgroup.
     const int p = blockIdx.x;
@@ -450,8 +549,7 @@ __global__ __launch_bounds__(AT_THREADS, 2) void k_attn_mfma(
         }
     }
 
-    // 2. exact tiles (packed routed keys), double-buffered, one barrier per
-    //    tile; the row map of tile it + 2 is fetched while tile it is computed.
+    // 2. exact tiles (packed routed keys)
     const int nk = nkeys[hc];
     if (nk > 0) {
         const int* rm = rowmap + hc * Nk;
@@ -460,39 +558,7 @@ __global__ __launch_bounds__(AT_THREADS, 2) void k_attn_mfma(
             (void*)(Kp + (size_t)h * Nk * AT_D), (short)0, (int)head_bytes, 0x00020000);
         const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(Vp + (size_t)h * Nk * AT_D), (short)0, (int)head_bytes, 0x00020000);
-        const int kc = tid & 15, kr = tid >> 4;
-        const int ntiles = (nk + AT_BN - 1) / AT_BN;
-        int row[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) row[i] = rm[min(kr + 16 * i, nk - 1)];
-        Stage sbuf;
-        stage_load_rows(sbuf, rk, rv, row, kc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) row[i] = rm[min(AT_BN + kr + 16 * i, nk - 1)];
-        stage_store(sbuf, KBUF(0), VBUF(0), tid);
-        __syncthreads();
-        for (int it = 0; it < ntiles; ++it) {
-            const int buf = it & 1;
-            const bool has_next = it + 1 < ntiles;
-            if (has_next) {
-                stage_load_rows(sbuf, rk, rv, row, kc);
-                const int v2 = (it + 2) * AT_BN + kr;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) row[i] = rm[min(v2 + 16 * i, nk - 1)];
-            }
-            if (wact) {
-                f32x16_t acc[2] = {f32x16_t{0}, f32x16_t{0}};
-                tile_scores(acc, KBUF(buf), qf, lane);
-                const int nvalid = nk - it * AT_BN;
-                if (nvalid < AT_BN) mask_rows(acc, nvalid, half);
-                bf16x8_t pf[4];
-                softmax_update(st, acc, scale2, pf);
-                tile_pv(st, VBUF(buf), pf, lane);
-            }
-            if (!has_next) break;
-            stage_store(sbuf, KBUF(buf ^ 1), VBUF(buf ^ 1), tid);
-            __syncthreads();
-        }
+        exact_tiles(KBUF(0), KBUF(1), st, qf, rk, rv, rm, nk, wave, lane, wact, scale2);
     }
 
     // 3. normalise, stage the tile in LDS as [query][d], store rows in token order
