@@ -90,6 +90,9 @@ SVG_HIDDEN Layout make_layout(const svgear_shape& s)
     L.at_comp = take(H * Cq * Ck * 4);
     L.at_ncomp = take(H * Cq * 4);
     L.at_rowmap = take(H * Cq * Nk * 4);
+    // work queues: meta (count, start, counter per XCD class), per-head class
+    // counts and in-class prefixes, the queue itself (at most H (ceil(Nq / rows) + Cq) tiles)
+    L.at_queue = take((3 * kXcd + H * kXcd + H * Cq + H * ((Nq + kAttnRows - 1) / kAttnRows + Cq)) * 4);
     L.at_end = off;
 
     size_t sc = L.cl_end;

@@ -53,9 +53,10 @@ constexpr int ROW_B = AT_D * 2;          // 256
 constexpr int T_BUF = AT_BN * ROW_B;     // 16384
 constexpr int AT_NBUF = 2;
 constexpr int K_PITCH = AT_D * 2 + 16;   // output staging rows (272 B)
-constexpr int AT_LDS = AT_NBUF * 2 * T_BUF + AT_BN * 4 + AT_BN * 4;
+constexpr int AT_LDS = AT_NBUF * 2 * T_BUF + AT_BN * 4 + AT_BN * 4 + 16;  // + bias, map, job slot
 static_assert(AT_BM * K_PITCH <= AT_NBUF * 2 * T_BUF, "output staging fits the tile buffers");
 static_assert(ST_ROWS * ST_STEP == AT_BN, "staging covers a tile");
+static_assert(AT_BM == kAttnRows, "tile rows as sized in the workspace layout");
 constexpr int AT_XCD = 8;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -184,6 +185,85 @@ __global__ __launch_bounds__(1024) void k_tile_prefix(const int32_t* __restrict_
         }
     }
     if (threadIdx.x == 1023) ts[Cq] = s_part[1023];
+}
+
+// Work queues.  Query tiles are dealt to eight queues by query cluster
+// (c mod 8), one per XCD: workgroup w starts on queue w mod 8, the XCD it is
+// dispatched to, so the tiles of one cluster, which read the same keys, run
+// together on one XCD and share its L2; within a queue tiles go head by head,
+// so all XCDs work on the same few heads at a time.  A workgroup that finds
+// its queue empty moves on to the next queue.
+// Per head: tiles per class and the exclusive prefix of tiles within the class.
+__global__ __launch_bounds__(256) void k_queue_count(const int* __restrict__ tstart, int Cq,
+                                                     int* __restrict__ cnt, int* __restrict__ pre)
+{
+    __shared__ int s_part[256];
+    const int h = blockIdx.x, tid = threadIdx.x;
+    const int x = tid >> 5, l = tid & 31;           // class x, 32 threads per class
+    const int* ts = tstart + (size_t)h * (Cq + 1);
+    const int nx = Cq > x ? (Cq - x + kXcd - 1) / kXcd : 0;  // members c = x + 8 q, q < nx
+    const int per = (nx + 31) / 32;
+    const int q0 = l * per;
+    int local = 0;
+    for (int k = 0; k < per; ++k) {
+        const int q = q0 + k;
+        if (q < nx) {
+            const int c = x + kXcd * q;
+            local += ts[c + 1] - ts[c];
+        }
+    }
+    s_part[tid] = local;
+    __syncthreads();
+    for (int off = 1; off < 32; off <<= 1) {
+        const int v = l >= off ? s_part[tid - off] : 0;
+        __syncthreads();
+        s_part[tid] += v;
+        __syncthreads();
+    }
+    int run = s_part[tid] - local;
+    for (int k = 0; k < per; ++k) {
+        const int q = q0 + k;
+        if (q < nx) {
+            const int c = x + kXcd * q;
+            pre[(size_t)h * Cq + c] = run;
+            run += ts[c + 1] - ts[c];
+        }
+    }
+    if (l == 31) cnt[h * kXcd + x] = s_part[tid];
+}
+
+// Queue entries (logical tile h * tiles_per_head + tile-in-head), class-major,
+// then head, cluster and tile; meta[x] = length of queue x, meta[8 + x] = its
+// first entry.
+__global__ __launch_bounds__(256) void k_queue_fill(const int* __restrict__ tstart,
+                                                    const int* __restrict__ cnt,
+                                                    const int* __restrict__ pre, int H, int Cq,
+                                                    int tiles_per_head, int* __restrict__ meta,
+                                                    int* __restrict__ list)
+{
+    __shared__ int s_base[kXcd];
+    const int h = blockIdx.x, tid = threadIdx.x;
+    if (tid < kXcd) {
+        const int x = tid;
+        int start = 0, off = 0, tot = 0;
+        for (int y = 0; y < x; ++y)
+            for (int g = 0; g < H; ++g) start += cnt[g * kXcd + y];
+        for (int g = 0; g < H; ++g) {
+            if (g < h) off += cnt[g * kXcd + x];
+            tot += cnt[g * kXcd + x];
+        }
+        s_base[x] = start + off;
+        if (h == 0) {
+            meta[x] = tot;
+            meta[kXcd + x] = start;
+        }
+    }
+    __syncthreads();
+    const int* ts = tstart + (size_t)h * (Cq + 1);
+    for (int c = tid; c < Cq; c += 256) {
+        const int base = s_base[c % kXcd] + pre[(size_t)h * Cq + c];
+        for (int t = ts[c]; t < ts[c + 1]; ++t) list[base + (t - ts[c])] = h * tiles_per_head + t;
+    }
 }
 
 // ----------------------------------------------------------------------------- tile staging
@@ -454,28 +534,21 @@ __device__ __forceinline__ void exact_tiles(char* __restrict__ b0, char* __restr
 
 // ----------------------------------------------------------------------------- main kernel
 
-__global__ __launch_bounds__(AT_THREADS, 2) void k_attn_mfma(
-    const bf16* __restrict__ Qp, const int32_t* __restrict__ offsets_q,
-    const int32_t* __restrict__ perm_q, const bf16* __restrict__ Kp, const bf16* __restrict__ Vp,
-    const bf16* __restrict__ kbh, const bf16* __restrict__ kbl, const bf16* __restrict__ vbh,
-    const bf16* __restrict__ vbl, const float* __restrict__ logm2, const int* __restrict__ rowmap,
-    const int* __restrict__ nkeys, const int* __restrict__ comp,
-    const int* __restrict__ ncomp, const int* __restrict__ tstart, int H, int Nq, int Nk, int Cq,
-    int Ck, int tiles_per_head, int grid_per_xcd, float scale2, bf16* __restrict__ O)
-{
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    float* const s_bias = (float*)(smem + AT_NBUF * 2 * T_BUF);
-    int* const s_map = (int*)(smem + AT_NBUF * 2 * T_BUF + AT_BN * 4);  // [64]
 #define KBUF(b) (smem + (b) * 2 * T_BUF)
 #define VBUF(b) (smem + (b) * 2 * T_BUF + T_BUF)
 
-    // XCD-aware order: logical tile = XCD-major position of this workgroup.
-    const int p = blockIdx.x;
-    const int logical = (p % AT_XCD) * grid_per_xcd + p / AT_XCD;
-    if (logical >= tiles_per_head * H) return;
+// One query tile: logical index h * tiles_per_head + tile-in-head.
+__device__ __forceinline__ void attn_tile(
+    int logical, char* smem, float* s_bias, int* s_map, const bf16* __restrict__ Qp,
+    const int32_t* __restrict__ offsets_q, const int32_t* __restrict__ perm_q,
+    const bf16* __restrict__ Kp, const bf16* __restrict__ Vp, const bf16* __restrict__ kbh,
+    const bf16* __restrict__ kbl, const bf16* __restrict__ vbh, const bf16* __restrict__ vbl,
+    const float* __restrict__ logm2, const int* __restrict__ rowmap, const int* __restrict__ nkeys,
+    const int* __restrict__ comp, const int* __restrict__ ncomp, const int* __restrict__ tstart, int Nq,
+    int Nk, int Cq, int Ck, int tiles_per_head, float scale2, bf16* __restrict__ O)
+{
     const int h = logical / tiles_per_head, t = logical - h * tiles_per_head;
     const int* ts = tstart + (size_t)h * (Cq + 1);
-    if (t >= ts[Cq]) return;
     int lo = 0, hi = Cq - 1;  // query cluster: last c with ts[c] <= t
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -591,9 +664,41 @@ __global__ __launch_bounds__(AT_THREADS, 2) void k_attn_mfma(
                 *(const u32x4_t*)(ost + r * K_PITCH + ch * 16);
         }
     }
+}
+
+__global__ __launch_bounds__(AT_THREADS, 2) void k_attn_mfma(
+    const bf16* __restrict__ Qp, const int32_t* __restrict__ offsets_q,
+    const int32_t* __restrict__ perm_q, const bf16* __restrict__ Kp, const bf16* __restrict__ Vp,
+    const bf16* __restrict__ kbh, const bf16* __restrict__ kbl, const bf16* __restrict__ vbh,
+    const bf16* __restrict__ vbl, const float* __restrict__ logm2, const int* __restrict__ rowmap,
+    const int* __restrict__ nkeys, const int* __restrict__ comp,
+    const int* __restrict__ ncomp, const int* __restrict__ tstart, const int* __restrict__ qmeta,
+    int* __restrict__ qctr, const int* __restrict__ qlist, int H, int Nq, int Nk, int Cq, int Ck,
+    int tiles_per_head, float scale2, bf16* __restrict__ O)
+{
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    float* const s_bias = (float*)(smem + AT_NBUF * 2 * T_BUF);
+    int* const s_map = (int*)(smem + AT_NBUF * 2 * T_BUF + AT_BN * 4);  // [64]
+    int* const s_job = (int*)(smem + AT_NBUF * 2 * T_BUF + 2 * AT_BN * 4);
+
+    const int x0 = blockIdx.x % AT_XCD;
+    for (int k = 0; k < AT_XCD; ++k) {
+        const int x = (x0 + k) % AT_XCD;
+        const int qlen = qmeta[x], qstart = qmeta[AT_XCD + x];
+        for (;;) {
+            __syncthreads();  // the previous tile is done with LDS (s_job included)
+            if (threadIdx.x == 0) *s_job = atomicAdd(qctr + x, 1);
+            __syncthreads();
+            const int j = *s_job;
+            if (j >= qlen) break;
+            attn_tile(qlist[qstart + j], smem, s_bias, s_map, Qp, offsets_q, perm_q, Kp, Vp, kbh, kbl,
+                      vbh, vbl, logm2, rowmap, nkeys, comp, ncomp, tstart, Nq, Nk, Cq, Ck, tiles_per_head,
+                      scale2, O);
+        }
+    }
+}
 #undef KBUF
 #undef VBUF
-}
 
 // ----------------------------------------------------------------------------- dispatch
 
@@ -625,14 +730,25 @@ SVG_HIDDEN hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t st)
                        a.Ck, a.Nk, segs, nsegs, nkeys, comp, ncomp, rowmap);
     hipLaunchKernelGGL(k_tile_prefix, dim3(a.H), dim3(1024), 0, st, a.offsets_q, a.Cq, tstart);
     const int tiles_per_head = (a.Nq + AT_BM - 1) / AT_BM + a.Cq;
-    const long total = (long)tiles_per_head * a.H;
-    const int per_xcd = (int)((total + AT_XCD - 1) / AT_XCD);
+    int* qmeta = (int*)(s + L.at_queue);       // [8] lengths, [8] starts, [8] counters
+    int* qcnt = qmeta + 3 * AT_XCD;            // [H][8]
+    int* qpre = qcnt + (size_t)a.H * AT_XCD;   // [H][Cq]
+    int* qlist = qpre + (size_t)a.H * a.Cq;    // [total tiles]
+    hipLaunchKernelGGL(k_queue_count, dim3(a.H), dim3(256), 0, st, tstart, a.Cq, qcnt, qpre);
+    hipLaunchKernelGGL(k_queue_fill, dim3(a.H), dim3(256), 0, st, tstart, qcnt, qpre, a.H, a.Cq,
+                       tiles_per_head, qmeta, qlist);
+    zero_words(qmeta + 2 * AT_XCD, AT_XCD * 4, st);
+    // persistent: two workgroups per CU (the occupancy the register use allows)
+    int dev = 0, ncu = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    const int nwg = 2 * (ncu > 0 ? ncu : 256);
     const float scale2 = (float)(1.4426950408889634 / sqrt((double)AT_D));
-    hipLaunchKernelGGL(k_attn_mfma, dim3(per_xcd * AT_XCD), dim3(AT_THREADS), AT_LDS, st,
+    hipLaunchKernelGGL(k_attn_mfma, dim3(nwg), dim3(AT_THREADS), AT_LDS, st,
                        (const bf16*)a.Qp, a.offsets_q, a.perm_q, (const bf16*)a.Kp,
                        (const bf16*)a.Vp, kbh, kbl, vbh, vbl, logm2, rowmap, nkeys, comp, ncomp,
-                       tstart, a.H, a.Nq, a.Nk, a.Cq, a.Ck, tiles_per_head, per_xcd, scale2,
-                       (bf16*)a.O);
+                       tstart, qmeta, qmeta + 2 * AT_XCD, qlist, a.H, a.Nq, a.Nk, a.Cq, a.Ck,
+                       tiles_per_head, scale2, (bf16*)a.O);
     return hipGetLastError();
 }
 

@@ -76,6 +76,8 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return f32
 
 constexpr int kTile = 256;          // tokens per counting-sort / run-length tile
 constexpr int kMaxC = 4096;         // largest cluster count
+constexpr int kAttnRows = 128;      // query rows per attention tile (bf16, d = 128 kernel)
+constexpr int kXcd = 8;             // XCDs per device: attention work queues
 constexpr int kMaxN = 1 << 20;      // largest token count
 
 // Fixed-point scale 2^S of the exact centroid sums: |x| < 2^8 and N < 2^lgN give
@@ -109,7 +111,7 @@ struct Layout {
     size_t pr_end;
     // attention scratch (relative to scratch)
     size_t at_err, at_kvplanes, at_logm, at_tiles, at_segs, at_nsegs, at_nkeys, at_comp, at_ncomp,
-        at_rowmap;
+        at_rowmap, at_queue;
     size_t at_end;
     size_t total;
 };
