@@ -98,14 +98,15 @@ __global__ __launch_bounds__(256) void k_seg_list(const uint8_t* __restrict__ ma
                                                   int* __restrict__ rowmap)
 {
     __shared__ int s_a[256], s_b[256];
-    const int c = blockIdx.x, h = blockIdx.y;
+    __shared__ int s_start[kMaxC], s_pref[kMaxC + 1];  // routed segments: first row, key prefix
+    const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
     const uint8_t* mrow = mask + ((size_t)h * Cq + c) * Ck;
     const int32_t* ok = offsets_k + (size_t)h * (Ck + 1);
     int2* out = segs + ((size_t)h * Cq + c) * Ck;
     int* cout = comp + ((size_t)h * Cq + c) * Ck;
-    int base = 0, cbase = 0, keys = 0;
+    int base = 0, cbase = 0;
     for (int g0 = 0; g0 < Ck; g0 += 256) {
-        const int g = g0 + threadIdx.x;
+        const int g = g0 + tid;
         int sel = 0, cmp = 0, start = 0, len = 0;
         if (g < Ck) {
             start = ok[g];
@@ -113,46 +114,63 @@ __global__ __launch_bounds__(256) void k_seg_list(const uint8_t* __restrict__ ma
             sel = mrow[g] && len > 0;
             cmp = !mrow[g] && len > 0;
         }
-        s_a[threadIdx.x] = sel;
-        s_b[threadIdx.x] = cmp;
+        s_a[tid] = sel;
+        s_b[tid] = cmp;
         __syncthreads();
         for (int off = 1; off < 256; off <<= 1) {
-            const int va = threadIdx.x >= off ? s_a[threadIdx.x - off] : 0;
-            const int vb = threadIdx.x >= off ? s_b[threadIdx.x - off] : 0;
+            const int va = tid >= off ? s_a[tid - off] : 0;
+            const int vb = tid >= off ? s_b[tid - off] : 0;
             __syncthreads();
-            s_a[threadIdx.x] += va;
-            s_b[threadIdx.x] += vb;
+            s_a[tid] += va;
+            s_b[tid] += vb;
             __syncthreads();
         }
-        if (sel) out[base + s_a[threadIdx.x] - 1] = make_int2(start, len);
-        if (cmp) cout[cbase + s_b[threadIdx.x] - 1] = g;
+        if (sel) {
+            const int si = base + s_a[tid] - 1;
+            out[si] = make_int2(start, len);
+            s_start[si] = start;
+            s_pref[si] = len;
+        }
+        if (cmp) cout[cbase + s_b[tid] - 1] = g;
         base += s_a[255];
         cbase += s_b[255];
         __syncthreads();
-        // routed keys in this chunk
-        s_a[threadIdx.x] = sel ? len : 0;
+    }
+    // exclusive prefix of the segment lengths (contiguous runs per thread)
+    const int per = (base + 255) / 256, s0 = tid * per;
+    int run = 0;
+    for (int k = 0; k < per && s0 + k < base; ++k) run += s_pref[s0 + k];
+    s_a[tid] = run;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+        const int v = tid >= off ? s_a[tid - off] : 0;
         __syncthreads();
-        for (int off = 128; off >= 1; off >>= 1) {
-            if (threadIdx.x < off) s_a[threadIdx.x] += s_a[threadIdx.x + off];
-            __syncthreads();
-        }
-        keys += s_a[0];
+        s_a[tid] += v;
         __syncthreads();
     }
-    if (threadIdx.x == 0) {
+    int acc = s_a[tid] - run;
+    for (int k = 0; k < per && s0 + k < base; ++k) {
+        const int len = s_pref[s0 + k];
+        s_pref[s0 + k] = acc;
+        acc += len;
+    }
+    const int keys = s_a[255];
+    if (tid == 0) s_pref[base] = keys;
+    __syncthreads();
+    if (tid == 0) {
         nsegs[(size_t)h * Cq + c] = base;
         ncomp[(size_t)h * Cq + c] = cbase;
         nkeys[(size_t)h * Cq + c] = keys;
     }
-    // Row map: list position -> reordered key row, segment after segment
-    // (the segment list above was written by this workgroup).
-    __syncthreads();
+    // Row map: list position k -> reordered key row (segment found by binary search)
     int* rm = rowmap + ((size_t)h * Cq + c) * Nk;
-    int pos = 0;
-    for (int si = 0; si < base; ++si) {
-        const int2 sg = out[si];
-        for (int k = threadIdx.x; k < sg.y; k += 256) rm[pos + k] = sg.x + k;
-        pos += sg.y;
+    for (int k = tid; k < keys; k += 256) {
+        int lo = 0, hi = base - 1;  // last segment with s_pref <= k
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_pref[mid] <= k) lo = mid; else hi = mid - 1;
+        }
+        rm[k] = s_start[lo] + (k - s_pref[lo]);
     }
 }
 

@@ -47,40 +47,64 @@ __global__ __launch_bounds__(256) void k_key_scalars(const T* __restrict__ Vp,
     for (int o = 8; o >= 1; o >>= 1) p += __shfl_xor(p, o, 16);
     if (threadIdx.x == 0) pg[(size_t)h * Ck + g] = p;
     const int j0 = offsets_k[(size_t)h * (Ck + 1) + g], j1 = offsets_k[(size_t)h * (Ck + 1) + g + 1];
-    for (int j = j0 + row; j < j1; j += 16) {
-        const T* v = Vp + ((size_t)h * Nk + j) * D + sub * EPT;
-        float qd = 0.f, r = 0.f;
+    // four rows per pass, their loads issued together
+    constexpr int RU = 4;
+    for (int jb = j0; jb < j1; jb += 16 * RU) {
+        T vv[RU][EPT];
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-            float dl = vbr[e] - to_f32<T>(v[e]);
-            qd = fmaf(vbr[e], dl, qd);
-            r = fmaf(dl, dl, r);
+        for (int u = 0; u < RU; ++u) {
+            const int j = min(jb + row + 16 * u, j1 - 1);
+            const T* v = Vp + ((size_t)h * Nk + j) * D + sub * EPT;
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) vv[u][e] = v[e];
         }
 #pragma unroll
-        for (int o = 8; o >= 1; o >>= 1) {
-            qd += __shfl_xor(qd, o, 16);
-            r += __shfl_xor(r, o, 16);
+        for (int u = 0; u < RU; ++u) {
+            float qd = 0.f, r = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) {
+                float dl = vbr[e] - to_f32<T>(vv[u][e]);
+                qd = fmaf(vbr[e], dl, qd);
+                r = fmaf(dl, dl, r);
+            }
+#pragma unroll
+            for (int o = 8; o >= 1; o >>= 1) {
+                qd += __shfl_xor(qd, o, 16);
+                r += __shfl_xor(r, o, 16);
+            }
+            const int j = jb + row + 16 * u;
+            if (sub == 0 && j < j1) keys[(size_t)h * Nk + j] = make_float2(qd, r);
         }
-        if (sub == 0) keys[(size_t)h * Nk + j] = make_float2(qd, r);
     }
 }
 
-// sbar[c, g] = tau qbar_c . kbar_g, accumulated in fp64 and rounded once to fp32.
+// sbar[c, g] = tau qbar_c . kbar_g, accumulated in fp64 in dimension order and
+// rounded once to fp32.  A workgroup takes 4 query clusters x 64 key clusters:
+// the 64 kbar rows are staged in LDS (row pitch D + 1 floats, so the 64 lanes
+// of a wave, one row each, read one dimension from distinct banks) and the 4
+// qbar rows as fp64 (one row per wave, broadcast).
 template <int D>
 __global__ __launch_bounds__(256) void k_sbar(const float* __restrict__ qbar,
                                               const float* __restrict__ kbar, int Cq, int Ck,
                                               double tau, float* __restrict__ sbar)
 {
-    __shared__ double s_q[D];
-    const int c = blockIdx.x, h = blockIdx.z;
-    for (int t = threadIdx.x; t < D; t += 256) s_q[t] = qbar[((size_t)h * Cq + c) * D + t];
+    __shared__ float s_k[64][D + 1];
+    __shared__ double s_q[4][D];
+    const int c0 = blockIdx.x * 4, g0 = blockIdx.y * 64, h = blockIdx.z, tid = threadIdx.x;
+    for (int i = tid; i < 64 * D; i += 256) {
+        const int r = i / D, t = i - r * D, g = g0 + r;
+        s_k[r][t] = g < Ck ? kbar[((size_t)h * Ck + g) * D + t] : 0.f;
+    }
+    for (int i = tid; i < 4 * D; i += 256) {
+        const int r = i / D, t = i - r * D, c = c0 + r;
+        s_q[r][t] = c < Cq ? (double)qbar[((size_t)h * Cq + c) * D + t] : 0.0;
+    }
     __syncthreads();
-    const int g = blockIdx.y * 256 + threadIdx.x;
-    if (g >= Ck) return;
-    const float* kb = kbar + ((size_t)h * Ck + g) * D;
+    const int r = tid >> 6, gl = tid & 63, c = c0 + r, g = g0 + gl;
+    if (c >= Cq || g >= Ck) return;
     double s = 0.0;
 #pragma unroll 8
-    for (int t = 0; t < D; ++t) s = fma(s_q[t], (double)kb[t], s);
+    for (int t = 0; t < D; ++t) s = fma(s_q[r][t], (double)s_k[gl][t], s);
     sbar[((size_t)h * Cq + c) * Ck + g] = (float)(tau * s);
 }
 
@@ -205,7 +229,7 @@ static hipError_t run_probe(const ProbeArgs& a, hipStream_t st)
     float* pg = (float*)(a.scratch + L.pr_pg);
     const float tau = 1.0f / sqrtf((float)D);
     if (a.flags & SVGEAR_PROBE_SCORE) {
-        hipLaunchKernelGGL((k_sbar<D>), dim3(a.Cq, (a.Ck + 255) / 256, a.H), dim3(256), 0, st, a.qbar,
+        hipLaunchKernelGGL((k_sbar<D>), dim3((a.Cq + 3) / 4, (a.Ck + 63) / 64, a.H), dim3(256), 0, st, a.qbar,
                            a.kbar, a.Cq, a.Ck, 1.0 / sqrt((double)D), sbar);
         hipLaunchKernelGGL(k_score_ratio, dim3(a.Cq, a.H), dim3(256), 0, st, sbar, a.counts_q,
                            a.counts_k, a.Cq, a.Ck, a.log_ratio);
@@ -213,7 +237,7 @@ static hipError_t run_probe(const ProbeArgs& a, hipStream_t st)
     }
     hipLaunchKernelGGL((k_key_scalars<T, D>), dim3(a.Ck, a.H), dim3(256), 0, st, (const T*)a.Vp,
                        a.vbar, a.offsets_k, a.Nk, a.Ck, keys, pg, (a.flags & SVGEAR_PROBE_LOGIT) ? 1 : 0);
-    hipLaunchKernelGGL((k_sbar<D>), dim3(a.Cq, (a.Ck + 255) / 256, a.H), dim3(256), 0, st, a.qbar,
+    hipLaunchKernelGGL((k_sbar<D>), dim3((a.Cq + 3) / 4, (a.Ck + 63) / 64, a.H), dim3(256), 0, st, a.qbar,
                        a.kbar, a.Cq, a.Ck, 1.0 / sqrt((double)D), sbar);
     if (probe_mfma_supported(a)) return launch_probe_mfma(a, sbar, keys, pg, st);
     hipLaunchKernelGGL((k_probe_generic<T, D>), dim3(a.Ck, a.H), dim3(256), 0, st, a.qbar,

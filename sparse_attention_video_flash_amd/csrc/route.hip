@@ -37,6 +37,28 @@ __device__ long long block_sum_i64(long long v, long long* s_red)
     return t;
 }
 
+// Block b = c Ck + g of this thread in a sweep b = b0 + threadIdx.x, b0 += kRouteThreads:
+// (c, g) advanced without a division per step.
+struct BlockWalk {
+    int c, g, dc, dg;
+    __device__ BlockWalk(int Ck)
+    {
+        c = (int)threadIdx.x / Ck;
+        g = (int)threadIdx.x - c * Ck;
+        dc = kRouteThreads / Ck;
+        dg = kRouteThreads - dc * Ck;
+    }
+    __device__ void next(int Ck)
+    {
+        c += dc;
+        g += dg;
+        if (g >= Ck) {
+            g -= Ck;
+            ++c;
+        }
+    }
+};
+
 __global__ __launch_bounds__(kRouteThreads) void k_route(const float* __restrict__ log_ratio,
                                                          const int32_t* __restrict__ counts_q,
                                                          const int32_t* __restrict__ counts_k,
@@ -47,6 +69,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(const float* __restrict
     __shared__ long long s_hist[256];
     __shared__ long long s_red[kRouteThreads / 64];
     __shared__ long long s_scan[kRouteThreads];
+    __shared__ int s_cq[kMaxC], s_ck[kMaxC];
     __shared__ int s_stop;
     __shared__ uint32_t s_prefix;
     __shared__ long long s_base;
@@ -55,8 +78,9 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(const float* __restrict
     const int h = blockIdx.x;
     const int nb = Cq * Ck;
     const float* lr = log_ratio + (size_t)h * nb;
-    const int32_t* cq = counts_q + (size_t)h * Cq;
-    const int32_t* ck = counts_k + (size_t)h * Ck;
+    for (int i = threadIdx.x; i < Cq; i += kRouteThreads) s_cq[i] = counts_q[(size_t)h * Cq + i];
+    for (int i = threadIdx.x; i < Ck; i += kRouteThreads) s_ck[i] = counts_k[(size_t)h * Ck + i];
+    __syncthreads();
 
     // Radix select of the key of the first block that does not fit.
     uint32_t prefix = 0;     // determined high bits of the crossing key
@@ -66,14 +90,17 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(const float* __restrict
         const int shift = 24 - 8 * pass;
         for (int b = threadIdx.x; b < 256; b += kRouteThreads) s_hist[b] = 0;
         __syncthreads();
-        for (int b = threadIdx.x; b < nb; b += kRouteThreads) {
-            const uint32_t key = order_key(lr[b]);
-            const bool match = pass == 0 || (key >> (shift + 8)) == prefix;
-            if (match) {
-                const long long w = (long long)cq[b / Ck] * (long long)ck[b % Ck];
-                if (w) atomicAdd((unsigned long long*)&s_hist[(key >> shift) & 255u],
-                                 (unsigned long long)w);
+        BlockWalk bw(Ck);
+        for (int b0 = 0; b0 < nb; b0 += kRouteThreads, bw.next(Ck)) {
+            const int b = b0 + threadIdx.x;
+            uint32_t key = 0;
+            long long w = 0;
+            if (b < nb) {
+                key = order_key(lr[b]);
+                const bool match = pass == 0 || (key >> (shift + 8)) == prefix;
+                if (match) w = (long long)s_cq[bw.c] * (long long)s_ck[bw.g];
             }
+            if (w) atomicAdd((unsigned long long*)&s_hist[(key >> shift) & 255u], (unsigned long long)w);
         }
         __syncthreads();
         if (threadIdx.x == 0) {
@@ -100,16 +127,19 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(const float* __restrict
     }
 
     // Tie group (key == prefix) in block-index order: the first block whose
-    // inclusive prefix cost exceeds the budget stops the walk.
+    // inclusive prefix cost exceeds the budget stops the walk.  Sweeps with no
+    // member of the group skip the scan.
     int stop = nb;
     if (crosses) {
         if (threadIdx.x == 0) s_stop = nb;
         __syncthreads();
         long long run = base;
-        for (int b0 = 0; b0 < nb; b0 += kRouteThreads) {
+        BlockWalk bw(Ck);
+        for (int b0 = 0; b0 < nb; b0 += kRouteThreads, bw.next(Ck)) {
             const int b = b0 + threadIdx.x;
             long long w = 0;
-            if (b < nb && order_key(lr[b]) == prefix) w = (long long)cq[b / Ck] * (long long)ck[b % Ck];
+            if (b < nb && order_key(lr[b]) == prefix) w = (long long)s_cq[bw.c] * (long long)s_ck[bw.g];
+            if (!__syncthreads_or(w > 0)) continue;
             s_scan[threadIdx.x] = w;
             __syncthreads();
             for (int off = 1; off < kRouteThreads; off <<= 1) {
@@ -128,14 +158,17 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(const float* __restrict
 
     long long used = 0;
     uint8_t* mk = mask + (size_t)h * nb;
-    for (int b = threadIdx.x; b < nb; b += kRouteThreads) {
+    BlockWalk bw(Ck);
+    for (int b0 = 0; b0 < nb; b0 += kRouteThreads, bw.next(Ck)) {
+        const int b = b0 + threadIdx.x;
+        if (b >= nb) continue;
         bool sel = true;
         if (crosses) {
             const uint32_t key = order_key(lr[b]);
             sel = key > prefix || (key == prefix && b < stop);
         }
         mk[b] = sel ? 1 : 0;
-        if (sel) used += (long long)cq[b / Ck] * (long long)ck[b % Ck];
+        if (sel) used += (long long)s_cq[bw.c] * (long long)s_ck[bw.g];
     }
     used = block_sum_i64(used, s_red);
     if (threadIdx.x == 0) sel_cost[h] = used;
