@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "internal.h"
 
 #define SVG_API extern "C" __attribute__((visibility("default")))
@@ -98,8 +100,40 @@ SVG_HIDDEN Layout make_layout(const svgear_shape& s)
     size_t sc = L.cl_end;
     if (L.pr_end > sc) sc = L.pr_end;
     if (L.at_end > sc) sc = L.at_end;
-    L.total = L.scratch + sc;
+    L.scratch2 = L.scratch + align256(sc);
+    L.total = L.scratch2 + L.cl_end;
     return L;
+}
+
+// One side stream (default priority, non-blocking) and a fork/join event pair
+// per device, created on first use and kept for the life of the process.  The
+// mutex serialises the record/wait sequence of concurrent host callers.
+struct SideStream {
+    hipStream_t stream;
+    hipEvent_t fork, join;
+    std::mutex mu;
+};
+
+static SideStream* side_stream()
+{
+    constexpr int kMaxDev = 64;
+    static SideStream g_side[kMaxDev];
+    static bool g_ready[kMaxDev];
+    static std::mutex g_init;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nullptr;
+    std::lock_guard<std::mutex> lock(g_init);
+    if (!g_ready[dev]) {
+        SideStream& s = g_side[dev];
+        if (hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking) != hipSuccess) return nullptr;
+        if (hipEventCreateWithFlags(&s.fork, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&s.join, hipEventDisableTiming) != hipSuccess) {
+            hipStreamDestroy(s.stream);
+            return nullptr;
+        }
+        g_ready[dev] = true;
+    }
+    return &g_side[dev];
 }
 
 SVG_HIDDEN int read_device_error(const int* err, hipStream_t st)
@@ -194,7 +228,7 @@ static int cluster_impl(const svgear_shape* shape, int side, const void* X, cons
                         const int32_t* init_idx, int flags, int32_t* labels, float* cent,
                         float* vbar, int32_t* counts, int32_t* offsets, int32_t* perm,
                         int32_t* inv_perm, void* Xp, void* Vp, void* ws, const Layout& L,
-                        hipStream_t st)
+                        hipStream_t st, size_t scratch_off = 0)
 {
     ClusterArgs a;
     a.H = shape->H;
@@ -218,7 +252,7 @@ static int cluster_impl(const svgear_shape* shape, int side, const void* X, cons
     a.inv_perm = inv_perm;
     a.Xp = Xp;
     a.Vp = Vp;
-    a.scratch = (char*)ws + L.scratch;
+    a.scratch = (char*)ws + (scratch_off ? scratch_off : L.scratch);
     a.L = &L;
     zero_words(a.scratch + L.cl_err, 256, st);
     hipError_t e = launch_cluster(a, st);
@@ -450,12 +484,32 @@ SVG_API int svgear_forward(const svgear_shape* shape, double rho, const void* Q,
     SVG_PICK(sel_cost, int64_t*)
 #undef SVG_PICK
     hipStream_t st = (hipStream_t)stream;
-    rc = cluster_impl(shape, 0, Q, nullptr, init_q, 0, labels_q, qbar, nullptr, counts_q,
-                      offsets_q, perm_q, inv_perm_q, Qp, nullptr, ws, L, st);
-    if (rc) return rc;
-    rc = cluster_impl(shape, 1, K, V, init_k, 0, labels_k, kbar, vbar, counts_k, offsets_k, perm_k,
-                      inv_perm_k, Kp, Vp, ws, L, st);
-    if (rc) return rc;
+    // The two clusterings are independent: Q's runs on a side stream (its own
+    // scratch) while K's runs on the caller's stream, then the caller's stream
+    // waits for the side stream.
+    SideStream* ss = side_stream();
+    if (ss) {
+        std::lock_guard<std::mutex> lock(ss->mu);
+        if (hipEventRecord(ss->fork, st) != hipSuccess ||
+            hipStreamWaitEvent(ss->stream, ss->fork, 0) != hipSuccess)
+            return SVGEAR_E_HIP;
+        const int rq = cluster_impl(shape, 0, Q, nullptr, init_q, 0, labels_q, qbar, nullptr,
+                                    counts_q, offsets_q, perm_q, inv_perm_q, Qp, nullptr, ws, L,
+                                    ss->stream, L.scratch2);
+        const bool joined = hipEventRecord(ss->join, ss->stream) == hipSuccess;
+        const int rk = cluster_impl(shape, 1, K, V, init_k, 0, labels_k, kbar, vbar, counts_k,
+                                    offsets_k, perm_k, inv_perm_k, Kp, Vp, ws, L, st);
+        if (!joined || hipStreamWaitEvent(st, ss->join, 0) != hipSuccess) return SVGEAR_E_HIP;
+        if (rq) return rq;
+        if (rk) return rk;
+    } else {
+        rc = cluster_impl(shape, 0, Q, nullptr, init_q, 0, labels_q, qbar, nullptr, counts_q,
+                          offsets_q, perm_q, inv_perm_q, Qp, nullptr, ws, L, st);
+        if (rc) return rc;
+        rc = cluster_impl(shape, 1, K, V, init_k, 0, labels_k, kbar, vbar, counts_k, offsets_k,
+                          perm_k, inv_perm_k, Kp, Vp, ws, L, st);
+        if (rc) return rc;
+    }
     rc = probe_impl(shape, qbar, counts_q, Kp, Vp, kbar, vbar, counts_k, offsets_k, 0, log_ratio,
                     nullptr, ws, L, st);
     if (rc) return rc;

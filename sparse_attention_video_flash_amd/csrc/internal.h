@@ -94,7 +94,9 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Device-detected invalid data (reported under SVGEAR_DEBUG_SYNC).
 enum : int { ERR_INIT_INDEX = 1, ERR_LABEL = 2, ERR_RANGE = 4 };
 
-// Workspace map.  [ intermediates of svgear_forward | stage scratch (union) ].
+// Workspace map.  [ intermediates of svgear_forward | stage scratch (union) |
+// second cluster scratch ].  svgear_forward clusters Q in the second cluster
+// scratch on a side stream while K is clustered in the first.
 struct Layout {
     // forward intermediates
     size_t labels_q, qbar, counts_q, offsets_q, perm_q, inv_perm_q, Qp;
@@ -113,6 +115,7 @@ struct Layout {
     size_t at_err, at_kvplanes, at_logm, at_tiles, at_segs, at_nsegs, at_nkeys, at_comp, at_ncomp,
         at_rowmap, at_queue;
     size_t at_end;
+    size_t scratch2;  // second cluster scratch (absolute offset)
     size_t total;
 };
 

@@ -374,3 +374,43 @@ def test_probe_exact_special_cases(case):
     sv.probe(shape, _dev(qbar, torch.float32), _dev(cq, torch.int32), o["Xp"], o["Vp"], o["cent"], o["vbar"],
              o["counts"], o["offsets"], lr2, ws, flags=sv.DEBUG_SYNC)
     assert (lr2.cpu().numpy() == -np.inf).all()
+
+
+@pytest.mark.parametrize("case", ["ragged", "small"])
+def test_forward_equals_stage_by_stage_path(case):
+    """svgear_forward clusters Q on a side stream while K is clustered; its
+    intermediates and output must equal those of the per-stage entry points run
+    one after another on one stream, bit for bit, call after call."""
+    torch = torch_gpu()
+    w = CASES[case]
+    log("forward vs stages %s" % case)
+    data = upload(w)
+    H = len(data["heads"])
+    shape = shape_of(w, H)
+    ws = sv.alloc_workspace(shape)
+    rho = w.rhos[0]
+    ref_im = sv.alloc_intermediates(shape)
+    O_ref = torch.empty_like(data["Q"])
+    im = ref_im
+    sv.cluster(shape, 0, data["Q"], data["init_q"], dict(labels=im["labels_q"], cent=im["qbar"], counts=im["counts_q"],
+                                                         offsets=im["offsets_q"], perm=im["perm_q"],
+                                                         inv_perm=im["inv_perm_q"], Xp=im["Qp"]), ws)
+    sv.cluster(shape, 1, data["K"], data["init_k"], dict(labels=im["labels_k"], cent=im["kbar"], vbar=im["vbar"],
+                                                         counts=im["counts_k"], offsets=im["offsets_k"],
+                                                         perm=im["perm_k"], inv_perm=im["inv_perm_k"], Xp=im["Kp"],
+                                                         Vp=im["Vp"]), ws, V=data["V"])
+    sv.probe(shape, im["qbar"], im["counts_q"], im["Kp"], im["Vp"], im["kbar"], im["vbar"], im["counts_k"],
+             im["offsets_k"], im["log_ratio"], ws)
+    sv.route(shape, rho, im["log_ratio"], im["counts_q"], im["counts_k"], im["mask"], im["sel_cost"], ws)
+    sv.attention(shape, im["Qp"], im["offsets_q"], im["perm_q"], im["Kp"], im["Vp"], im["kbar"], im["vbar"],
+                 im["counts_k"], im["offsets_k"], im["mask"], O_ref, ws)
+    torch.cuda.synchronize()
+    ref = {k: v.cpu() for k, v in ref_im.items()}
+    for rep in range(3):
+        im2 = sv.alloc_intermediates(shape)
+        O = torch.empty_like(data["Q"])
+        sv.forward(shape, rho, data["Q"], data["K"], data["V"], data["init_q"], data["init_k"], O, ws, im2)
+        torch.cuda.synchronize()
+        for k, v in im2.items():
+            assert torch.equal(v.cpu(), ref[k]), "%s differs on call %d" % (k, rep)
+        assert torch.equal(O.cpu(), O_ref.cpu()), "output differs on call %d" % rep
