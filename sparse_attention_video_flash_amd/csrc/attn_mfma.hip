@@ -98,7 +98,9 @@ __global__ __launch_bounds__(256) void k_seg_list(const uint8_t* __restrict__ ma
                                                   int* __restrict__ rowmap)
 {
     __shared__ int s_a[256], s_b[256];
-    __shared__ int s_start[kMaxC], s_pref[kMaxC + 1];  // routed segments: first row, key prefix
+    extern __shared__ int s_seg[];       // [Ck] first rows, [Ck + 1] key prefixes of routed segments
+    int* const s_start = s_seg;
+    int* const s_pref = s_seg + Ck;
     const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
     const uint8_t* mrow = mask + ((size_t)h * Cq + c) * Ck;
     const int32_t* ok = offsets_k + (size_t)h * (Ck + 1);
@@ -162,15 +164,11 @@ __global__ __launch_bounds__(256) void k_seg_list(const uint8_t* __restrict__ ma
         ncomp[(size_t)h * Cq + c] = cbase;
         nkeys[(size_t)h * Cq + c] = keys;
     }
-    // Row map: list position k -> reordered key row (segment found by binary search)
+    // Row map: list position -> reordered key row, segment after segment
     int* rm = rowmap + ((size_t)h * Cq + c) * Nk;
-    for (int k = tid; k < keys; k += 256) {
-        int lo = 0, hi = base - 1;  // last segment with s_pref <= k
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (s_pref[mid] <= k) lo = mid; else hi = mid - 1;
-        }
-        rm[k] = s_start[lo] + (k - s_pref[lo]);
+    for (int si = 0; si < base; ++si) {
+        const int r0 = s_start[si], p0 = s_pref[si], len = s_pref[si + 1] - p0;
+        for (int k = tid; k < len; k += 256) rm[p0 + k] = r0 + k;
     }
 }
 
@@ -744,7 +742,7 @@ SVG_HIDDEN hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t st)
     int* rowmap = (int*)(s + L.at_rowmap);
     hipLaunchKernelGGL(k_comp_planes, dim3(a.Ck, a.H), dim3(AT_D), 0, st, a.kbar, a.vbar, a.counts_k,
                        a.Ck, kbh, kbl, vbh, vbl, logm2);
-    hipLaunchKernelGGL(k_seg_list, dim3(a.Cq, a.H), dim3(256), 0, st, a.mask, a.offsets_k, a.Cq,
+    hipLaunchKernelGGL(k_seg_list, dim3(a.Cq, a.H), dim3(256), (2 * a.Ck + 1) * 4, st, a.mask, a.offsets_k, a.Cq,
                        a.Ck, a.Nk, segs, nsegs, nkeys, comp, ncomp, rowmap);
     hipLaunchKernelGGL(k_tile_prefix, dim3(a.H), dim3(1024), 0, st, a.offsets_q, a.Cq, tstart);
     const int tiles_per_head = (a.Nq + AT_BM - 1) / AT_BM + a.Cq;

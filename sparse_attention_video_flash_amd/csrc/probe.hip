@@ -91,9 +91,21 @@ __global__ __launch_bounds__(256) void k_sbar(const float* __restrict__ qbar,
     __shared__ float s_k[64][D + 1];
     __shared__ double s_q[4][D];
     const int c0 = blockIdx.x * 4, g0 = blockIdx.y * 64, h = blockIdx.z, tid = threadIdx.x;
-    for (int i = tid; i < 64 * D; i += 256) {
-        const int r = i / D, t = i - r * D, g = g0 + r;
-        s_k[r][t] = g < Ck ? kbar[((size_t)h * Ck + g) * D + t] : 0.f;
+    // 64 rows x D floats as float4, all loads of a thread issued together
+    constexpr int V4 = 64 * D / 4 / 256;
+    float4 kv[V4];
+#pragma unroll
+    for (int u = 0; u < V4; ++u) {
+        const int i = tid + 256 * u, r = i / (D / 4), t4 = i - r * (D / 4), g = g0 + r;
+        kv[u] = g < Ck ? *(const float4*)(kbar + ((size_t)h * Ck + g) * D + 4 * t4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < V4; ++u) {
+        const int i = tid + 256 * u, r = i / (D / 4), t4 = i - r * (D / 4);
+        s_k[r][4 * t4] = kv[u].x;
+        s_k[r][4 * t4 + 1] = kv[u].y;
+        s_k[r][4 * t4 + 2] = kv[u].z;
+        s_k[r][4 * t4 + 3] = kv[u].w;
     }
     for (int i = tid; i < 4 * D; i += 256) {
         const int r = i / D, t = i - r * D, c = c0 + r;
