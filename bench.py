@@ -99,6 +99,39 @@ def work_counts(w, im):
                 density=exact_pairs / float(w.N * w.N * H))
 
 
+def stage_rooflines(w, wk, stage_ms, perm_ms):
+    """Achieved rate of each stage against its bound, from the event-timed
+    stage durations and algorithmic work: k-means against the bf16 MFMA peak
+    (10 iterations of 2 d flop per (token, centroid) distance); probe, route and
+    permutation against HBM (one read of what they must read, one write of what
+    they must write)."""
+    eb = 2 if w.dtype == "bf16" else 4
+    H, N, d, Cq, Ck = w.H, w.N, w.d, w.Cq, w.Ck
+    row = N * d * eb * H                       # one [H, N, d] tensor
+    out = {}
+
+    def mf(name, flops, ms):
+        a = flops / (ms * 1e-3) / 1e12
+        out[name] = {"bound": "mfma", "achieved": round(a, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(a / PEAK_BF16_TFLOPS, 4), "work": flops}
+
+    def bw(name, nbytes, ms):
+        a = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(a / PEAK_HBM_GBS, 4), "bytes": nbytes}
+
+    mf("cluster_q (k-means Q)", w.iters * 2.0 * d * N * Cq * H, stage_ms["cluster_q"])
+    mf("cluster_k (k-means K)", w.iters * 2.0 * d * N * Ck * H, stage_ms["cluster_k"])
+    # probe: K_p and V_p read once, ln r written
+    bw("probe", 2 * row + Cq * Ck * 4 * H, stage_ms["probe"])
+    # route: ln r read, mask written
+    bw("route", Cq * Ck * 5 * H, stage_ms["route"])
+    # permutation: X read, X_p written, labels read, perm and inv_perm written (+ V, V_p on the K side)
+    bw("permute_q", 2 * row + 12 * N * H, perm_ms["q"])
+    bw("permute_k", 4 * row + 12 * N * H, perm_ms["k"])
+    return out
+
+
 def cpu_baseline(w, rho, rows_stride=16):
     """The fp64 oracle on head 0: full k-means (Q and K), probe and route, and the
     hybrid output on every rows_stride-th query; scaled to a whole call."""
@@ -279,6 +312,28 @@ def main():
                 for i, st in enumerate(STAGES)}
     log("staged: %.3f ms/call; stages %s" % (staged_ms, {k: round(v, 3) for k, v in stage_ms.items()}))
 
+    # Third timed region: the permutation alone (counting sort, gathers into
+    # cluster order, centroid and value means) through svgear_cluster with the
+    # labels the forward produced, Q side and K side.
+    perm_ms = {}
+    for side in (0, 1):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        lab = im["labels_q" if side == 0 else "labels_k"].clone()
+        out = (dict(labels=lab, cent=im["qbar"], counts=im["counts_q"], offsets=im["offsets_q"], perm=im["perm_q"],
+                    inv_perm=im["inv_perm_q"], Xp=im["Qp"]) if side == 0 else
+               dict(labels=lab, cent=im["kbar"], vbar=im["vbar"], counts=im["counts_k"], offsets=im["offsets_k"],
+                    perm=im["perm_k"], inv_perm=im["inv_perm_k"], Xp=im["Kp"], Vp=im["Vp"]))
+        torch.cuda.synchronize()
+        e[0].record()
+        for s_ in range(args.steps):
+            sv.cluster(shape, side, Q if side == 0 else K, None, out, ws, V=None if side == 0 else V,
+                       flags=sv.LABELS_GIVEN)
+            e[s_ + 1].record()
+        torch.cuda.synchronize()
+        perm_ms["q" if side == 0 else "k"] = float(np.mean([e[i].elapsed_time(e[i + 1])
+                                                           for i in range(args.steps)]))
+    log("permutation: %s ms" % {k: round(v, 3) for k, v in perm_ms.items()})
+
     wk = work_counts(w, im)
     t_att = stage_ms["attention"] * 1e-3
     att_flops = wk["exact"] + wk["comp"]
@@ -308,6 +363,7 @@ def main():
         "realised_density": round(wk["density"], 5),
         "executed_tflops": round(executed / (ms_per_step * 1e-3) / 1e12, 2),
         "dense_equiv_tflops": round(wk["dense"] / (ms_per_step * 1e-3) / 1e12, 2),
+        "stage_rooflines": stage_rooflines(w, wk, stage_ms, perm_ms),
         "roofline": {"kernel": "hybrid attention (svgear_attention)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
