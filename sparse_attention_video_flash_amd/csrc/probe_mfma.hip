@@ -48,17 +48,17 @@ __device__ __forceinline__ float expm1_nonpos(float a, float w)
     return a > -0.0625f ? p : w - 1.f;
 }
 
-// Splits 8 fp32 values into packed bf16 hi and lo = bf16(x - hi) words.
+// Splits 8 fp32 values into packed bf16 hi and lo = bf16(x - hi) words
+// (round to nearest even: the conversions compile to v_cvt_pk_bf16_f32).
 __device__ __forceinline__ void split8(const float x[8], u32x4_t& hi, u32x4_t& lo)
 {
+    bf16x8_t h, l;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const bf16 h0 = f32_to_bf16(x[2 * k]), h1 = f32_to_bf16(x[2 * k + 1]);
-        const bf16 l0 = f32_to_bf16(x[2 * k] - bf16_to_f32(h0));
-        const bf16 l1 = f32_to_bf16(x[2 * k + 1] - bf16_to_f32(h1));
-        hi[k] = (unsigned)h0 | ((unsigned)h1 << 16);
-        lo[k] = (unsigned)l0 | ((unsigned)l1 << 16);
-    }
+    for (int k = 0; k < 8; ++k) h[k] = (__bf16)x[k];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) l[k] = (__bf16)(x[k] - (float)h[k]);
+    hi = __builtin_bit_cast(u32x4_t, h);
+    lo = __builtin_bit_cast(u32x4_t, l);
 }
 
 template <int NCBW>
