@@ -100,3 +100,12 @@ def test_forward_density_extremes(rho):
         assert cost == (0 if rho == 0.0 else 1380 * 1380)
     _check(w, 1380, 1380, rho, out, O, host)
 
+
+
+def test_forward_many_query_clusters_uses_generic_probe():
+    """Cq = 300 (above the MFMA probe's 256 query clusters): the generic probe
+    runs next to the MFMA k-means and attention on bf16, d = 128."""
+    w = _workload("bf16", 128, 300, 64)
+    log("many query clusters: Cq=300")
+    out, O, host = _run(w, 2400, 1380, 0.3, iters=3)
+    _check(w, 2400, 1380, 0.3, out, O, host, iters=3)
