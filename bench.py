@@ -157,16 +157,17 @@ def cpu_baseline(w, rho, rows_stride=16):
                        % (w.H, rows_stride, len(rows), t2 - t0))
 
 
-def traffic_entry(kernel_file):
+def traffic_entry(kernel_file, workload):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3
-    counter summary, if it was taken on the current kernel source; else None."""
+    counter summary, if it was taken on the current kernel source and on this
+    workload; else None."""
     path = os.path.join(ROOT, "profiles", "attention_counters.json")
     src = os.path.join(ROOT, "sparse_attention_video_flash_amd", "csrc", kernel_file)
     if not (os.path.exists(path) and os.path.exists(src)):
         return None
     rec = json.load(open(path))
     digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if rec.get("source_sha256") != digest:
+    if rec.get("source_sha256") != digest or not str(rec.get("workload", "")).startswith(workload + ":"):
         return None
     return rec.get("bytes_per_launch")
 
@@ -367,7 +368,7 @@ def main():
         "roofline": {"kernel": "hybrid attention (svgear_attention)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_entry("attn_mfma.hip")},
+                     "traffic": traffic_entry("attn_mfma.hip", w.name)},
     }
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample ...")
