@@ -328,11 +328,15 @@ __global__ __launch_bounds__(256, 2) void k_assign_partial(
     bf16x8_t xf[2][8];
     float nx[2];
     int tok[2], own[2];
+    float pub[2], plb[2], plr[2];   // stored bounds, fetched before the screen so their latency overlaps it
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
         tok[tb] = blockIdx.x * KM_TOK + wave * 64 + tb * 32 + tcol;
         const int row = tok[tb] < N ? tok[tb] : N - 1;
         own[tb] = mpos[(size_t)h * C + labels[(size_t)h * N + row]];   // list position or -1
+        pub[tb] = ub_own[(size_t)h * N + row];
+        plb[tb] = lb_own[(size_t)h * N + row];
+        plr[tb] = lb_rest[(size_t)h * N + row];
         const bf16* xp = Xh + (size_t)row * KM_D + half * 8;
         float ss = 0.f;
 #pragma unroll
@@ -415,9 +419,9 @@ __global__ __launch_bounds__(256, 2) void k_assign_partial(
             const float E = screen_error(nx[tb], R, cmax);
             const size_t t = (size_t)h * N + tok[tb];
             const bool own_moved = nod < __builtin_inff();
-            const float UBa = own_moved ? bound_up(nod + E) : ub_own[t];
-            const float LBa = own_moved ? bound_dn(nod - E) : lb_own[t];
-            const float LBr = lb_rest[t];
+            const float UBa = own_moved ? bound_up(nod + E) : pub[tb];
+            const float LBa = own_moved ? bound_dn(nod - E) : plb[tb];
+            const float LBr = plr[tb];
             const float LBo1 = bound_dn(nb1 - E), UBo1 = bound_up(nb1 + E), LBo2 = bound_dn(nb2 - E);
             if (UBa < fminf(LBr, LBo1)) {
                 ub_own[t] = UBa;
