@@ -61,7 +61,7 @@ __device__ __forceinline__ void split8(const float x[8], u32x4_t& hi, u32x4_t& l
     lo = __builtin_bit_cast(u32x4_t, l);
 }
 
-template <int NCBW>
+template <int NCBW, bool EPS>
 __global__ __launch_bounds__(256) void k_probe_mfma(
     const float* __restrict__ qbar, const int32_t* __restrict__ counts_q, const bf16* __restrict__ Kp,
     const float* __restrict__ kbar, const float* __restrict__ sbar, const float2* __restrict__ keys,
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(256) void k_probe_mfma(
                     }
 #pragma unroll
                     for (int r = 0; r < 4; ++r) S[i] = fmaf(f[r], __builtin_amdgcn_exp2f(u[r] - sh[i]), S[i]);
-                    if (log_eps2) {
+                    if (EPS) {
                         const int c = (wave + 4 * i) * 16 + col;
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
@@ -240,9 +240,14 @@ SVG_HIDDEN hipError_t launch_probe_mfma(const ProbeArgs& a, const float* sbar, c
     const float tau = 1.0f / sqrtf((float)PR_D);
 #define SVG_PROBE_CASE(n)                                                                          \
     case n:                                                                                        \
-        hipLaunchKernelGGL(k_probe_mfma<n>, dim3(gx, a.H), dim3(256), PR_LDS, st, a.qbar,         \
-                           a.counts_q, (const bf16*)a.Kp, a.kbar, sbar, keys, pg, a.offsets_k,     \
-                           a.Nk, a.Cq, a.Ck, tau, a.log_ratio, eps);                               \
+        if (eps)                                                                                   \
+            hipLaunchKernelGGL((k_probe_mfma<n, true>), dim3(gx, a.H), dim3(256), PR_LDS, st,      \
+                               a.qbar, a.counts_q, (const bf16*)a.Kp, a.kbar, sbar, keys, pg,      \
+                               a.offsets_k, a.Nk, a.Cq, a.Ck, tau, a.log_ratio, eps);              \
+        else                                                                                       \
+            hipLaunchKernelGGL((k_probe_mfma<n, false>), dim3(gx, a.H), dim3(256), PR_LDS, st,     \
+                               a.qbar, a.counts_q, (const bf16*)a.Kp, a.kbar, sbar, keys, pg,      \
+                               a.offsets_k, a.Nk, a.Cq, a.Ck, tau, a.log_ratio, eps);              \
         break;
     switch (ncbw) {
         SVG_PROBE_CASE(1) SVG_PROBE_CASE(2) SVG_PROBE_CASE(3) SVG_PROBE_CASE(4)
