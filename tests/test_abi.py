@@ -109,3 +109,19 @@ def test_probe_route_attention_forward_validation():
         == sv.E_WORKSPACE
     bad = _shape(d=32)
     assert L.svgear_forward(r(bad), 0.2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, big, None) == sv.E_SHAPE
+
+
+def test_route_rows_and_probe_variant_validation():
+    L = sv.load()
+    s = _shape()
+    big = sv.workspace_bytes(s)
+    r = ctypes.byref
+    for rho in (-0.1, 1.5, float("nan")):
+        assert L.svgear_route_rows(r(s), rho, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == sv.E_RHO
+    assert L.svgear_route_rows(r(s), 0.5, FAKE, FAKE, None, FAKE, FAKE, FAKE, big, None) == sv.E_NULL
+    assert L.svgear_route_rows(r(s), 0.5, FAKE, FAKE, FAKE, FAKE + 2, FAKE, FAKE, big, None) == sv.E_ALIGN
+    assert L.svgear_route_rows(r(s), 0.5, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 17, None) == sv.E_WORKSPACE
+    # the score ratio combines with neither the logit-only estimate nor the per-key debug output
+    for flags in (sv.PROBE_SCORE | sv.PROBE_LOGIT, sv.PROBE_SCORE | sv.DEBUG_EPS, 32):
+        assert L.svgear_probe(r(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, flags, FAKE, FAKE, FAKE, big,
+                              None) == sv.E_ARG
