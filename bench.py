@@ -172,6 +172,47 @@ def traffic_entry(kernel_file, workload):
     return rec.get("bytes_per_launch")
 
 
+def peaks(torch, dev):
+    """What this GPU sustains, to set the published peaks (8 TB/s HBM, 2.5 PFLOP/s
+    dense bf16) in context: a 4 GiB device copy (bytes read + written per
+    second) and a large bf16 GEMM through the vendor library (torch.matmul),
+    each the median of several event-timed runs."""
+    out = {}
+    n = 4 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    ts = []
+    for _ in range(6):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    t = float(np.median(ts[1:])) * 1e-3
+    out["hbm_copy"] = {"bytes": 2 * n, "ms": round(t * 1e3, 3), "achieved_GBs": round(2 * n / t / 1e9, 1),
+                       "published_GBs": PEAK_HBM_GBS, "frac": round(2 * n / t / 1e9 / PEAK_HBM_GBS, 4)}
+    del src, dst
+    m = 8192
+    a = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    c = a @ b
+    ts = []
+    for _ in range(6):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            c = a @ b
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) / 10)
+    t = float(np.median(ts[1:])) * 1e-3
+    fl = 2.0 * m * m * m
+    out["bf16_gemm"] = {"m=n=k": m, "ms": round(t * 1e3, 3), "achieved_TFLOPs": round(fl / t / 1e12, 1),
+                        "published_TFLOPs": PEAK_BF16_TFLOPS, "frac": round(fl / t / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    return out
+
+
 VARIANTS = (("error", False), ("logit", False), ("score", False), ("error", True), ("score", True))
 
 
@@ -242,6 +283,8 @@ def main():
     ap.add_argument("--rho", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows-stride", type=int, default=1)
+    ap.add_argument("--peaks", action="store_true",
+                    help="measure achievable HBM copy bandwidth and bf16 GEMM throughput on this GPU and exit")
     ap.add_argument("--quality", action="store_true",
                     help="compare the routing variants' output error against dense attention and exit")
     ap.add_argument("--quality-row-stride", type=int, default=16)
@@ -270,6 +313,9 @@ def main():
     dev = torch.device("cuda:0")
     w = WORKLOADS[args.workload or "wan"]
     rho = w.rhos[0] if args.rho is None else args.rho
+    if args.peaks:
+        print(json.dumps(peaks(torch, dev)), flush=True)
+        return
     if args.quality:
         wq = WORKLOADS[args.workload or "stress"]
         print(json.dumps(quality(wq, torch, dev, args.quality_row_stride)), flush=True)
