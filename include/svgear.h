@@ -14,7 +14,9 @@
  * ---------------------------------------
  * - Every tensor argument is a DEVICE pointer to contiguous, row-major memory
  *   owned by the caller.  The library allocates no device memory and keeps no
- *   state between calls apart from loaded code objects.
+ *   state between calls apart from loaded code objects and, per device, one
+ *   side stream and two events that svgear_forward creates on first use and
+ *   keeps until the process ends.
  * - Heads are independent.  Q is [H, Nq, d]; K and V are [H, Nk, d], in the
  *   element type given by svgear_shape.dtype (fp32 or bf16).  Cluster-indexed
  *   arrays are [H, C, ...], block arrays [H, Cq, Ck] with block (c, g) at
@@ -194,10 +196,14 @@ int svgear_attention(const svgear_shape* shape, const void* Qp, const int32_t* o
                      const uint8_t* mask, void* O, void* ws, size_t ws_bytes, void* stream);
 
 /* Steps 1-4 of [R] in one call: cluster Q and K, probe, route, hybrid
- * attention, all enqueued on `stream` without host synchronisation.  O
- * [H, Nq, d] receives the output in token order.  init_q [H, Cq] and init_k
- * [H, Ck] are the k-means initial token indices.  im may be NULL.  Errors as
- * the stages. */
+ * attention, all enqueued without host synchronisation.  O [H, Nq, d]
+ * receives the output in token order.  init_q [H, Cq] and init_k [H, Ck] are
+ * the k-means initial token indices.  im may be NULL.  The Q clustering runs
+ * on a per-device side stream (default priority) forked from `stream` by an
+ * event and joined back by another before the probe, so it overlaps the K
+ * clustering; everything else runs on `stream`, and when the call returns all
+ * of its work is ordered on `stream` (safe under stream capture).  `stream`
+ * must belong to the current device.  Errors as the stages. */
 int svgear_forward(const svgear_shape* shape, double rho, const void* Q, const void* K,
                    const void* V, const int32_t* init_q, const int32_t* init_k, void* O,
                    const svgear_intermediates* im, void* ws, size_t ws_bytes, void* stream);

@@ -23,9 +23,10 @@
 //      tile's math.
 // One online softmax (base-2 exponent) covers both kinds of terms.
 //
-// Workgroups are ordered so that the query tiles of one cluster run
-// back-to-back on the same XCD (workgroup ids are dealt round-robin over the
-// eight XCDs), letting them share key/value lines in that XCD's L2.
+// The kernel is persistent (two workgroups per CU) and takes query tiles from
+// eight work queues, one per XCD: tiles are dealt to queue c mod 8 by query
+// cluster, so the tiles of one cluster, which read the same keys, run
+// together on one XCD and share its L2 (see the queue kernels below).
 #include "internal.h"
 
 namespace svg {
