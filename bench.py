@@ -172,6 +172,60 @@ def traffic_entry(kernel_file, workload):
     return rec.get("bytes_per_launch")
 
 
+def probe_vs_torch(w, torch, dev, steps):
+    """Context for the pages' claim that their error-estimation kernel beats
+    native PyTorch: the value-aware estimate and its block ratios written as
+    plain PyTorch tensor operations (fp32, logits materialised per head, raw
+    exponentials as printed), timed against svgear_probe on the same clustered
+    inputs.  Returns both times and their ratio."""
+    Q, K, V, iq, ik = upload(w, torch, dev)
+    shape = sv.make_shape(w.H, w.N, w.N, w.d, w.Cq, w.Ck, w.iters, sv.BF16 if w.dtype == "bf16" else sv.F32)
+    ws = sv.alloc_workspace(shape, dev)
+    im = sv.alloc_intermediates(shape, dev)
+    O = torch.empty_like(Q)
+    sv.forward(shape, w.rhos[0], Q, K, V, iq, ik, O, ws, im)
+    torch.cuda.synchronize()
+    tau = 1.0 / np.sqrt(w.d)
+
+    def torch_probe():
+        out = []
+        for h in range(w.H):
+            kp, vp = im["Kp"][h].float(), im["Vp"][h].float()
+            qb, kb, vb = im["qbar"][h], im["kbar"][h], im["vbar"][h]
+            cnt = im["counts_k"][h]
+            g = torch.repeat_interleave(torch.arange(w.Ck, device=dev), cnt.long(), output_size=w.N)
+            b = torch.exp(tau * (qb @ kp.T))                       # [Cq, Nk]
+            a = torch.exp(tau * (qb @ kb.T))[:, g]                  # [Cq, Nk]
+            r = (vp * vp).sum(1)
+            x = (vb[g] * vp).sum(1)
+            pg = (vb * vb).sum(1)[g]
+            e = a * a * pg - 2.0 * a * b * x + b * b * r
+            E = torch.zeros(w.Cq, w.Ck, device=dev).index_add_(1, g, e)
+            out.append(E / cnt.clamp(min=1).float())
+        return out
+
+    def ours():
+        sv.probe(shape, im["qbar"], im["counts_q"], im["Kp"], im["Vp"], im["kbar"], im["vbar"], im["counts_k"],
+                 im["offsets_k"], im["log_ratio"], ws)
+
+    res = {}
+    for name, fn in (("torch", torch_probe), ("svgear_probe", ours)):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(max(steps, 3)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        res[name + "_ms"] = round(float(np.median(ts)), 4)
+    res["speedup"] = round(res["torch_ms"] / res["svgear_probe_ms"], 2)
+    res["workload"] = "%s: %d heads x %d tokens, Cq=%d, Ck=%d" % (w.name, w.H, w.N, w.Cq, w.Ck)
+    return res
+
+
 def peaks(torch, dev):
     """What this GPU sustains, to set the published peaks (8 TB/s HBM, 2.5 PFLOP/s
     dense bf16) in context: a 4 GiB device copy (bytes read + written per
@@ -283,6 +337,8 @@ def main():
     ap.add_argument("--rho", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows-stride", type=int, default=1)
+    ap.add_argument("--probe-vs-torch", action="store_true",
+                    help="time the probe stage against the same estimate written in plain PyTorch and exit")
     ap.add_argument("--peaks", action="store_true",
                     help="measure achievable HBM copy bandwidth and bf16 GEMM throughput on this GPU and exit")
     ap.add_argument("--quality", action="store_true",
@@ -313,6 +369,9 @@ def main():
     dev = torch.device("cuda:0")
     w = WORKLOADS[args.workload or "wan"]
     rho = w.rhos[0] if args.rho is None else args.rho
+    if args.probe_vs_torch:
+        print(json.dumps(probe_vs_torch(WORKLOADS[args.workload or "wan"], torch, dev, args.steps)), flush=True)
+        return
     if args.peaks:
         print(json.dumps(peaks(torch, dev)), flush=True)
         return
