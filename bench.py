@@ -172,6 +172,44 @@ def traffic_entry(kernel_file, workload):
     return rec.get("bytes_per_launch")
 
 
+def vs_dense(w, torch, dev, steps):
+    """Context for the pages' end-to-end speed-ups: dense attention over the same
+    Q, K, V through PyTorch's fused attention (flash or memory-efficient
+    kernels only; the unfused path would need the full score matrix), and one
+    svgear_forward call, both event-timed on this GPU."""
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    Q, K, V, iq, ik = upload(w, torch, dev)
+    shape = sv.make_shape(w.H, w.N, w.N, w.d, w.Cq, w.Ck, w.iters, sv.BF16 if w.dtype == "bf16" else sv.F32)
+    ws = sv.alloc_workspace(shape, dev)
+    O = torch.empty_like(Q)
+    res = {}
+
+    def dense():
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
+            return torch.nn.functional.scaled_dot_product_attention(Q[None], K[None], V[None])
+
+    def ours():
+        sv.forward(shape, w.rhos[0], Q, K, V, iq, ik, O, ws)
+
+    for name, fn in (("dense_sdpa", dense), ("svgear_forward", ours)):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(max(steps, 3)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        res[name + "_ms"] = round(float(np.median(ts)), 3)
+    dense_flops = 4.0 * w.N * w.N * w.d * w.H
+    res["dense_sdpa_tflops"] = round(dense_flops / (res["dense_sdpa_ms"] * 1e-3) / 1e12, 1)
+    res["speedup"] = round(res["dense_sdpa_ms"] / res["svgear_forward_ms"], 2)
+    res["workload"] = "%s: %d heads x %d tokens, d=%d, rho=%g" % (w.name, w.H, w.N, w.d, w.rhos[0])
+    return res
+
+
 def probe_vs_torch(w, torch, dev, steps):
     """Context for the pages' claim that their error-estimation kernel beats
     native PyTorch: the value-aware estimate and its block ratios written as
@@ -337,6 +375,8 @@ def main():
     ap.add_argument("--rho", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows-stride", type=int, default=1)
+    ap.add_argument("--vs-dense", action="store_true",
+                    help="time dense attention (PyTorch's fused scaled_dot_product_attention) on the workload and exit")
     ap.add_argument("--probe-vs-torch", action="store_true",
                     help="time the probe stage against the same estimate written in plain PyTorch and exit")
     ap.add_argument("--peaks", action="store_true",
@@ -369,6 +409,9 @@ def main():
     dev = torch.device("cuda:0")
     w = WORKLOADS[args.workload or "wan"]
     rho = w.rhos[0] if args.rho is None else args.rho
+    if args.vs_dense:
+        print(json.dumps(vs_dense(WORKLOADS[args.workload or "wan"], torch, dev, args.steps)), flush=True)
+        return
     if args.probe_vs_torch:
         print(json.dumps(probe_vs_torch(WORKLOADS[args.workload or "wan"], torch, dev, args.steps)), flush=True)
         return
