@@ -414,3 +414,35 @@ def test_forward_equals_stage_by_stage_path(case):
         for k, v in im2.items():
             assert torch.equal(v.cpu(), ref[k]), "%s differs on call %d" % (k, rep)
         assert torch.equal(O.cpu(), O_ref.cpu()), "output differs on call %d" % rep
+
+
+def test_forward_replays_from_a_hip_graph():
+    """svgear_forward captured into a HIP graph (torch.cuda.graph) and replayed
+    several times, with eager work and synchronisations in between: every
+    replay equals the eager call bit for bit (the side-stream fork/join, the
+    queue counters and every cleared buffer are graph-safe: kernels only)."""
+    torch = torch_gpu()
+    w = CASES["small"]
+    log("forward under graph capture")
+    data = upload(w)
+    H = len(data["heads"])
+    shape = shape_of(w, H)
+    ws = sv.alloc_workspace(shape)
+    rho = w.rhos[0]
+    O_ref = torch.empty_like(data["Q"])
+    sv.forward(shape, rho, data["Q"], data["K"], data["V"], data["init_q"], data["init_k"], O_ref, ws)
+    torch.cuda.synchronize()
+    ref = O_ref.cpu()
+    O = torch.empty_like(data["Q"])
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sv.forward(shape, rho, data["Q"], data["K"], data["V"], data["init_q"], data["init_k"], O, ws)
+    for rep in range(4):
+        O.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(O.cpu(), ref), "replay %d differs from the eager call" % rep
+        # eager work between replays, on the same workspace
+        sv.forward(shape, rho, data["Q"], data["K"], data["V"], data["init_q"], data["init_k"], O_ref, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(O_ref.cpu(), ref)
