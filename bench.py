@@ -447,6 +447,21 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     log("timed %d calls: %.3f ms/call" % (args.steps, ms_per_step))
 
+    # The same call captured once in a HIP graph and replayed (reported beside
+    # the headline, which stays the eager call).
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sv.forward(shape, rho, Q, K, V, iq, ik, O, ws, im)
+    graph.replay()
+    torch.cuda.synchronize()
+    tg = time.perf_counter()
+    for s in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_ms = (time.perf_counter() - tg) * 1e3 / args.steps
+    del graph
+    log("graph replay: %.3f ms/call" % graph_ms)
+
     # Second timed region: the same path through the per-stage entry points, one
     # after another on one stream, with HIP events between the stages (stage
     # breakdown and the attention kernel's duration for the roofline).
@@ -508,6 +523,7 @@ def main():
                    "parallelism": "single GPU"},
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "staged_ms_per_call": round(staged_ms, 4),
+        "graph_replay_ms_per_call": round(graph_ms, 4),
         "routing_share": round(routing_ms / sum(stage_ms.values()), 4),
         "realised_density": round(wk["density"], 5),
         "executed_tflops": round(executed / (ms_per_step * 1e-3) / 1e12, 2),
