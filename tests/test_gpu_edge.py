@@ -109,3 +109,23 @@ def test_forward_many_query_clusters_uses_generic_probe():
     log("many query clusters: Cq=300")
     out, O, host = _run(w, 2400, 1380, 0.3, iters=3)
     _check(w, 2400, 1380, 0.3, out, O, host, iters=3)
+
+
+def test_forward_single_query_cluster():
+    """Cq = 1: every query tile of a head belongs to one cluster, so one work
+    queue of the attention kernel holds them all and the other queues' workgroups
+    take work from it."""
+    w = _workload("bf16", 128, 1, 37)
+    log("single query cluster")
+    out, O, host = _run(w, 1380, 1380, 0.3, iters=3)
+    _check(w, 1380, 1380, 0.3, out, O, host, iters=3)
+
+
+def test_forward_largest_key_cluster_count():
+    """Ck = 4096, the largest supported cluster count (route, segment lists and
+    compensation lists at their maximum length)."""
+    w = Workload("edge_maxc", 1, (2, 64, 64), 128, "bf16", 16, 4096, 2, (0.3,), 13,
+                 (Mixture((0, 1), 64, (2, 4, 4), 0.25, "normal", 0.08, 2.0, "add"),))
+    log("largest key cluster count: Ck=4096, N=8192")
+    out, O, host = _run(w, 8192, 8192, 0.3, iters=2)
+    _check(w, 8192, 8192, 0.3, out, O, host, iters=2)
