@@ -2,7 +2,7 @@
 // SVG-EAR pipeline: exact blocks plus parameter-free centroid compensation,
 // review page inference-pipeline paragraph; German summary 2A).
 //
-// One workgroup (4 waves) owns a tile of BM = 128 reordered query rows of one
+// One workgroup (8 waves) owns a tile of BM = 256 reordered query rows of one
 // query cluster c; each wave owns 32 queries.  Scores are computed transposed,
 // S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so every lane holds one query
 // column and the softmax row statistics stay inside a lane (one exchange with
@@ -23,7 +23,7 @@
 //      tile's math.
 // One online softmax (base-2 exponent) covers both kinds of terms.
 //
-// The kernel is persistent (two workgroups per CU) and takes query tiles from
+// The kernel is persistent (one workgroup per CU) and takes query tiles from
 // eight work queues, one per XCD: tiles are dealt to queue c mod 8 by query
 // cluster, so the tiles of one cluster, which read the same keys, run
 // together on one XCD and share its L2 (see the queue kernels below).
@@ -38,7 +38,7 @@ typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
-constexpr int AT_WAVES = 4;                  // 32 query rows per wave
+constexpr int AT_WAVES = 8;                  // 32 query rows per wave; one workgroup per CU
 constexpr int AT_BM = 32 * AT_WAVES;
 constexpr int AT_BN = 64;
 constexpr int AT_D = 128;
@@ -54,8 +54,8 @@ constexpr int ROW_B = AT_D * 2;          // 256
 constexpr int T_BUF = AT_BN * ROW_B;     // 16384
 constexpr int AT_NBUF = 2;
 constexpr int K_PITCH = AT_D * 2 + 16;   // output staging rows (272 B)
-constexpr int AT_LDS = AT_NBUF * 2 * T_BUF + AT_BN * 4 + AT_BN * 4 + 16;  // + bias, map, job slot
-static_assert(AT_BM * K_PITCH <= AT_NBUF * 2 * T_BUF, "output staging fits the tile buffers");
+constexpr int AT_AREA = AT_NBUF * 2 * T_BUF > AT_BM * K_PITCH ? AT_NBUF * 2 * T_BUF : AT_BM * K_PITCH;
+constexpr int AT_LDS = AT_AREA + AT_BN * 4 + AT_BN * 4 + 16;  // + bias, map, job slot
 static_assert(ST_ROWS * ST_STEP == AT_BN, "staging covers a tile");
 static_assert(AT_BM == kAttnRows, "tile rows as sized in the workspace layout");
 constexpr int AT_XCD = 8;
@@ -694,9 +694,9 @@ __global__ __launch_bounds__(AT_THREADS, 2) void k_attn_mfma(
     int tiles_per_head, float scale2, bf16* __restrict__ O)
 {
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    float* const s_bias = (float*)(smem + AT_NBUF * 2 * T_BUF);
-    int* const s_map = (int*)(smem + AT_NBUF * 2 * T_BUF + AT_BN * 4);  // [64]
-    int* const s_job = (int*)(smem + AT_NBUF * 2 * T_BUF + 2 * AT_BN * 4);
+    float* const s_bias = (float*)(smem + AT_AREA);
+    int* const s_map = (int*)(smem + AT_AREA + AT_BN * 4);  // [64]
+    int* const s_job = (int*)(smem + AT_AREA + 2 * AT_BN * 4);
 
     const int x0 = blockIdx.x % AT_XCD;
     for (int k = 0; k < AT_XCD; ++k) {
@@ -755,11 +755,11 @@ SVG_HIDDEN hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t st)
     hipLaunchKernelGGL(k_queue_fill, dim3(a.H), dim3(256), 0, st, tstart, qcnt, qpre, a.H, a.Cq,
                        tiles_per_head, qmeta, qlist);
     zero_words(qmeta + 2 * AT_XCD, AT_XCD * 4, st);
-    // persistent: two workgroups per CU (the occupancy the register use allows)
+    // persistent: one workgroup per CU (two waves per SIMD, the occupancy the register use allows)
     int dev = 0, ncu = 256;
     if (hipGetDevice(&dev) == hipSuccess)
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-    const int nwg = 2 * (ncu > 0 ? ncu : 256);
+    const int nwg = ncu > 0 ? ncu : 256;   // one 8-wave workgroup per CU (two waves per SIMD)
     const float scale2 = (float)(1.4426950408889634 / sqrt((double)AT_D));
     hipLaunchKernelGGL(k_attn_mfma, dim3(nwg), dim3(AT_THREADS), AT_LDS, st,
                        (const bf16*)a.Qp, a.offsets_q, a.perm_q, (const bf16*)a.Kp,
