@@ -369,9 +369,18 @@ __device__ __forceinline__ float pair_sum(float x)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Online softmax with raw scores x (logit = x * scale2 + bias, base 2); the
-// accumulators are rescaled as soon as some lane's running max grows.
-// Returns the probabilities as PV B-operand fragments pf[kb * 2 + ks].
+// Online softmax with raw scores x (logit = x * scale2 + bias, base 2) against
+// a lazily raised reference max st.m: O and l are rescaled only when some
+// lane's tile max exceeds the reference by more than kLazy, so the weights
+// stay at most 2^kLazy.  O and l always share one reference, so the final
+// O / l is unchanged, and bf16 and fp32 keep their relative precision at any
+// such magnitude.  The normaliser sums the bf16-rounded weights that the PV
+// product uses (v_dot2 against ones).  Returns the weights as PV B-operand
+// fragments pf[kb * 2 + ks].
+constexpr float kLazy = 8.f;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ void softmax_update(Softmax& st, const f32x16_t x[2], float scale2,
                                                bf16x8_t pf[4])
 {
@@ -381,31 +390,32 @@ __device__ __forceinline__ void softmax_update(Softmax& st, const f32x16_t x[2],
 #pragma unroll
         for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, x[kb][i]);
     mloc = pair_max(mloc) * scale2;
-    const float mnew = fmaxf(st.m, mloc);
-    const float muse = mnew == -__builtin_inff() ? 0.f : mnew;
-    if (__any(mnew > st.m)) {
-        const float alpha = __builtin_amdgcn_exp2f(st.m - muse);
+    if (__any(mloc > st.m + kLazy)) {
+        const float mnew = fmaxf(st.m, mloc);
+        const float alpha = __builtin_amdgcn_exp2f(st.m - mnew);   // 0 while st.m = -inf
         st.l *= alpha;
 #pragma unroll
         for (int db = 0; db < 4; ++db) st.o[db] *= alpha;
+        st.m = mnew;
     }
-    st.m = mnew;
-    float sum = 0.f;
+    const float muse = st.m == -__builtin_inff() ? 0.f : st.m;
+    const bf16x2_t one = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
+    float sum = st.l;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             bf16x8_t f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(x[kb][8 * ks + i], scale2, -muse));
-                sum += p;
-                f[i] = (__bf16)p;
-            }
+            for (int i = 0; i < 8; ++i)
+                f[i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(x[kb][8 * ks + i], scale2, -muse));
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                sum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{f[2 * j], f[2 * j + 1]}, one, sum, false);
             pf[kb * 2 + ks] = f;
         }
     }
-    st.l += sum;
+    st.l = sum;
 }
 
 // O^T += V^T P^T for one 64-key tile held row-major in vbuf (transpose loads),
