@@ -43,8 +43,6 @@ constexpr int AT_BM = 32 * AT_WAVES;
 constexpr int AT_BN = 64;
 constexpr int AT_D = 128;
 constexpr int AT_THREADS = 64 * AT_WAVES;
-constexpr int ST_STEP = AT_THREADS / 16;     // rows staged per pass (16 lanes x 16 B per row)
-constexpr int ST_ROWS = AT_BN / ST_STEP;     // rows of a 64-row tile per thread
 // Key and value tiles: 64 rows of 256 B, unpadded, the 16-B chunks of each row
 // XOR-swizzled so that the score reads (16 rows, one chunk) and the transpose
 // reads (4 rows, 4 chunks) hit distinct banks.  The exact tiles are written
@@ -54,9 +52,14 @@ constexpr int ROW_B = AT_D * 2;          // 256
 constexpr int T_BUF = AT_BN * ROW_B;     // 16384
 constexpr int AT_NBUF = 2;
 constexpr int K_PITCH = AT_D * 2 + 16;   // output staging rows (272 B)
-constexpr int AT_AREA = AT_NBUF * 2 * T_BUF > AT_BM * K_PITCH ? AT_NBUF * 2 * T_BUF : AT_BM * K_PITCH;
-constexpr int AT_LDS = AT_AREA + AT_BN * 4 + AT_BN * 4 + 16;  // + bias, map, job slot
-static_assert(ST_ROWS * ST_STEP == AT_BN, "staging covers a tile");
+// Compensation tiles: k-bar hi, k-bar lo, v-bar hi, v-bar lo planes of 64
+// centroids per buffer, two buffers, then the two buffers' biases.
+constexpr int C_BUF = 4 * T_BUF;
+constexpr int C_AREA = 2 * C_BUF + 2 * AT_BN * 4;
+constexpr int at_max(int a, int b) { return a > b ? a : b; }
+constexpr int AT_AREA = at_max(C_AREA, at_max(AT_NBUF * 2 * T_BUF, AT_BM * K_PITCH));
+constexpr int AT_LDS = AT_AREA + 16;  // + job slot
+static_assert(AT_LDS <= 160 * 1024, "LDS of one workgroup");
 static_assert(AT_BM == kAttnRows, "tile rows as sized in the workspace layout");
 constexpr int AT_XCD = 8;
 
@@ -280,39 +283,6 @@ __global__ __launch_bounds__(256) void k_queue_fill(const int* __restrict__ tsta
     for (int c = tid; c < Cq; c += 256) {
         const int base = s_base[c % kXcd] + pre[(size_t)h * Cq + c];
         for (int t = ts[c]; t < ts[c + 1]; ++t) list[base + (t - ts[c])] = h * tiles_per_head + t;
-    }
-}
-
-// ----------------------------------------------------------------------------- tile staging
-
-// Rows kr + 16 i (i = 0..3), 16-byte chunk kc of K and V; row r of the tile is
-// source row map[r] (always a valid row: rows past the list are clamped and
-// masked out later).
-struct Stage {
-    u32x4_t k[ST_ROWS];
-    u32x4_t v[ST_ROWS];
-};
-
-__device__ __forceinline__ void stage_load(Stage& s, const bf16* __restrict__ K,
-                                           const bf16* __restrict__ V, const int* map, int tid)
-{
-    const int kc = tid & 15, kr = tid >> 4;
-#pragma unroll
-    for (int i = 0; i < ST_ROWS; ++i) {
-        const size_t row = (size_t)map[kr + ST_STEP * i];
-        s.k[i] = *(const u32x4_t*)(K + row * AT_D + kc * 8);
-        s.v[i] = *(const u32x4_t*)(V + row * AT_D + kc * 8);
-    }
-}
-
-__device__ __forceinline__ void stage_store(const Stage& s, char* kbuf, char* vbuf, int tid)
-{
-    const int kc = tid & 15, kr = tid >> 4;
-#pragma unroll
-    for (int i = 0; i < ST_ROWS; ++i) {
-        const int r = kr + ST_STEP * i;
-        *(u32x4_t*)(kbuf + r * ROW_B + k_pos(r, kc) * 16) = s.k[i];
-        *(u32x4_t*)(vbuf + r * ROW_B + v_pos(r, kc) * 16) = s.v[i];
     }
 }
 
@@ -559,6 +529,90 @@ __device__ __forceinline__ void exact_tiles(char* __restrict__ b0, char* __restr
 #undef ROWS
 }
 
+// ----------------------------------------------------------------------------- compensation tiles
+
+// The compensation tiles of one query tile: the key clusters skipped for this
+// query cluster and non-empty (packed list cl, nc entries), 64 per tile.  A
+// tile holds the bf16 hi and lo planes of k-bar and v-bar of its centroids and
+// their biases log2 m_g; like the exact tiles, its rows are gathered by index
+// straight into LDS (the bias with one dword load per lane, by wave 0), two
+// buffers deep, the next tile's loads in flight during the current tile's math.
+__device__ __forceinline__ void comp_fill(char* b, float* bias, __amdgpu_buffer_rsrc_t rkh,
+                                          __amdgpu_buffer_rsrc_t rkl, __amdgpu_buffer_rsrc_t rvh,
+                                          __amdgpu_buffer_rsrc_t rvl, __amdgpu_buffer_rsrc_t rlm, int wv,
+                                          const int r[FILL_N], int br, const int kx[FILL_N], int vx)
+{
+    char* kh = b + FILL_ROWS * wv * ROW_B;
+#pragma unroll
+    for (int i = 0; i < FILL_N; ++i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rkh, (lds_ptr)(kh + 4 * i * ROW_B), 16, r[i] * ROW_B + kx[i], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rkl, (lds_ptr)(kh + T_BUF + 4 * i * ROW_B), 16, r[i] * ROW_B + kx[i], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < FILL_N; ++i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rvh, (lds_ptr)(kh + 2 * T_BUF + 4 * i * ROW_B), 16, r[i] * ROW_B + vx, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rvl, (lds_ptr)(kh + 3 * T_BUF + 4 * i * ROW_B), 16, r[i] * ROW_B + vx, 0, 0, 0);
+    }
+    if (wv == 0) __builtin_amdgcn_raw_ptr_buffer_load_lds(rlm, (lds_ptr)bias, 4, br * 4, 0, 0, 0);
+}
+
+__device__ __forceinline__ void comp_tiles(char* __restrict__ c0, char* __restrict__ c1, float* __restrict__ bias0,
+                                           float* __restrict__ bias1, Softmax& st, const bf16x8_t qf[8],
+                                           __amdgpu_buffer_rsrc_t rkh, __amdgpu_buffer_rsrc_t rkl,
+                                           __amdgpu_buffer_rsrc_t rvh, __amdgpu_buffer_rsrc_t rvl,
+                                           __amdgpu_buffer_rsrc_t rlm, const int* __restrict__ cl, int nc,
+                                           int wave, int lane, bool wact, float scale2)
+{
+    const int ntiles = (nc + AT_BN - 1) / AT_BN;
+    const int half = lane >> 5;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int lr = FILL_ROWS * wv + (lane >> 4), p = lane & 15;
+    int kx[FILL_N];
+#pragma unroll
+    for (int i = 0; i < FILL_N; ++i) kx[i] = k_pos(lr + 4 * i, p) * 16;
+    const int vx = v_pos(lr, p) * 16;   // rows lr + 4 i share it
+    int ra[FILL_N], rb[FILL_N], ba, bb;
+#define CROWS(SET, B, T)                                                                      \
+    _Pragma("unroll") for (int i = 0; i < FILL_N; ++i)                                        \
+        SET[i] = cl[min((T) * AT_BN + lr + 4 * i, nc - 1)];                                   \
+    B = cl[min((T) * AT_BN + lane, nc - 1)];
+    CROWS(ra, ba, 0)
+    CROWS(rb, bb, 1)
+    comp_fill(c0, bias0, rkh, rkl, rvh, rvl, rlm, wv, ra, ba, kx, vx);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | 0);
+    tile_barrier();
+#define COMP_STEP(T, CUR, NXT, BCUR, BNXT, RT, BT, RN, BN)                                    \
+    {                                                                                         \
+        CROWS(RT, BT, (T) + 2)           /* rows of tile T + 2 (set of tile T, now free) */   \
+        comp_fill(NXT, BNXT, rkh, rkl, rvh, rvl, rlm, wv, RN, BN, kx, vx);   /* tile T + 1 */ \
+        if (wact && (T) < ntiles) {                                                           \
+            f32x16_t acc[2] = {f32x16_t{0}, f32x16_t{0}};                                     \
+            tile_scores(acc, CUR, qf, lane);                                                  \
+            tile_scores(acc, CUR + T_BUF, qf, lane);                                          \
+            /* logit = acc * scale2 + bias: fold the bias in as acc + bias / scale2 */        \
+            _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                                  \
+                _Pragma("unroll") for (int i = 0; i < 16; ++i) {                              \
+                    const int kt = kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);               \
+                    acc[kb][i] = fmaf(BCUR[kt], 1.0f / scale2, acc[kb][i]);                   \
+                }                                                                             \
+            const int nvalid = nc - (T) * AT_BN;                                              \
+            if (nvalid < AT_BN) mask_rows(acc, nvalid, half);                                 \
+            bf16x8_t pf[4];                                                                   \
+            softmax_update(st, acc, scale2, pf);                                              \
+            tile_pv(st, CUR + 2 * T_BUF, pf, lane);                                           \
+            tile_pv(st, CUR + 3 * T_BUF, pf, lane);                                           \
+        }                                                                                     \
+        __builtin_amdgcn_s_waitcnt(0x0F70 | 0);   /* tile T + 1 and rows of T + 2 landed */   \
+        tile_barrier();                                                                       \
+    }
+    for (int t = 0; t < ntiles; t += 2) {
+        COMP_STEP(t, c0, c1, bias0, bias1, ra, ba, rb, bb)
+        COMP_STEP(t + 1, c1, c0, bias1, bias0, rb, bb, ra, ba)
+    }
+#undef COMP_STEP
+#undef CROWS
+}
+
 // ----------------------------------------------------------------------------- main kernel
 
 #define KBUF(b) (smem + (b) * 2 * T_BUF)
@@ -566,7 +620,7 @@ __device__ __forceinline__ void exact_tiles(char* __restrict__ b0, char* __restr
 
 // One query tile: logical index h * tiles_per_head + tile-in-head.
 __device__ __forceinline__ void attn_tile(
-    int logical, char* smem, float* s_bias, int* s_map, const bf16* __restrict__ Qp,
+    int logical, char* smem, const bf16* __restrict__ Qp,
     const int32_t* __restrict__ offsets_q, const int32_t* __restrict__ perm_q,
     const bf16* __restrict__ Kp, const bf16* __restrict__ Vp, const bf16* __restrict__ kbh,
     const bf16* __restrict__ kbl, const bf16* __restrict__ vbh, const bf16* __restrict__ vbl,
@@ -610,43 +664,18 @@ __device__ __forceinline__ void attn_tile(
     const float* lm = logm2 + (size_t)h * Ck;
 
     // 1. compensation tiles: packed list of skipped non-empty key clusters
-    {
-        const int nc = ncomp[hc];
-        const int* cl = comp + hc * Ck;
+    const int nc = ncomp[hc];
+    if (nc > 0) {
         const size_t pb = (size_t)h * Ck * AT_D;
-        for (int v0 = 0; v0 < nc; v0 += AT_BN) {
-            const int nv = min(AT_BN, nc - v0);
-            if (tid < AT_BN) {
-                const int g = cl[v0 + (tid < nv ? tid : 0)];
-                s_map[tid] = g;
-                s_bias[tid] = tid < nv ? lm[g] : -__builtin_inff();
-            }
-            __syncthreads();
-            Stage sh, sl;
-            stage_load(sh, kbh + pb, vbh + pb, s_map, tid);
-            stage_load(sl, kbl + pb, vbl + pb, s_map, tid);
-            stage_store(sh, KBUF(0), VBUF(0), tid);
-            stage_store(sl, KBUF(1), VBUF(1), tid);
-            __syncthreads();
-            if (wact) {
-                f32x16_t acc[2] = {f32x16_t{0}, f32x16_t{0}};
-                tile_scores(acc, KBUF(0), qf, lane);
-                tile_scores(acc, KBUF(1), qf, lane);
-                // logit = acc * scale2 + bias: fold the bias in as acc + bias / scale2
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int kt = kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-                        acc[kb][i] = fmaf(s_bias[kt], 1.0f / scale2, acc[kb][i]);
-                    }
-                bf16x8_t pf[4];
-                softmax_update(st, acc, scale2, pf);
-                tile_pv(st, VBUF(0), pf, lane);
-                tile_pv(st, VBUF(1), pf, lane);
-            }
-            __syncthreads();
-        }
+        const int plane_bytes = Ck * AT_D * 2;
+        const __amdgpu_buffer_rsrc_t rkh = __builtin_amdgcn_make_buffer_rsrc((void*)(kbh + pb), (short)0, plane_bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rkl = __builtin_amdgcn_make_buffer_rsrc((void*)(kbl + pb), (short)0, plane_bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rvh = __builtin_amdgcn_make_buffer_rsrc((void*)(vbh + pb), (short)0, plane_bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rvl = __builtin_amdgcn_make_buffer_rsrc((void*)(vbl + pb), (short)0, plane_bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rlm = __builtin_amdgcn_make_buffer_rsrc((void*)lm, (short)0, Ck * 4, 0x00020000);
+        float* const cb = (float*)(smem + 2 * C_BUF);
+        comp_tiles(smem, smem + C_BUF, cb, cb + AT_BN, st, qf, rkh, rkl, rvh, rvl, rlm, comp + hc * Ck, nc, wave,
+                   lane, wact, scale2);
     }
 
     // 2. exact tiles (packed routed keys)
@@ -665,7 +694,7 @@ __device__ __forceinline__ void attn_tile(
     const float ltot = pair_sum(st.l);
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     __syncthreads();
-    char* ost = smem;  // 128 rows x K_PITCH bytes = 2 K buffers
+    char* ost = smem;  // AT_BM rows x K_PITCH bytes
     {
         const int r = wave * 32 + qcol;
 #pragma unroll
@@ -704,9 +733,7 @@ __global__ __launch_bounds__(AT_THREADS, 2) void k_attn_mfma(
     int tiles_per_head, float scale2, bf16* __restrict__ O)
 {
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    float* const s_bias = (float*)(smem + AT_AREA);
-    int* const s_map = (int*)(smem + AT_AREA + AT_BN * 4);  // [64]
-    int* const s_job = (int*)(smem + AT_AREA + 2 * AT_BN * 4);
+    int* const s_job = (int*)(smem + AT_AREA);
 
     const int x0 = blockIdx.x % AT_XCD;
     for (int k = 0; k < AT_XCD; ++k) {
@@ -718,7 +745,7 @@ __global__ __launch_bounds__(AT_THREADS, 2) void k_attn_mfma(
             __syncthreads();
             const int j = *s_job;
             if (j >= qlen) break;
-            attn_tile(qlist[qstart + j], smem, s_bias, s_map, Qp, offsets_q, perm_q, Kp, Vp, kbh, kbl,
+            attn_tile(qlist[qstart + j], smem, Qp, offsets_q, perm_q, Kp, Vp, kbh, kbl,
                       vbh, vbl, logm2, rowmap, nkeys, comp, ncomp, tstart, Nq, Nk, Cq, Ck, tiles_per_head,
                       scale2, O);
         }
