@@ -151,23 +151,35 @@ def cpu_baseline(w, rho, rows_stride=16):
     oracle.hybrid(q, k, v, lq, lk, kbar, vbar, ck, mask, rows)
     t2 = time.perf_counter()
     per_head_s = (t1 - t0) + (t2 - t1) * (w.N / float(len(rows)))
+    which = "every query row" if rows_stride == 1 else "every %dth query row" % rows_stride
     return dict(value=per_head_s * w.H * 1e3, unit="ms/call", cores=threads, kind="oracle",
-                sample="head 0 of %d: full k-means, probe, route; hybrid output on every %dth query row "
-                       "(%d rows), scaled by rows and heads; %.1f s of CPU work"
-                       % (w.H, rows_stride, len(rows), t2 - t0))
+                sample="head 0 of %d: full k-means, probe, route; hybrid output on %s (%d rows), "
+                       "scaled by rows and heads; %.1f s of CPU work"
+                       % (w.H, which, len(rows), t2 - t0))
+
+
+def code_digest(path):
+    """sha256 of a C++/HIP source with its comments and white space removed, so
+    that an edit of comments alone does not mark counters taken on the same
+    code as stale."""
+    import re
+    text = open(path, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = re.sub(r"\s+", "", text)
+    return hashlib.sha256(text.encode("utf-8")).hexdigest()
 
 
 def traffic_entry(kernel_file, workload):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3
-    counter summary, if it was taken on the current kernel source and on this
+    counter summary, if it was taken on the current kernel code and on this
     workload; else None."""
     path = os.path.join(ROOT, "profiles", "attention_counters.json")
     src = os.path.join(ROOT, "sparse_attention_video_flash_amd", "csrc", kernel_file)
     if not (os.path.exists(path) and os.path.exists(src)):
         return None
     rec = json.load(open(path))
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if rec.get("source_sha256") != digest or not str(rec.get("workload", "")).startswith(workload + ":"):
+    if rec.get("code_sha256") != code_digest(src) or not str(rec.get("workload", "")).startswith(workload + ":"):
         return None
     return rec.get("bytes_per_launch")
 

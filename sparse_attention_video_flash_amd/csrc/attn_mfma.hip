@@ -17,11 +17,11 @@
 //   1. compensation tiles: the centroids of the key clusters that are skipped
 //      for c and non-empty, split into bf16 hi + lo planes (k-bar and v-bar are
 //      fp32), with logit tau q.kbar_g + ln m_g;
-//   2. exact tiles: the keys of every routed key cluster, gathered by row
-//      index straight from global memory into LDS (buffer loads with the lds
-//      flag), two buffers, the next tile's loads in flight during the current
-//      tile's math.
-// One online softmax (base-2 exponent) covers both kinds of terms.
+//   2. exact tiles: the keys of every routed key cluster.
+// Both kinds are gathered by row index straight from global memory into LDS
+// (buffer loads with the lds flag), two buffers deep, the next tile's loads in
+// flight during the current tile's math.  One online softmax (base-2
+// exponent, lazily raised reference max) covers both kinds of terms.
 //
 // The kernel is persistent (one workgroup per CU) and takes query tiles from
 // eight work queues, one per XCD: tiles are dealt to queue c mod 8 by query
