@@ -144,7 +144,11 @@ __device__ __forceinline__ void km_store(const KmStage& s, char* buf, int tid)
 
 // acc[tb] = (hi + lo rows of a 32-centroid block) x (token block tb)^T; the
 // fragment reads are issued two k-steps ahead of their MFMAs, which bounds the
-// registers they occupy.
+// registers they occupy.  Without LO the lo plane is known to be zero (the
+// first assignment, whose centroids are input tokens and so exact in bf16):
+// its MFMAs would add exact zeros, so skipping them leaves every accumulator
+// bit-identical.
+template <bool LO>
 __device__ __forceinline__ void km_tile(f32x16_t acc[2], const char* rh, const bf16x8_t xf[2][8])
 {
     const char* rl = rh + KM_PLANE;
@@ -152,23 +156,36 @@ __device__ __forceinline__ void km_tile(f32x16_t acc[2], const char* rh, const b
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
         const bf16x8_t ah = as_bf16x8(*(const u32x4_t*)(rh + s * 32));
-        const bf16x8_t al = as_bf16x8(*(const u32x4_t*)(rl + s * 32));
+        bf16x8_t al;
+        if (LO) al = as_bf16x8(*(const u32x4_t*)(rl + s * 32));
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
             acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xf[tb][s], acc[tb], 0, 0, 0);
-            acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xf[tb][s], acc[tb], 0, 0, 0);
+            if (LO) acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xf[tb][s], acc[tb], 0, 0, 0);
         }
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    if (LO) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int s = 0; s < 6; ++s) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        for (int s = 0; s < 6; ++s) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    } else {
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int s = 0; s < 6; ++s) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
 }
 
 // Screen: labels = screen argmin; near-ties appended to flags[h, *] (token ids).
+// LO: whether the centroids' lo plane can be non-zero (km_tile).
+template <bool LO>
 __global__ __launch_bounds__(256, 2) void k_assign_mfma(
     const bf16* __restrict__ X, const bf16* __restrict__ hi, const bf16* __restrict__ lo,
     const float* __restrict__ cn32, const unsigned* __restrict__ stats, int N, int C,
@@ -233,7 +250,7 @@ __global__ __launch_bounds__(256, 2) void k_assign_mfma(
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
             f32x16_t acc[2];
-            km_tile(acc, buf + (cb * 32 + tcol) * KM_PITCH + half * 16, xf);
+            km_tile<LO>(acc, buf + (cb * 32 + tcol) * KM_PITCH + half * 16, xf);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int r = cb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
@@ -381,7 +398,7 @@ __global__ __launch_bounds__(256, 2) void k_assign_partial(
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb) {
                 f32x16_t acc[2];
-                km_tile(acc, buf + (cb * 32 + tcol) * KM_PITCH + half * 16, xf);
+                km_tile<true>(acc, buf + (cb * 32 + tcol) * KM_PITCH + half * 16, xf);
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int r = cb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
@@ -620,10 +637,17 @@ SVG_HIDDEN hipError_t launch_assign_mfma(const ClusterArgs& a, const double* cen
 {
     // With `partial`, both screens are launched and each head runs in the one
     // its moved-centroid count selects (decided on the device).
+    // The first screen (not partial) runs on the initial centroids, input
+    // tokens exact in bf16, whose lo plane is zero.
     const dim3 grid((a.N + KM_TOK - 1) / KM_TOK, a.H);
-    hipLaunchKernelGGL(k_assign_mfma, grid, dim3(256), KM_LDS, st, (const bf16*)a.X, P.hi, P.lo,
-                       P.cn32, P.stats, a.N, a.C, a.labels, P.flags, P.nflag, P.ub_own, P.lb_own,
-                       P.lb_rest, partial ? (const int*)P.mcount : (const int*)nullptr);
+    if (partial)
+        hipLaunchKernelGGL(k_assign_mfma<true>, grid, dim3(256), KM_LDS, st, (const bf16*)a.X, P.hi, P.lo,
+                           P.cn32, P.stats, a.N, a.C, a.labels, P.flags, P.nflag, P.ub_own, P.lb_own,
+                           P.lb_rest, (const int*)P.mcount);
+    else
+        hipLaunchKernelGGL(k_assign_mfma<false>, grid, dim3(256), KM_LDS, st, (const bf16*)a.X, P.hi, P.lo,
+                           P.cn32, P.stats, a.N, a.C, a.labels, P.flags, P.nflag, P.ub_own, P.lb_own,
+                           P.lb_rest, (const int*)nullptr);
     if (partial)
         hipLaunchKernelGGL(k_assign_partial, grid, dim3(256), KM_BUF, st, (const bf16*)a.X, P.hi,
                            P.lo, P.cn32, P.stats, P.mlist, P.mpos, P.mcount, a.N, a.C, a.labels,
