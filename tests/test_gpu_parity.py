@@ -446,3 +446,39 @@ def test_forward_replays_from_a_hip_graph():
         sv.forward(shape, rho, data["Q"], data["K"], data["V"], data["init_q"], data["init_k"], O_ref, ws)
         torch.cuda.synchronize()
         assert torch.equal(O_ref.cpu(), ref)
+
+
+@pytest.mark.parametrize("case", ["ragged", "small"])
+def test_forward_is_deterministic_over_stale_workspace(case):
+    """The same inputs give bit-identical outputs and intermediates, whatever
+    the workspace and the intermediate buffers held before the call: two calls
+    over buffers filled with different random bytes agree exactly (nothing
+    reads memory the call did not write first)."""
+    torch = torch_gpu()
+    w = CASES[case]
+    log("forward determinism %s" % case)
+    data = upload(w)
+    H = len(data["heads"])
+    shape = shape_of(w, H)
+    rho = w.rhos[0]
+    gen = torch.Generator(device="cuda")
+    runs = []
+    for seed in (1, 2):
+        gen.manual_seed(seed)
+        ws = sv.alloc_workspace(shape)
+        ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, device="cuda", generator=gen))
+        im = sv.alloc_intermediates(shape, "cuda")
+        for t in im.values():
+            raw = t.view(torch.uint8)
+            raw.copy_(torch.randint(0, 256, raw.shape, dtype=torch.uint8, device="cuda", generator=gen))
+        O = torch.empty_like(data["Q"])
+        O.view(torch.uint8).copy_(torch.randint(0, 256, O.view(torch.uint8).shape, dtype=torch.uint8,
+                                                device="cuda", generator=gen))
+        sv.forward(shape, rho, data["Q"], data["K"], data["V"], data["init_q"], data["init_k"], O, ws, im)
+        torch.cuda.synchronize()
+        runs.append(({k: v.cpu() for k, v in im.items()}, O.cpu()))
+    (im1, O1), (im2, O2) = runs
+    for k in im1:
+        a, b = im1[k].view(torch.uint8), im2[k].view(torch.uint8)
+        assert torch.equal(a, b), "intermediate %s differs between the two calls" % k
+    assert torch.equal(O1.view(torch.uint8), O2.view(torch.uint8)), "output differs between the two calls"
