@@ -448,7 +448,7 @@ def test_forward_replays_from_a_hip_graph():
         assert torch.equal(O_ref.cpu(), ref)
 
 
-@pytest.mark.parametrize("case", ["ragged", "small"])
+@pytest.mark.parametrize("case", ["tiny", "ragged", "small"])
 def test_forward_is_deterministic_over_stale_workspace(case):
     """The same inputs give bit-identical outputs and intermediates, whatever
     the workspace and the intermediate buffers held before the call: two calls
@@ -482,3 +482,37 @@ def test_forward_is_deterministic_over_stale_workspace(case):
         a, b = im1[k].view(torch.uint8), im2[k].view(torch.uint8)
         assert torch.equal(a, b), "intermediate %s differs between the two calls" % k
     assert torch.equal(O1.view(torch.uint8), O2.view(torch.uint8)), "output differs between the two calls"
+
+
+def test_forward_on_two_streams_at_once():
+    """Two svgear_forward calls with their own workspaces, enqueued back to back
+    on two streams without a synchronisation in between (both share the
+    library's side stream for the Q clustering): each equals the same call
+    made alone."""
+    torch = torch_gpu()
+    wa, wb = CASES["small"], CASES["ragged"]
+    log("forward on two streams")
+    runs = []
+    for w in (wa, wb):
+        data = upload(w)
+        H = len(data["heads"])
+        shape = shape_of(w, H)
+        runs.append((w, data, shape, sv.alloc_workspace(shape)))
+    alone = []
+    for w, data, shape, ws in runs:
+        O = torch.empty_like(data["Q"])
+        sv.forward(shape, w.rhos[0], data["Q"], data["K"], data["V"], data["init_q"], data["init_k"], O, ws)
+        torch.cuda.synchronize()
+        alone.append(O.cpu())
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for (w, data, shape, ws), st in zip(runs, streams):
+        O = torch.empty_like(data["Q"])
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            sv.forward(shape, w.rhos[0], data["Q"], data["K"], data["V"], data["init_q"], data["init_k"], O, ws,
+                       stream=st)
+        outs.append(O)
+    torch.cuda.synchronize()
+    for ref, O in zip(alone, outs):
+        assert torch.equal(O.cpu(), ref), "a call made beside another differs from the call made alone"
