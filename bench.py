@@ -411,8 +411,8 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}), flush=True)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (heads shard across GPUs "
-              "without communication; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (heads would shard across "
+              "GPUs without communication). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

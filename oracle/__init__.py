@@ -9,7 +9,7 @@ It shares no code with the HIP library: it loads its own C library,
 The arithmetic lives in the C file; this module only marshals numpy arrays.
 ``forward_head`` composes the five steps of the pipeline paragraph of the
 SVG-EAR review page (cluster and reorder, probe, ratio, greedy route, hybrid
-output) for one head.  Parity status of each step is stated in the design notes:
+output) for one head.  Parity status of each step:
 k-means, permutation, means, route and the hybrid output are pinned by tests
 against library routines, closed forms and brute force; the probe on generic data
 is pinned only through its special cases and a brute-force block sum.

@@ -20,7 +20,7 @@
  * values (bf16 or fp32) promoted to fp64.  Row-major layouts throughout:
  * X[i*d + t], centroids cent[m*d + t], block arrays [c*Ck + g].
  *
- * Readings of points the pages leave open (each listed in the design notes):
+ * Readings of points the pages leave open:
  *   k-means: squared Euclidean distance, fixed iteration count, initial
  *   centroids are given token rows, argmin ties go to the lowest cluster
  *   index, an empty cluster keeps its previous centroid, the returned labels
