@@ -128,7 +128,7 @@ static SideStream* side_stream()
         if (hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking) != hipSuccess) return nullptr;
         if (hipEventCreateWithFlags(&s.fork, hipEventDisableTiming) != hipSuccess ||
             hipEventCreateWithFlags(&s.join, hipEventDisableTiming) != hipSuccess) {
-            hipStreamDestroy(s.stream);
+            (void)hipStreamDestroy(s.stream);
             return nullptr;
         }
         g_ready[dev] = true;

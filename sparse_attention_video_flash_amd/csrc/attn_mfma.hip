@@ -191,7 +191,7 @@ __global__ __launch_bounds__(1024) void k_tile_prefix(const int32_t* __restrict_
     s_part[threadIdx.x] = local;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {
-        int v = threadIdx.x >= off ? s_part[threadIdx.x - off] : 0;
+        int v = (int)threadIdx.x >= off ? s_part[threadIdx.x - off] : 0;
         __syncthreads();
         s_part[threadIdx.x] += v;
         __syncthreads();
@@ -793,9 +793,10 @@ SVG_HIDDEN hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t st)
                        tiles_per_head, qmeta, qlist);
     zero_words(qmeta + 2 * AT_XCD, AT_XCD * 4, st);
     // persistent: one workgroup per CU (two waves per SIMD, the occupancy the register use allows)
-    int dev = 0, ncu = 256;
-    if (hipGetDevice(&dev) == hipSuccess)
-        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        ncu = 0;
     const int nwg = ncu > 0 ? ncu : 256;   // one 8-wave workgroup per CU (two waves per SIMD)
     const float scale2 = (float)(1.4426950408889634 / sqrt((double)AT_D));
     hipLaunchKernelGGL(k_attn_mfma, dim3(nwg), dim3(AT_THREADS), AT_LDS, st,

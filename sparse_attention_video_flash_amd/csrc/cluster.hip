@@ -167,7 +167,7 @@ __global__ __launch_bounds__(1024) void k_count_scan(const int32_t* __restrict__
     s_part[threadIdx.x] = local;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {
-        int v = threadIdx.x >= off ? s_part[threadIdx.x - off] : 0;
+        int v = (int)threadIdx.x >= off ? s_part[threadIdx.x - off] : 0;
         __syncthreads();
         s_part[threadIdx.x] += v;
         __syncthreads();
@@ -401,7 +401,7 @@ __global__ __launch_bounds__(1024) void k_moved_list(int C, int* __restrict__ ch
         s_part[threadIdx.x] = f;
         __syncthreads();
         for (int off = 1; off < 1024; off <<= 1) {
-            const int v = threadIdx.x >= off ? s_part[threadIdx.x - off] : 0;
+            const int v = (int)threadIdx.x >= off ? s_part[threadIdx.x - off] : 0;
             __syncthreads();
             s_part[threadIdx.x] += v;
             __syncthreads();

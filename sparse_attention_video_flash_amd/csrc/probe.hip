@@ -194,7 +194,7 @@ __global__ __launch_bounds__(256) void k_probe_generic(
             __syncthreads();
             for (int k = threadIdx.x; k < kn * D; k += 256)
                 s_k[k / D][k % D] = kb[k % D] - to_f32<T>(Kp[((size_t)h * Nk + jb) * D + k]);
-            if (threadIdx.x < kn) s_ks[threadIdx.x] = keys[(size_t)h * Nk + jb + threadIdx.x];
+            if ((int)threadIdx.x < kn) s_ks[threadIdx.x] = keys[(size_t)h * Nk + jb + threadIdx.x];
             __syncthreads();
             if (!act) continue;
             for (int jj = 0; jj < kn; ++jj) {

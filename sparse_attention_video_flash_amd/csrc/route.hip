@@ -143,7 +143,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(const float* __restrict
             s_scan[threadIdx.x] = w;
             __syncthreads();
             for (int off = 1; off < kRouteThreads; off <<= 1) {
-                long long v = threadIdx.x >= off ? s_scan[threadIdx.x - off] : 0;
+                long long v = (int)threadIdx.x >= off ? s_scan[threadIdx.x - off] : 0;
                 __syncthreads();
                 s_scan[threadIdx.x] += v;
                 __syncthreads();
