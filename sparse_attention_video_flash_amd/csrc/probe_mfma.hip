@@ -61,8 +61,11 @@ __device__ __forceinline__ void split8(const float x[8], u32x4_t& hi, u32x4_t& l
     lo = __builtin_bit_cast(u32x4_t, l);
 }
 
+// Up to two column blocks per wave (C_q <= 128) the kernel fits three waves per
+// SIMD (at most 168 VGPRs) without spilling in its production form; more
+// blocks keep their registers and run at the occupancy they allow.
 template <int NCBW, bool EPS>
-__global__ __launch_bounds__(256) void k_probe_mfma(
+__global__ __launch_bounds__(256, (NCBW <= 2 ? 3 : 1)) void k_probe_mfma(
     const float* __restrict__ qbar, const int32_t* __restrict__ counts_q, const bf16* __restrict__ Kp,
     const float* __restrict__ kbar, const float* __restrict__ sbar, const float2* __restrict__ keys,
     const float* __restrict__ pg, const int32_t* __restrict__ offsets_k, int Nk, int Cq, int Ck,
