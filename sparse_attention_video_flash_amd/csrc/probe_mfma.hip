@@ -237,7 +237,9 @@ SVG_HIDDEN hipError_t launch_probe_mfma(const ProbeArgs& a, const float* sbar, c
                                         const float* pg, hipStream_t st)
 {
     const int ncbw = ((a.Cq + 15) / 16 + 3) / 4;   // column blocks per wave
-    int gx = (1024 + a.H - 1) / a.H;
+    // about 1536 workgroups in all: two rounds of three per CU (measured best of
+    // 768 to 2304 at the Wan and HunyuanVideo shapes)
+    int gx = (1536 + a.H - 1) / a.H;
     if (gx > a.Ck) gx = a.Ck;
     float* eps = (a.flags & SVGEAR_DEBUG_EPS) ? a.log_eps2 : nullptr;
     const float tau = 1.0f / sqrtf((float)PR_D);
