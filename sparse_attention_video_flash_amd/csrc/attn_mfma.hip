@@ -168,11 +168,13 @@ __global__ __launch_bounds__(256) void k_seg_list(const uint8_t* __restrict__ ma
         ncomp[(size_t)h * Cq + c] = cbase;
         nkeys[(size_t)h * Cq + c] = keys;
     }
-    // Row map: list position -> reordered key row, segment after segment
+    // Row map: list position -> reordered key row; wave w writes segments
+    // w, w + 4, ...
     int* rm = rowmap + ((size_t)h * Cq + c) * Nk;
-    for (int si = 0; si < base; ++si) {
+    const int wv = tid >> 6, ln = tid & 63;
+    for (int si = wv; si < base; si += 4) {
         const int r0 = s_start[si], p0 = s_pref[si], len = s_pref[si + 1] - p0;
-        for (int k = tid; k < len; k += 256) rm[p0 + k] = r0 + k;
+        for (int k = ln; k < len; k += 64) rm[p0 + k] = r0 + k;
     }
 }
 
