@@ -119,35 +119,48 @@ __global__ __launch_bounds__(256) void k_tile_hist(const int32_t* __restrict__ l
 }
 
 // Per-label exclusive prefix of the tile counts, in place, and the label
-// counts.  One block per 32 labels of a head; tiles are staged through LDS 64 at
-// a time so the loads of a chunk are issued together.
-constexpr int HC_L = 32, HC_T = 64;
+// counts.  One block per 32 labels of a head, 64 tiles per pass: thread
+// (group g, label) holds tiles 8 g .. 8 g + 7 of its label in registers, the
+// eight group sums are scanned through LDS, and each thread writes its tiles'
+// prefixes (a two-level scan, eight dependent steps instead of 64).
+constexpr int HC_L = 32, HC_G = 256 / HC_L, HC_R = 8, HC_T = HC_G * HC_R;
 __global__ __launch_bounds__(256) void k_hist_cols(int* __restrict__ hist, int C, int ntiles,
                                                    int32_t* __restrict__ counts)
 {
-    __shared__ int s_t[HC_T][HC_L + 1];
+    __shared__ int s_g[HC_G][HC_L];
     const int h = blockIdx.y, l0 = blockIdx.x * HC_L;
-    const int lab = threadIdx.x & (HC_L - 1), tr = threadIdx.x / HC_L;  // 8 tile rows per pass
-    int* hb = hist + (size_t)h * ntiles * C;
+    const int lab = threadIdx.x & (HC_L - 1), g = threadIdx.x / HC_L;
+    const bool lv = l0 + lab < C;
+    int* hb = hist + (size_t)h * ntiles * C + (lv ? l0 + lab : 0);
     int run = 0;
     for (int t0 = 0; t0 < ntiles; t0 += HC_T) {
-        const int tn = min(HC_T, ntiles - t0);
-        for (int t = tr; t < tn; t += 256 / HC_L)
-            s_t[t][lab] = (l0 + lab < C) ? hb[(size_t)(t0 + t) * C + l0 + lab] : 0;
-        __syncthreads();
-        if (threadIdx.x < HC_L) {
-            for (int t = 0; t < tn; ++t) {
-                const int v = s_t[t][lab];
-                s_t[t][lab] = run;
-                run += v;
-            }
+        int v[HC_R];
+        int local = 0;
+#pragma unroll
+        for (int k = 0; k < HC_R; ++k) {
+            const int t = t0 + g * HC_R + k;
+            v[k] = (lv && t < ntiles) ? hb[(size_t)t * C] : 0;
+            local += v[k];
         }
+        s_g[g][lab] = local;
         __syncthreads();
-        for (int t = tr; t < tn; t += 256 / HC_L)
-            if (l0 + lab < C) hb[(size_t)(t0 + t) * C + l0 + lab] = s_t[t][lab];
-        __syncthreads();
+        int pre = run, tot = 0;
+#pragma unroll
+        for (int q = 0; q < HC_G; ++q) {
+            const int x = s_g[q][lab];
+            pre += q < g ? x : 0;
+            tot += x;
+        }
+#pragma unroll
+        for (int k = 0; k < HC_R; ++k) {
+            const int t = t0 + g * HC_R + k;
+            if (lv && t < ntiles) hb[(size_t)t * C] = pre;
+            pre += v[k];
+        }
+        run += tot;
+        __syncthreads();   // s_g is rewritten by the next pass
     }
-    if (threadIdx.x < HC_L && l0 + lab < C) counts[(size_t)h * C + l0 + lab] = run;
+    if (g == 0 && lv) counts[(size_t)h * C + l0 + lab] = run;
 }
 
 // Per head: cluster offsets = exclusive prefix of the counts.  Also clears the
