@@ -47,8 +47,8 @@ __global__ __launch_bounds__(256) void k_key_scalars(const T* __restrict__ Vp,
     for (int o = 8; o >= 1; o >>= 1) p += __shfl_xor(p, o, 16);
     if (threadIdx.x == 0) pg[(size_t)h * Ck + g] = p;
     const int j0 = offsets_k[(size_t)h * (Ck + 1) + g], j1 = offsets_k[(size_t)h * (Ck + 1) + g + 1];
-    // four rows per pass, their loads issued together
-    constexpr int RU = 4;
+    // eight rows per pass, their loads issued together
+    constexpr int RU = 8;
     for (int jb = j0; jb < j1; jb += 16 * RU) {
         T vv[RU][EPT];
 #pragma unroll
