@@ -37,12 +37,30 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int KM_D = 128;
-constexpr int KM_CB = 64;                       // centroids per LDS chunk
 constexpr int KM_PITCH = KM_D * 2 + 16;         // bytes per centroid row of a plane
-constexpr int KM_PLANE = KM_CB * KM_PITCH;      // 17408
-constexpr int KM_BUF = 2 * KM_PLANE + KM_CB * 4;  // hi, lo, ||c||^2
-constexpr int KM_LDS = 2 * KM_BUF;
 constexpr int KM_TOK = 256;                     // tokens per workgroup (4 waves x 64)
+
+// A chunk of CB centroids staged in LDS: the hi plane, with LO the lo plane
+// after it, then ||c||^2 (fp32) per centroid.  NV: 16-byte vectors per thread.
+template <int CB, bool LO>
+struct KmChunk {
+    static constexpr int PLANE = CB * KM_PITCH;
+    static constexpr int NPL = LO ? 2 : 1;
+    static constexpr int BYTES = NPL * PLANE + CB * 4;
+    static constexpr int NV = NPL * CB / 16;
+};
+// The full screens stage 32 centroids per chunk, double-buffered (35 KB of LDS
+// with both planes): with at most 168 VGPRs, three workgroups (12 waves) share a
+// CU and hide each other's token loads.
+template <bool LO>
+struct KmScreen {
+    static constexpr int CB = 32;
+    using Chunk = KmChunk<CB, LO>;
+    static constexpr int LDS = 2 * Chunk::BYTES;
+};
+// The partial screen: 32 moved centroids, both planes, single-buffered (three
+// workgroups per CU as well; the 168-VGPR limit spills a few prologue values).
+using KmPartialChunk = KmChunk<32, true>;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
@@ -111,35 +129,41 @@ __global__ __launch_bounds__(KM_D) void k_km_prep(const double* __restrict__ cen
     }
 }
 
+// One thread's share of a chunk in registers: hi rows r, r + 16, ... (r = tid / 16,
+// 16-byte column tid & 15), then the same lo rows; ||c||^2 of centroid tid.
+template <int NV>
 struct KmStage {
-    u32x4_t v[8];  // hi rows r, r + 16, r + 32, r + 48 then lo rows, chunk tid & 15
+    u32x4_t v[NV];
     float cn;
 };
 
-__device__ __forceinline__ void km_load(KmStage& s, const bf16* __restrict__ hi,
+template <int CB, bool LO>
+__device__ __forceinline__ void km_load(KmStage<KmChunk<CB, LO>::NV>& s, const bf16* __restrict__ hi,
                                         const bf16* __restrict__ lo, const float* __restrict__ cn,
                                         int m0, int C, int tid)
 {
     const int ch = tid & 15, r = tid >> 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < CB / 16; ++i) {
         const int m = m0 + r + 16 * i;
         const bool ok = m < C;
         s.v[i] = ok ? *(const u32x4_t*)(hi + (size_t)m * KM_D + ch * 8) : u32x4_t{0, 0, 0, 0};
-        s.v[4 + i] = ok ? *(const u32x4_t*)(lo + (size_t)m * KM_D + ch * 8) : u32x4_t{0, 0, 0, 0};
+        if (LO) s.v[CB / 16 + i] = ok ? *(const u32x4_t*)(lo + (size_t)m * KM_D + ch * 8) : u32x4_t{0, 0, 0, 0};
     }
-    s.cn = (tid < KM_CB && m0 + tid < C) ? cn[m0 + tid] : __builtin_inff();
+    s.cn = (tid < CB && m0 + tid < C) ? cn[m0 + tid] : __builtin_inff();
 }
 
-__device__ __forceinline__ void km_store(const KmStage& s, char* buf, int tid)
+template <int CB, bool LO>
+__device__ __forceinline__ void km_store(const KmStage<KmChunk<CB, LO>::NV>& s, char* buf, int tid)
 {
+    using K = KmChunk<CB, LO>;
     const int ch = tid & 15, r = tid >> 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < CB / 16; ++i) {
         *(u32x4_t*)(buf + (r + 16 * i) * KM_PITCH + ch * 16) = s.v[i];
-        *(u32x4_t*)(buf + KM_PLANE + (r + 16 * i) * KM_PITCH + ch * 16) = s.v[4 + i];
+        if (LO) *(u32x4_t*)(buf + K::PLANE + (r + 16 * i) * KM_PITCH + ch * 16) = s.v[CB / 16 + i];
     }
-    if (tid < KM_CB) ((float*)(buf + 2 * KM_PLANE))[tid] = s.cn;
+    if (tid < CB) ((float*)(buf + K::NPL * K::PLANE))[tid] = s.cn;
 }
 
 // acc[tb] = (hi + lo rows of a 32-centroid block) x (token block tb)^T; the
@@ -148,10 +172,10 @@ __device__ __forceinline__ void km_store(const KmStage& s, char* buf, int tid)
 // first assignment, whose centroids are input tokens and so exact in bf16):
 // its MFMAs would add exact zeros, so skipping them leaves every accumulator
 // bit-identical.
-template <bool LO>
+template <bool LO, int PLANE>
 __device__ __forceinline__ void km_tile(f32x16_t acc[2], const char* rh, const bf16x8_t xf[2][8])
 {
-    const char* rl = rh + KM_PLANE;
+    const char* rl = rh + PLANE;
     acc[0] = acc[1] = f32x16_t{0};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -186,7 +210,7 @@ __device__ __forceinline__ void km_tile(f32x16_t acc[2], const char* rh, const b
 // Screen: labels = screen argmin; near-ties appended to flags[h, *] (token ids).
 // LO: whether the centroids' lo plane can be non-zero (km_tile).
 template <bool LO>
-__global__ __launch_bounds__(256, 2) void k_assign_mfma(
+__global__ __launch_bounds__(256, 3) void k_assign_mfma(
     const bf16* __restrict__ X, const bf16* __restrict__ hi, const bf16* __restrict__ lo,
     const float* __restrict__ cn32, const unsigned* __restrict__ stats, int N, int C,
     int32_t* __restrict__ labels, int32_t* __restrict__ flags, int* __restrict__ nflag,
@@ -237,25 +261,27 @@ __global__ __launch_bounds__(256, 2) void k_assign_mfma(
         i1[tb] = 0;
     }
 
-    const int nchunk = (C + KM_CB - 1) / KM_CB;
-    KmStage stg;
-    km_load(stg, hih, loh, cnh, 0, C, tid);
-    km_store(stg, smem, tid);
+    constexpr int CB = KmScreen<LO>::CB;
+    using K = typename KmScreen<LO>::Chunk;
+    const int nchunk = (C + CB - 1) / CB;
+    KmStage<K::NV> stg;
+    km_load<CB, LO>(stg, hih, loh, cnh, 0, C, tid);
+    km_store<CB, LO>(stg, smem, tid);
     __syncthreads();
     for (int k = 0; k < nchunk; ++k) {
-        char* buf = smem + (k & 1) * KM_BUF;
+        char* buf = smem + (k & 1) * K::BYTES;
         const bool more = k + 1 < nchunk;
-        if (more) km_load(stg, hih, loh, cnh, (k + 1) * KM_CB, C, tid);
-        const float* s_cn = (const float*)(buf + 2 * KM_PLANE);
+        if (more) km_load<CB, LO>(stg, hih, loh, cnh, (k + 1) * CB, C, tid);
+        const float* s_cn = (const float*)(buf + K::NPL * K::PLANE);
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
+        for (int cb = 0; cb < CB / 32; ++cb) {
             f32x16_t acc[2];
-            km_tile<LO>(acc, buf + (cb * 32 + tcol) * KM_PITCH + half * 16, xf);
+            km_tile<LO, K::PLANE>(acc, buf + (cb * 32 + tcol) * KM_PITCH + half * 16, xf);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int r = cb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
                 const float cnv = s_cn[r];  // +inf past the last centroid
-                const int m = k * KM_CB + r;
+                const int m = k * CB + r;
 #pragma unroll
                 for (int tb = 0; tb < 2; ++tb) {
                     const float d = fmaf(-2.f, acc[tb][i], cnv);
@@ -267,7 +293,7 @@ __global__ __launch_bounds__(256, 2) void k_assign_mfma(
             }
         }
         if (more) {
-            km_store(stg, smem + ((k + 1) & 1) * KM_BUF, tid);
+            km_store<CB, LO>(stg, smem + ((k + 1) & 1) * K::BYTES, tid);
             __syncthreads();
         }
     }
@@ -301,28 +327,29 @@ __global__ __launch_bounds__(256, 2) void k_assign_mfma(
 
 // The moved centroids (list mlist[h, 0 .. mcount)) staged like km_load; rows
 // past the list get ||c||^2 = +inf.
-__device__ __forceinline__ void km_load_list(KmStage& s, const bf16* __restrict__ hi,
-                                             const bf16* __restrict__ lo,
+template <int CB>
+__device__ __forceinline__ void km_load_list(KmStage<KmChunk<CB, true>::NV>& s,
+                                             const bf16* __restrict__ hi, const bf16* __restrict__ lo,
                                              const float* __restrict__ cn,
                                              const int* __restrict__ ml, int k0, int cnt, int tid)
 {
     const int ch = tid & 15, r = tid >> 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < CB / 16; ++i) {
         const int k = k0 + r + 16 * i;
         const bool ok = k < cnt;
         const int m = ok ? ml[k] : 0;
         s.v[i] = ok ? *(const u32x4_t*)(hi + (size_t)m * KM_D + ch * 8) : u32x4_t{0, 0, 0, 0};
-        s.v[4 + i] = ok ? *(const u32x4_t*)(lo + (size_t)m * KM_D + ch * 8) : u32x4_t{0, 0, 0, 0};
+        s.v[CB / 16 + i] = ok ? *(const u32x4_t*)(lo + (size_t)m * KM_D + ch * 8) : u32x4_t{0, 0, 0, 0};
     }
-    const bool okc = tid < KM_CB && k0 + tid < cnt;
+    const bool okc = tid < CB && k0 + tid < cnt;
     s.cn = okc ? cn[ml[k0 + tid]] : __builtin_inff();
 }
 
 // Iterations after the first: screen against the moved centroids only and
 // decide from the stored bounds (file comment); undecided tokens are queued for
 // the exact recheck.
-__global__ __launch_bounds__(256, 2) void k_assign_partial(
+__global__ __launch_bounds__(256, 3) void k_assign_partial(
     const bf16* __restrict__ X, const bf16* __restrict__ hi, const bf16* __restrict__ lo,
     const float* __restrict__ cn32, const unsigned* __restrict__ stats, const int* __restrict__ mlist,
     const int* __restrict__ mpos, const int* __restrict__ mcount, int N, int C,
@@ -382,28 +409,30 @@ __global__ __launch_bounds__(256, 2) void k_assign_partial(
     }
 
     // Single-buffered chunks (the moved list is short after the first few
-    // iterations; this keeps the kernel within 256 VGPRs).
-    const int nchunk = (cnt + KM_CB - 1) / KM_CB;
+    // iterations; it keeps the registers within the three-workgroup limit).
+    using K = KmPartialChunk;
+    constexpr int CB = 32;
+    const int nchunk = (cnt + CB - 1) / CB;
     for (int k = 0; k < nchunk; ++k) {
         char* const buf = smem;
         {
-            KmStage stg;
-            km_load_list(stg, hih, loh, cnh, ml, k * KM_CB, cnt, tid);
+            KmStage<K::NV> stg;
+            km_load_list<CB>(stg, hih, loh, cnh, ml, k * CB, cnt, tid);
             __syncthreads();   // the previous chunk's readers are done
-            km_store(stg, buf, tid);
+            km_store<CB, true>(stg, buf, tid);
             __syncthreads();
         }
         {
-            const float* s_cn = (const float*)(buf + 2 * KM_PLANE);
+            const float* s_cn = (const float*)(buf + K::NPL * K::PLANE);
 #pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
+            for (int cb = 0; cb < CB / 32; ++cb) {
                 f32x16_t acc[2];
-                km_tile<true>(acc, buf + (cb * 32 + tcol) * KM_PITCH + half * 16, xf);
+                km_tile<true, K::PLANE>(acc, buf + (cb * 32 + tcol) * KM_PITCH + half * 16, xf);
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int r = cb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
                     const float cnv = s_cn[r];  // +inf past the list
-                    const int m = k * KM_CB + r;   // list position
+                    const int m = k * CB + r;   // list position
 #pragma unroll
                     for (int tb = 0; tb < 2; ++tb) {
                         const float d = fmaf(-2.f, acc[tb][i], cnv);
@@ -641,15 +670,15 @@ SVG_HIDDEN hipError_t launch_assign_mfma(const ClusterArgs& a, const double* cen
     // tokens exact in bf16, whose lo plane is zero.
     const dim3 grid((a.N + KM_TOK - 1) / KM_TOK, a.H);
     if (partial)
-        hipLaunchKernelGGL(k_assign_mfma<true>, grid, dim3(256), KM_LDS, st, (const bf16*)a.X, P.hi, P.lo,
+        hipLaunchKernelGGL(k_assign_mfma<true>, grid, dim3(256), KmScreen<true>::LDS, st, (const bf16*)a.X, P.hi, P.lo,
                            P.cn32, P.stats, a.N, a.C, a.labels, P.flags, P.nflag, P.ub_own, P.lb_own,
                            P.lb_rest, (const int*)P.mcount);
     else
-        hipLaunchKernelGGL(k_assign_mfma<false>, grid, dim3(256), KM_LDS, st, (const bf16*)a.X, P.hi, P.lo,
+        hipLaunchKernelGGL(k_assign_mfma<false>, grid, dim3(256), KmScreen<false>::LDS, st, (const bf16*)a.X, P.hi, P.lo,
                            P.cn32, P.stats, a.N, a.C, a.labels, P.flags, P.nflag, P.ub_own, P.lb_own,
                            P.lb_rest, (const int*)nullptr);
     if (partial)
-        hipLaunchKernelGGL(k_assign_partial, grid, dim3(256), KM_BUF, st, (const bf16*)a.X, P.hi,
+        hipLaunchKernelGGL(k_assign_partial, grid, dim3(256), KmPartialChunk::BYTES, st, (const bf16*)a.X, P.hi,
                            P.lo, P.cn32, P.stats, P.mlist, P.mpos, P.mcount, a.N, a.C, a.labels,
                            P.flags, P.nflag, P.ub_own, P.lb_own, P.lb_rest);
     hipLaunchKernelGGL(k_recheck, dim3(256, a.H), dim3(256), 0, st, (const bf16*)a.X, cent64, P.cn64,
