@@ -61,11 +61,13 @@ __device__ __forceinline__ void split8(const float x[8], u32x4_t& hi, u32x4_t& l
     lo = __builtin_bit_cast(u32x4_t, l);
 }
 
-// Up to two column blocks per wave (C_q <= 128) the kernel fits three waves per
-// SIMD (at most 168 VGPRs) without spilling in its production form; more
-// blocks keep their registers and run at the occupancy they allow.
+// Up to two column blocks per wave the kernel fits three waves per SIMD (at
+// most 168 VGPRs) without spilling in its production form.  A workgroup covers
+// a slice of 4 NCBW column blocks (blockIdx.z); with more query clusters than
+// one slice holds, the slices are separate workgroups over the same keys, so
+// each keeps that occupancy (the key-side staging is repeated per slice).
 template <int NCBW, bool EPS>
-__global__ __launch_bounds__(256, (NCBW <= 2 ? 3 : 1)) void k_probe_mfma(
+__global__ __launch_bounds__(256, 3) void k_probe_mfma(
     const float* __restrict__ qbar, const int32_t* __restrict__ counts_q, const bf16* __restrict__ Kp,
     const float* __restrict__ kbar, const float* __restrict__ sbar, const float2* __restrict__ keys,
     const float* __restrict__ pg, const int32_t* __restrict__ offsets_k, int Nk, int Cq, int Ck,
@@ -79,13 +81,15 @@ __global__ __launch_bounds__(256, (NCBW <= 2 ? 3 : 1)) void k_probe_mfma(
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int col = lane & 15, grp = lane >> 4;   // A row / D column, and row group
     const int ncb = (Cq + 15) / 16;
+    const int cbw = blockIdx.z * 4 * NCBW + wave;   // this wave's first column block
+    const int c_lo = blockIdx.z * 4 * NCBW * 16, c_hi = min(Cq, c_lo + 4 * NCBW * 16);
 
     // B fragments of this wave's column blocks: centroid cb*16 + col, dims
     // 32 ks + 8 grp + 0..7, split into bf16 hi and lo.
     bf16x8_t bh[NCBW][4], bl[NCBW][4];
 #pragma unroll
     for (int i = 0; i < NCBW; ++i) {
-        const int c = (wave + 4 * i) * 16 + col;
+        const int c = (cbw + 4 * i) * 16 + col;
         const bool cv = c < Cq;
         const float* qp = qbar + ((size_t)h * Cq + (cv ? c : 0)) * PR_D + 8 * grp;
 #pragma unroll
@@ -106,7 +110,7 @@ __global__ __launch_bounds__(256, (NCBW <= 2 ? 3 : 1)) void k_probe_mfma(
         const int j0 = ok[g], j1 = ok[g + 1];
         const int mg = j1 - j0;
         if (mg == 0) {
-            for (int c = tid; c < Cq; c += 256) log_ratio[((size_t)h * Cq + c) * Ck + g] = -__builtin_inff();
+            for (int c = c_lo + tid; c < c_hi; c += 256) log_ratio[((size_t)h * Cq + c) * Ck + g] = -__builtin_inff();
             continue;
         }
         float kb8[8];
@@ -119,7 +123,7 @@ __global__ __launch_bounds__(256, (NCBW <= 2 ? 3 : 1)) void k_probe_mfma(
         float sb[NCBW], sh[NCBW], S[NCBW];
 #pragma unroll
         for (int i = 0; i < NCBW; ++i) {
-            const int c = (wave + 4 * i) * 16 + col;
+            const int c = (cbw + 4 * i) * 16 + col;
             sb[i] = c < Cq ? sbar[((size_t)h * Cq + c) * Ck + g] : 0.f;
             sh[i] = 0.f;
             S[i] = 0.f;
@@ -161,7 +165,7 @@ __global__ __launch_bounds__(256, (NCBW <= 2 ? 3 : 1)) void k_probe_mfma(
                 for (int r = 0; r < 4; ++r) kq[r] = s_ks[kr0 + r];
 #pragma unroll
                 for (int i = 0; i < NCBW; ++i) {
-                    if (wave + 4 * i >= ncb) continue;   // wave-uniform
+                    if (cbw + 4 * i >= ncb) continue;   // wave-uniform
                     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int ks = 0; ks < 4; ++ks) {
@@ -195,7 +199,7 @@ __global__ __launch_bounds__(256, (NCBW <= 2 ? 3 : 1)) void k_probe_mfma(
 #pragma unroll
                     for (int r = 0; r < 4; ++r) S[i] = fmaf(f[r], __builtin_amdgcn_exp2f(u[r] - sh[i]), S[i]);
                     if (EPS) {
-                        const int c = (wave + 4 * i) * 16 + col;
+                        const int c = (cbw + 4 * i) * 16 + col;
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
                             if (c < Cq && kr0 + r < nv)
@@ -208,7 +212,7 @@ __global__ __launch_bounds__(256, (NCBW <= 2 ? 3 : 1)) void k_probe_mfma(
         // combine the four row groups (lanes col, col + 16, col + 32, col + 48)
 #pragma unroll
         for (int i = 0; i < NCBW; ++i) {
-            if (wave + 4 * i >= ncb) continue;
+            if (cbw + 4 * i >= ncb) continue;
             float m = sh[i], s = S[i];
 #pragma unroll
             for (int o = 16; o <= 32; o <<= 1) {
@@ -217,7 +221,7 @@ __global__ __launch_bounds__(256, (NCBW <= 2 ? 3 : 1)) void k_probe_mfma(
                 s = s * __builtin_amdgcn_exp2f(m - mn) + os * __builtin_amdgcn_exp2f(om - mn);
                 m = mn;
             }
-            const int c = (wave + 4 * i) * 16 + col;
+            const int c = (cbw + 4 * i) * 16 + col;
             if (grp == 0 && c < Cq) {
                 float lr = -__builtin_inff();
                 if (counts_q[(size_t)h * Cq + c] > 0 && s > 0.f)
@@ -236,26 +240,28 @@ SVG_HIDDEN bool probe_mfma_supported(const ProbeArgs& a)
 SVG_HIDDEN hipError_t launch_probe_mfma(const ProbeArgs& a, const float* sbar, const float2* keys,
                                         const float* pg, hipStream_t st)
 {
-    const int ncbw = ((a.Cq + 15) / 16 + 3) / 4;   // column blocks per wave
+    const int ncb = (a.Cq + 15) / 16;
+    const int ncbw = ncb > 4 ? 2 : 1;                  // column blocks per wave
+    const int slices = (ncb + 4 * ncbw - 1) / (4 * ncbw);
     // about 1536 workgroups in all: two rounds of three per CU (measured best of
     // 768 to 2304 at the Wan and HunyuanVideo shapes)
-    int gx = (1536 + a.H - 1) / a.H;
+    int gx = (1536 + a.H * slices - 1) / (a.H * slices);
     if (gx > a.Ck) gx = a.Ck;
     float* eps = (a.flags & SVGEAR_DEBUG_EPS) ? a.log_eps2 : nullptr;
     const float tau = 1.0f / sqrtf((float)PR_D);
 #define SVG_PROBE_CASE(n)                                                                          \
     case n:                                                                                        \
         if (eps)                                                                                   \
-            hipLaunchKernelGGL((k_probe_mfma<n, true>), dim3(gx, a.H), dim3(256), PR_LDS, st,      \
+            hipLaunchKernelGGL((k_probe_mfma<n, true>), dim3(gx, a.H, slices), dim3(256), PR_LDS, st, \
                                a.qbar, a.counts_q, (const bf16*)a.Kp, a.kbar, sbar, keys, pg,      \
                                a.offsets_k, a.Nk, a.Cq, a.Ck, tau, a.log_ratio, eps);              \
         else                                                                                       \
-            hipLaunchKernelGGL((k_probe_mfma<n, false>), dim3(gx, a.H), dim3(256), PR_LDS, st,     \
+            hipLaunchKernelGGL((k_probe_mfma<n, false>), dim3(gx, a.H, slices), dim3(256), PR_LDS, st, \
                                a.qbar, a.counts_q, (const bf16*)a.Kp, a.kbar, sbar, keys, pg,      \
                                a.offsets_k, a.Nk, a.Cq, a.Ck, tau, a.log_ratio, eps);              \
         break;
     switch (ncbw) {
-        SVG_PROBE_CASE(1) SVG_PROBE_CASE(2) SVG_PROBE_CASE(3) SVG_PROBE_CASE(4)
+        SVG_PROBE_CASE(1) SVG_PROBE_CASE(2)
     default: return hipErrorInvalidValue;
     }
 #undef SVG_PROBE_CASE

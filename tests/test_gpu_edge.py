@@ -111,6 +111,17 @@ def test_forward_many_query_clusters_uses_generic_probe():
     _check(w, 2400, 1380, 0.3, out, O, host, iters=3)
 
 
+@pytest.mark.parametrize("Cq", [129, 256])
+def test_forward_query_clusters_over_two_probe_slices(Cq):
+    """129 to 256 query clusters: the MFMA probe covers its column blocks in two
+    workgroup slices over the same key clusters (the second slice holds one
+    block at Cq = 129 and eight at 256, the largest MFMA probe)."""
+    w = _workload("bf16", 128, Cq, 64)
+    log("two probe slices: Cq=%d" % Cq)
+    out, O, host = _run(w, 2400, 1380, 0.3, iters=3)
+    _check(w, 2400, 1380, 0.3, out, O, host, iters=3)
+
+
 def test_forward_single_query_cluster():
     """Cq = 1: every query tile of a head belongs to one cluster, so one work
     queue of the attention kernel holds them all and the other queues' workgroups
