@@ -33,8 +33,16 @@
  *   faults surface as SVGEAR_E_HIP from a later synchronising call.
  * - Results are deterministic: identical inputs give bitwise identical outputs
  *   (integer atomics only; no floating-point atomics).
- * - Input values must be finite with |x| < 256 (the exact fixed-point centroid
- *   sums rely on it).
+ * - Input values.  Any finite values with |x| < 2^56 are supported.  The
+ *   clustering sums the members of a cluster exactly (two 64-bit fixed-point
+ *   words per element at a power-of-two scale chosen per head from its largest
+ *   magnitude M < 2^E), which captures every value whose unit in the last place
+ *   is at least 2^(E - 2B), B = min(51, 62 - ceil(log2(N + 1))): for bf16 that
+ *   is every non-zero |x| >= 2^(E + 7 - 2B) (2^(E - 83) at N = 75,600), for
+ *   fp32 every |x| >= 2^(E + 23 - 2B).  A head with a non-finite value, a value
+ *   of magnitude 2^56 or more, or a non-zero value below that floor is
+ *   detected on the device; under SVGEAR_DEBUG_SYNC the call then returns
+ *   SVGEAR_E_RANGE (without it, results of such a head are unspecified).
  */
 #ifndef SVGEAR_H
 #define SVGEAR_H
@@ -55,7 +63,10 @@ typedef enum {
     SVGEAR_E_WORKSPACE = -5, /* ws_bytes is smaller than svgear_workspace_bytes()        */
     SVGEAR_E_RHO = -6,       /* rho is NaN or outside [0, 1]                             */
     SVGEAR_E_HIP = -7,       /* the HIP runtime reported an error                        */
-    SVGEAR_E_ARG = -8        /* another invalid argument (side, flags)                   */
+    SVGEAR_E_ARG = -8,       /* another invalid argument (side, flags); under
+                                SVGEAR_DEBUG_SYNC also an init or label index out of range */
+    SVGEAR_E_RANGE = -9      /* under SVGEAR_DEBUG_SYNC: an input value is out of the
+                                supported range (see "Input values" above)                  */
 } svgear_status;
 
 typedef enum { SVGEAR_F32 = 0, SVGEAR_BF16 = 1 } svgear_dtype;
@@ -123,7 +134,8 @@ int svgear_workspace_bytes(const svgear_shape* shape, size_t* bytes);
  * [0, C)) and init_idx may be NULL; k-means is skipped, cent holds the member
  * means (zero for an empty cluster).  V/vbar/Vp must be NULL on side 0 and
  * non-NULL on side 1.  Errors: _NULL, _SHAPE, _DTYPE, _ALIGN, _WORKSPACE, _ARG
- * (side or flags), _HIP. */
+ * (side or flags), _HIP; under SVGEAR_DEBUG_SYNC also _RANGE (see "Input
+ * values") and _ARG for an init or label index outside its range. */
 int svgear_cluster(const svgear_shape* shape, int side, const void* X, const void* V,
                    const int32_t* init_idx, int flags, int32_t* labels, float* cent, float* vbar,
                    int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* Xp,
@@ -203,10 +215,14 @@ int svgear_attention(const svgear_shape* shape, const void* Qp, const int32_t* o
  * event and joined back by another before the probe, so it overlaps the K
  * clustering; everything else runs on `stream`, and when the call returns all
  * of its work is ordered on `stream` (safe under stream capture).  `stream`
- * must belong to the current device.  Errors as the stages. */
+ * must belong to the current device.  flags: 0 or SVGEAR_DEBUG_SYNC, which
+ * waits for the call and reports the data errors the clusterings detect on the
+ * device (SVGEAR_E_RANGE, or SVGEAR_E_ARG for an init index outside [0, N)).
+ * Errors as the stages, and _ARG for other flags. */
 int svgear_forward(const svgear_shape* shape, double rho, const void* Q, const void* K,
                    const void* V, const int32_t* init_q, const int32_t* init_k, void* O,
-                   const svgear_intermediates* im, void* ws, size_t ws_bytes, void* stream);
+                   const svgear_intermediates* im, int flags, void* ws, size_t ws_bytes,
+                   void* stream);
 
 /* Static description of a status code. */
 const char* svgear_status_string(int code);

@@ -45,13 +45,13 @@ SVG_HIDDEN Layout make_layout(const svgear_shape& s)
     L.log_ratio = take(H * Cq * Ck * 4);
     L.mask = take(H * Cq * Ck);
     L.sel_cost = take(H * 8);
+    L.errs = take(256);   // device error words: [0] K side / stage calls, [16] Q side of svgear_forward
     L.scratch = off;
 
     // cluster scratch (sized for the larger side)
     const size_t N = Nq > Nk ? Nq : Nk, C = Cq > Ck ? Cq : Ck;
     const size_t ntiles = (N + kTile - 1) / kTile;
     off = 0;
-    L.cl_err = take(256);
     L.cl_cent64 = take(H * C * d * 8);
     L.cl_hi = take(H * C * d * 2);
     L.cl_lo = take(H * C * d * 2);
@@ -62,7 +62,8 @@ SVG_HIDDEN Layout make_layout(const svgear_shape& s)
     L.cl_nflag = take(H * 4);
     L.cl_hist = take(H * ntiles * C * 4);
     L.cl_perm = take(H * N * 4);
-    L.cl_sums = take(H * C * d * 8);
+    L.cl_sums = take(2 * H * C * d * 8);
+    L.cl_range = take(H * kRangeStride * 4);
     L.cl_resid = take(H * C * 4);
     L.cl_labprev = take(H * N * 4);
     L.cl_bounds = take(3 * H * N * 4);
@@ -74,24 +75,19 @@ SVG_HIDDEN Layout make_layout(const svgear_shape& s)
     L.cl_end = off;
 
     off = 0;
-    L.pr_err = take(256);
-    L.pr_qplanes = take(3 * H * Cq * d * 2);
     L.pr_sbar = take(H * Cq * Ck * 4);
     L.pr_keys = take(H * Nk * 8);
     L.pr_pg = take(H * Ck * 4);
     L.pr_end = off;
 
     off = 0;
-    L.at_err = take(256);
     L.at_kvplanes = take(4 * H * Ck * d * 2);
     L.at_logm = take(H * Ck * 4);
     L.at_tiles = take(H * (Cq + 1) * 4 + 256);
     L.at_segs = take(H * Cq * Ck * 8);
-    L.at_nsegs = take(H * Cq * 4);
-    L.at_nkeys = take(H * Cq * 4);
+    L.at_cinfo = take(H * Cq * 16);
     L.at_comp = take(H * Cq * Ck * 4);
-    L.at_ncomp = take(H * Cq * 4);
-    L.at_rowmap = take(H * Cq * Nk * 4);
+    L.at_rows = take((size_t)kAttnSlots * Nk * 4);   // one routed-key row list per attention workgroup
     // work queues: meta (count, start, counter per XCD class), per-head class
     // counts and in-class prefixes, the queue itself (at most H (ceil(Nq / rows) + Cq) tiles)
     L.at_queue = take((3 * kXcd + H * kXcd + H * Cq + H * ((Nq + kAttnRows - 1) / kAttnRows + Cq)) * 4);
@@ -183,21 +179,26 @@ static int check_ws(const svgear_shape* s, void* ws, size_t ws_bytes, Layout* L)
     return SVGEAR_OK;
 }
 
+// Status of a device error word: out-of-range data first, then invalid indices.
+static int device_status(int v)
+{
+    if (v < 0) return SVGEAR_E_HIP;
+    if (v & ERR_RANGE) return SVGEAR_E_RANGE;
+    if (v != 0) return SVGEAR_E_ARG;
+    return SVGEAR_OK;
+}
+
 static int finish(hipError_t e, int flags, hipStream_t st, const int* err_word)
 {
     if (e != hipSuccess) return SVGEAR_E_HIP;
     if (flags & SVGEAR_DEBUG_SYNC) {
         if (hipStreamSynchronize(st) != hipSuccess) return SVGEAR_E_HIP;
-        if (err_word) {
-            int v = read_device_error(err_word, st);
-            if (v < 0) return SVGEAR_E_HIP;
-            if (v != 0) return SVGEAR_E_ARG;
-        }
+        if (err_word) return device_status(read_device_error(err_word, st));
     }
     return SVGEAR_OK;
 }
 
-SVG_API int svgear_version(void) { return 10000; }
+SVG_API int svgear_version(void) { return 20000; }
 
 SVG_API const char* svgear_status_string(int code)
 {
@@ -211,6 +212,7 @@ SVG_API const char* svgear_status_string(int code)
     case SVGEAR_E_RHO: return "rho must be in [0, 1]";
     case SVGEAR_E_HIP: return "HIP runtime error";
     case SVGEAR_E_ARG: return "invalid argument";
+    case SVGEAR_E_RANGE: return "input values out of the supported range";
     default: return "unknown status";
     }
 }
@@ -224,11 +226,14 @@ SVG_API int svgear_workspace_bytes(const svgear_shape* shape, size_t* bytes)
     return SVGEAR_OK;
 }
 
+// Byte offset, in the workspace's error region, of the Q-side word of svgear_forward.
+constexpr size_t kErrQ = 64;
+
 static int cluster_impl(const svgear_shape* shape, int side, const void* X, const void* V,
                         const int32_t* init_idx, int flags, int32_t* labels, float* cent,
                         float* vbar, int32_t* counts, int32_t* offsets, int32_t* perm,
                         int32_t* inv_perm, void* Xp, void* Vp, void* ws, const Layout& L,
-                        hipStream_t st, size_t scratch_off = 0)
+                        hipStream_t st, size_t scratch_off = 0, size_t err_off = 0)
 {
     ClusterArgs a;
     a.H = shape->H;
@@ -239,7 +244,6 @@ static int cluster_impl(const svgear_shape* shape, int side, const void* X, cons
     a.dtype = shape->dtype;
     a.side = side;
     a.flags = flags;
-    a.shift = fixed_point_shift(a.N);
     a.X = X;
     a.V = V;
     a.init = init_idx;
@@ -253,10 +257,11 @@ static int cluster_impl(const svgear_shape* shape, int side, const void* X, cons
     a.Xp = Xp;
     a.Vp = Vp;
     a.scratch = (char*)ws + (scratch_off ? scratch_off : L.scratch);
+    a.err = (int*)((char*)ws + L.errs + err_off);
     a.L = &L;
-    zero_words(a.scratch + L.cl_err, 256, st);
+    zero_words(a.err, 64, st);
     hipError_t e = launch_cluster(a, st);
-    return finish(e, flags, st, (const int*)(a.scratch + L.cl_err));
+    return finish(e, flags, st, a.err);
 }
 
 SVG_API int svgear_cluster(const svgear_shape* shape, int side, const void* X, const void* V,
@@ -446,11 +451,13 @@ SVG_API int svgear_attention(const svgear_shape* shape, const void* Qp, const in
 
 SVG_API int svgear_forward(const svgear_shape* shape, double rho, const void* Q, const void* K,
                            const void* V, const int32_t* init_q, const int32_t* init_k, void* O,
-                           const svgear_intermediates* im, void* ws, size_t ws_bytes, void* stream)
+                           const svgear_intermediates* im, int flags, void* ws, size_t ws_bytes,
+                           void* stream)
 {
     int rc = check_shape(shape);
     if (rc) return rc;
     if (!(rho >= 0.0 && rho <= 1.0)) return SVGEAR_E_RHO;
+    if (flags & ~SVGEAR_DEBUG_SYNC) return SVGEAR_E_ARG;
     rc = check_ptrs({Q, K, V, init_q, init_k, O});
     if (rc) return rc;
     Layout L;
@@ -495,7 +502,7 @@ SVG_API int svgear_forward(const svgear_shape* shape, double rho, const void* Q,
             return SVGEAR_E_HIP;
         const int rq = cluster_impl(shape, 0, Q, nullptr, init_q, 0, labels_q, qbar, nullptr,
                                     counts_q, offsets_q, perm_q, inv_perm_q, Qp, nullptr, ws, L,
-                                    ss->stream, L.scratch2);
+                                    ss->stream, L.scratch2, kErrQ);
         const bool joined = hipEventRecord(ss->join, ss->stream) == hipSuccess;
         const int rk = cluster_impl(shape, 1, K, V, init_k, 0, labels_k, kbar, vbar, counts_k,
                                     offsets_k, perm_k, inv_perm_k, Kp, Vp, ws, L, st);
@@ -504,7 +511,7 @@ SVG_API int svgear_forward(const svgear_shape* shape, double rho, const void* Q,
         if (rk) return rk;
     } else {
         rc = cluster_impl(shape, 0, Q, nullptr, init_q, 0, labels_q, qbar, nullptr, counts_q,
-                          offsets_q, perm_q, inv_perm_q, Qp, nullptr, ws, L, st);
+                          offsets_q, perm_q, inv_perm_q, Qp, nullptr, ws, L, st, 0, kErrQ);
         if (rc) return rc;
         rc = cluster_impl(shape, 1, K, V, init_k, 0, labels_k, kbar, vbar, counts_k, offsets_k,
                           perm_k, inv_perm_k, Kp, Vp, ws, L, st);
@@ -524,6 +531,14 @@ SVG_API int svgear_forward(const svgear_shape* shape, double rho, const void* Q,
     ra.mask = mask;
     ra.sel_cost = sel_cost;
     if (launch_route(ra, st) != hipSuccess) return SVGEAR_E_HIP;
-    return attention_impl(shape, Qp, offsets_q, perm_q, Kp, Vp, kbar, vbar, counts_k, offsets_k,
-                          mask, O, ws, L, 0, st);
+    rc = attention_impl(shape, Qp, offsets_q, perm_q, Kp, Vp, kbar, vbar, counts_k, offsets_k, mask,
+                        O, ws, L, 0, st);
+    if (rc || !(flags & SVGEAR_DEBUG_SYNC)) return rc;
+    // Device-detected data errors of both clusterings (K side word first).
+    if (hipStreamSynchronize(st) != hipSuccess) return SVGEAR_E_HIP;
+    const int* err = (const int*)(w + L.errs);
+    const int ek = read_device_error(err, st);
+    const int eq = read_device_error((const int*)((const char*)err + kErrQ), st);
+    if (ek < 0 || eq < 0) return SVGEAR_E_HIP;
+    return device_status(ek | eq);
 }

@@ -215,7 +215,7 @@ __global__ __launch_bounds__(256, 3) void k_assign_mfma(
     const float* __restrict__ cn32, const unsigned* __restrict__ stats, int N, int C,
     int32_t* __restrict__ labels, int32_t* __restrict__ flags, int* __restrict__ nflag,
     float* __restrict__ ub_own, float* __restrict__ lb_own, float* __restrict__ lb_rest,
-    const int* __restrict__ mcount)
+    const int* __restrict__ mcount, unsigned* __restrict__ range)
 {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int h = blockIdx.y;
@@ -250,6 +250,18 @@ __global__ __launch_bounds__(256, 3) void k_assign_mfma(
         }
         ss += __shfl_xor(ss, 32);
         nx[tb] = sqrtf(ss);
+    }
+    if (range) {   // the first screen reads every row of X: its largest magnitude sets the sums' scale
+        RangeBf16 rg;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const u32x4_t w = __builtin_bit_cast(u32x4_t, xf[tb][s]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) rg.add_max(w[e]);
+            }
+        range_commit(rg.max_word(), 0u, range + kRangeStride * h, false);
     }
 
     // per lane and token block: the two smallest screen distances, index of the first
@@ -600,6 +612,9 @@ __global__ __launch_bounds__(256) void k_recheck(const bf16* __restrict__ X,
                     best = s_rb[w];
                     bi = s_ri[w];
                 }
+            // No candidate only with non-finite distances (an out-of-range input,
+            // reported as ERR_RANGE): keep the screen's label, which is in range.
+            if (bi >= C) bi = labels[(size_t)h * N + token];
             labels[(size_t)h * N + token] = bi;
             s_win = bi;
         }
@@ -662,7 +677,8 @@ SVG_HIDDEN hipError_t launch_km_prep(const ClusterArgs& a, const double* cent64,
 }
 
 SVG_HIDDEN hipError_t launch_assign_mfma(const ClusterArgs& a, const double* cent64,
-                                         const KmPlanes& P, bool partial, hipStream_t st)
+                                         const KmPlanes& P, bool partial, unsigned* range,
+                                         hipStream_t st)
 {
     // With `partial`, both screens are launched and each head runs in the one
     // its moved-centroid count selects (decided on the device).
@@ -672,11 +688,11 @@ SVG_HIDDEN hipError_t launch_assign_mfma(const ClusterArgs& a, const double* cen
     if (partial)
         hipLaunchKernelGGL(k_assign_mfma<true>, grid, dim3(256), KmScreen<true>::LDS, st, (const bf16*)a.X, P.hi, P.lo,
                            P.cn32, P.stats, a.N, a.C, a.labels, P.flags, P.nflag, P.ub_own, P.lb_own,
-                           P.lb_rest, (const int*)P.mcount);
+                           P.lb_rest, (const int*)P.mcount, (unsigned*)nullptr);
     else
         hipLaunchKernelGGL(k_assign_mfma<false>, grid, dim3(256), KmScreen<false>::LDS, st, (const bf16*)a.X, P.hi, P.lo,
                            P.cn32, P.stats, a.N, a.C, a.labels, P.flags, P.nflag, P.ub_own, P.lb_own,
-                           P.lb_rest, (const int*)nullptr);
+                           P.lb_rest, (const int*)nullptr, range);
     if (partial)
         hipLaunchKernelGGL(k_assign_partial, grid, dim3(256), KmPartialChunk::BYTES, st, (const bf16*)a.X, P.hi,
                            P.lo, P.cn32, P.stats, P.mlist, P.mpos, P.mcount, a.N, a.C, a.labels,

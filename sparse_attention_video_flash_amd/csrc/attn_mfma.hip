@@ -58,8 +58,13 @@ constexpr int C_BUF = 4 * T_BUF;
 constexpr int C_AREA = 2 * C_BUF + 2 * AT_BN * 4;
 constexpr int at_max(int a, int b) { return a > b ? a : b; }
 constexpr int AT_AREA = at_max(C_AREA, at_max(AT_NBUF * 2 * T_BUF, AT_BM * K_PITCH));
-constexpr int AT_LDS = AT_AREA + 16;  // + job slot
+// The exact phase's segment table (at most kMaxC (end, delta) pairs) sits
+// after its two tile buffers.
+constexpr int AT_TAB_OFF = AT_NBUF * 2 * T_BUF;
+constexpr int AT_JOB_OFF = at_max(AT_AREA, AT_TAB_OFF + kMaxC * 8);
+constexpr int AT_LDS = AT_JOB_OFF + 16;   // + job slot
 static_assert(AT_LDS <= 160 * 1024, "LDS of one workgroup");
+static_assert(kAttnSlots >= 1, "row-list slots");
 static_assert(AT_BM == kAttnRows, "tile rows as sized in the workspace layout");
 constexpr int AT_XCD = 8;
 
@@ -91,15 +96,16 @@ __global__ void k_comp_planes(const float* __restrict__ kbar, const float* __res
     }
 }
 
-// Per (head, query cluster), in key-cluster order: the routed segments
-// (first reordered key, length) of every g with mask[c, g] = 1 and m_g > 0, their
-// total length, and the list of compensated clusters (mask = 0, m_g > 0).
+// Per (head, query cluster), in key-cluster order: the routed segments of every
+// g with mask[c, g] = 1 and m_g > 0, as a table of (end, delta) pairs over the
+// packed key list (list positions pref_s .. end_s - 1 hold the reordered key
+// rows pref_s + delta_s .. end_s - 1 + delta_s of cluster s's segment), and the
+// list of compensated clusters (mask = 0, m_g > 0); cinfo holds (routed keys,
+// segments, compensated clusters).
 __global__ __launch_bounds__(256) void k_seg_list(const uint8_t* __restrict__ mask,
                                                   const int32_t* __restrict__ offsets_k, int Cq,
-                                                  int Ck, int Nk, int2* __restrict__ segs,
-                                                  int* __restrict__ nsegs, int* __restrict__ nkeys,
-                                                  int* __restrict__ comp, int* __restrict__ ncomp,
-                                                  int* __restrict__ rowmap)
+                                                  int Ck, int2* __restrict__ segs,
+                                                  int4* __restrict__ cinfo, int* __restrict__ comp)
 {
     __shared__ int s_a[256], s_b[256];
     extern __shared__ int s_seg[];       // [Ck] first rows, [Ck + 1] key prefixes of routed segments
@@ -133,7 +139,6 @@ __global__ __launch_bounds__(256) void k_seg_list(const uint8_t* __restrict__ ma
         }
         if (sel) {
             const int si = base + s_a[tid] - 1;
-            out[si] = make_int2(start, len);
             s_start[si] = start;
             s_pref[si] = len;
         }
@@ -157,25 +162,10 @@ __global__ __launch_bounds__(256) void k_seg_list(const uint8_t* __restrict__ ma
     int acc = s_a[tid] - run;
     for (int k = 0; k < per && s0 + k < base; ++k) {
         const int len = s_pref[s0 + k];
-        s_pref[s0 + k] = acc;
+        out[s0 + k] = make_int2(acc + len, s_start[s0 + k] - acc);
         acc += len;
     }
-    const int keys = s_a[255];
-    if (tid == 0) s_pref[base] = keys;
-    __syncthreads();
-    if (tid == 0) {
-        nsegs[(size_t)h * Cq + c] = base;
-        ncomp[(size_t)h * Cq + c] = cbase;
-        nkeys[(size_t)h * Cq + c] = keys;
-    }
-    // Row map: list position -> reordered key row; wave w writes segments
-    // w, w + 4, ...
-    int* rm = rowmap + ((size_t)h * Cq + c) * Nk;
-    const int wv = tid >> 6, ln = tid & 63;
-    for (int si = wv; si < base; si += 4) {
-        const int r0 = s_start[si], p0 = s_pref[si], len = s_pref[si + 1] - p0;
-        for (int k = ln; k < len; k += 64) rm[p0 + k] = r0 + k;
-    }
+    if (tid == 0) cinfo[(size_t)h * Cq + c] = make_int4(s_a[255], base, cbase, 0);   // keys, segments, comp
 }
 
 // Per head: first query tile of each cluster (exclusive prefix of ceil(n_c/BM)).
@@ -475,16 +465,40 @@ __device__ __forceinline__ void tile_fill(char* b, __amdgpu_buffer_rsrc_t rk, __
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)(vb + 4 * i * ROW_B), 16, r[i] * ROW_B + vx, 0, 0, 0);
 }
 
-// The exact tiles of one query tile: the routed keys (row map rm, nk keys) in
+// Row list: the packed routed-key list of one (head, query cluster), list
+// position -> reordered key row, written by the whole workgroup into its own
+// slot of device memory from the segment table tab (in LDS, ns entries
+// (end_s, delta_s): positions end_{s-1} .. end_s - 1 hold rows position +
+// delta_s).  Thread t fills a run of consecutive positions: a binary search
+// finds the segment of its first position, then it walks forward.
+__device__ __forceinline__ void row_list(int* __restrict__ w, const int2* __restrict__ tab, int ns, int nk)
+{
+    const int per = (nk + AT_THREADS - 1) / AT_THREADS;
+    const int q0 = (int)threadIdx.x * per;
+    const int q1 = min(q0 + per, nk);
+    if (q0 >= q1) return;
+    int lo = 0, hi = ns - 1;   // first segment whose end exceeds q0
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (tab[mid].x > q0) hi = mid; else lo = mid + 1;
+    }
+    int2 e = tab[lo];
+    for (int q = q0; q < q1; ++q) {
+        while (e.x <= q) e = tab[++lo];
+        w[q] = q + e.y;
+    }
+}
+
+// The exact tiles of one query tile: the routed keys, rows rm[0 .. nk), in
 // 64-key tiles through two LDS buffers.  Each step requests the row indices of
 // tile t + 2, then the rows of tile t + 1 straight into the other buffer, then
-// computes tile t; the loads land during the math.  The two buffers are
-// distinct restrict-qualified pointers and the loop is unrolled by two, so
-// the compiler sees that the loads in flight never alias the buffer being
-// read and adds no wait of its own before the reads; the explicit wait before
-// each barrier covers this wave's loads and the barrier publishes every
-// wave's rows.  Loads past the last tile use clamped rows into a buffer no
-// one reads; all loads drain before returning.
+// computes tile t; the loads land during the math.  The two buffers and
+// the row list are distinct restrict-qualified pointers and the loop is
+// unrolled by two, so the compiler sees that the loads in flight never alias
+// the buffer being read and adds no wait of its own before the reads; the
+// explicit wait before each barrier covers this wave's loads and the barrier
+// publishes every wave's rows.  Loads past the last tile use clamped rows into
+// a buffer no one reads; all loads drain before returning.
 __device__ __forceinline__ void exact_tiles(char* __restrict__ b0, char* __restrict__ b1, Softmax& st,
                                             const bf16x8_t qf[8], __amdgpu_buffer_rsrc_t rk,
                                             __amdgpu_buffer_rsrc_t rv, const int* __restrict__ rm, int nk,
@@ -520,7 +534,7 @@ __device__ __forceinline__ void exact_tiles(char* __restrict__ b0, char* __restr
             softmax_update(st, acc, scale2, pf);                                              \
             tile_pv(st, CUR + T_BUF, pf, lane);                                               \
         }                                                                                     \
-        __builtin_amdgcn_s_waitcnt(0x0F70 | 0);   /* tile T + 1 and rows of T + 2 landed */   \
+        __builtin_amdgcn_s_waitcnt(0x0F70 | 0);   /* tile T + 1 landed */                     \
         tile_barrier();                                                                       \
     }
     for (int t = 0; t < ntiles; t += 2) {
@@ -626,8 +640,8 @@ __device__ __forceinline__ void attn_tile(
     const int32_t* __restrict__ offsets_q, const int32_t* __restrict__ perm_q,
     const bf16* __restrict__ Kp, const bf16* __restrict__ Vp, const bf16* __restrict__ kbh,
     const bf16* __restrict__ kbl, const bf16* __restrict__ vbh, const bf16* __restrict__ vbl,
-    const float* __restrict__ logm2, const int* __restrict__ rowmap, const int* __restrict__ nkeys,
-    const int* __restrict__ comp, const int* __restrict__ ncomp, const int* __restrict__ tstart, int Nq,
+    const float* __restrict__ logm2, const int2* __restrict__ segs, const int4* __restrict__ cinfo,
+    const int* __restrict__ comp, const int* __restrict__ tstart, int* __restrict__ rows, int Nq,
     int Nk, int Cq, int Ck, int tiles_per_head, float scale2, bf16* __restrict__ O)
 {
     const int h = logical / tiles_per_head, t = logical - h * tiles_per_head;
@@ -664,9 +678,10 @@ __device__ __forceinline__ void attn_tile(
 
     const size_t hc = (size_t)h * Cq + c;
     const float* lm = logm2 + (size_t)h * Ck;
+    const int4 ci = cinfo[hc];   // (routed keys, segments, compensated clusters)
 
     // 1. compensation tiles: packed list of skipped non-empty key clusters
-    const int nc = ncomp[hc];
+    const int nc = ci.z;
     if (nc > 0) {
         const size_t pb = (size_t)h * Ck * AT_D;
         const int plane_bytes = Ck * AT_D * 2;
@@ -680,16 +695,24 @@ __device__ __forceinline__ void attn_tile(
                    lane, wact, scale2);
     }
 
-    // 2. exact tiles (packed routed keys)
-    const int nk = nkeys[hc];
+    // 2. exact tiles (packed routed keys); their row window uses the LDS half
+    // that the exact tiles leave free (the compensation tiles, which use it, are
+    // done: their last step ended in a barrier)
+    const int nk = ci.x;
     if (nk > 0) {
-        const int* rm = rowmap + hc * Nk;
         const size_t head_bytes = (size_t)Nk * AT_D * 2;
         const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(Kp + (size_t)h * Nk * AT_D), (short)0, (int)head_bytes, 0x00020000);
         const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(Vp + (size_t)h * Nk * AT_D), (short)0, (int)head_bytes, 0x00020000);
-        exact_tiles(KBUF(0), KBUF(1), st, qf, rk, rv, rm, nk, wave, lane, wact, scale2);
+        const int ns = ci.y;
+        int2* const tab = (int2*)(smem + AT_TAB_OFF);
+        const int2* sgh = segs + hc * Ck;
+        for (int k = tid; k < ns; k += AT_THREADS) tab[k] = sgh[k];
+        __syncthreads();
+        row_list(rows, tab, ns, nk);
+        __syncthreads();   // the slot's rows are visible to every wave of the workgroup
+        exact_tiles(KBUF(0), KBUF(1), st, qf, rk, rv, rows, nk, wave, lane, wact, scale2);
     }
 
     // 3. normalise, stage the tile in LDS as [query][d], store rows in token order
@@ -724,18 +747,26 @@ __device__ __forceinline__ void attn_tile(
     }
 }
 
+// planes: the k-bar hi, k-bar lo, v-bar hi and v-bar lo planes, [H, Ck, d] each,
+// one after another; qmeta: the work-queue region (lengths, starts, counters,
+// per-head counts and prefixes, then the queue itself).
 __global__ __launch_bounds__(AT_THREADS, 2) void k_attn_mfma(
     const bf16* __restrict__ Qp, const int32_t* __restrict__ offsets_q,
     const int32_t* __restrict__ perm_q, const bf16* __restrict__ Kp, const bf16* __restrict__ Vp,
-    const bf16* __restrict__ kbh, const bf16* __restrict__ kbl, const bf16* __restrict__ vbh,
-    const bf16* __restrict__ vbl, const float* __restrict__ logm2, const int* __restrict__ rowmap,
-    const int* __restrict__ nkeys, const int* __restrict__ comp,
-    const int* __restrict__ ncomp, const int* __restrict__ tstart, const int* __restrict__ qmeta,
-    int* __restrict__ qctr, const int* __restrict__ qlist, int H, int Nq, int Nk, int Cq, int Ck,
+    const bf16* __restrict__ planes, const float* __restrict__ logm2, const int2* __restrict__ segs,
+    const int4* __restrict__ cinfo, const int* __restrict__ comp, const int* __restrict__ tstart,
+    int* __restrict__ qmeta, int* __restrict__ rowbuf, int H, int Nq, int Nk, int Cq, int Ck,
     int tiles_per_head, float scale2, bf16* __restrict__ O)
 {
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    int* const s_job = (int*)(smem + AT_AREA);
+    int* const s_job = (int*)(smem + AT_JOB_OFF);
+    const size_t plane = (size_t)H * Ck * AT_D;
+    const bf16* const kbh = planes;
+    const bf16* const kbl = planes + plane;
+    const bf16* const vbh = planes + 2 * plane;
+    const bf16* const vbl = planes + 3 * plane;
+    int* const qctr = qmeta + 2 * AT_XCD;
+    const int* const qlist = qmeta + 3 * AT_XCD + (size_t)H * AT_XCD + (size_t)H * Cq;
 
     const int x0 = blockIdx.x % AT_XCD;
     for (int k = 0; k < AT_XCD; ++k) {
@@ -748,8 +779,8 @@ __global__ __launch_bounds__(AT_THREADS, 2) void k_attn_mfma(
             const int j = *s_job;
             if (j >= qlen) break;
             attn_tile(qlist[qstart + j], smem, Qp, offsets_q, perm_q, Kp, Vp, kbh, kbl,
-                      vbh, vbl, logm2, rowmap, nkeys, comp, ncomp, tstart, Nq, Nk, Cq, Ck, tiles_per_head,
-                      scale2, O);
+                      vbh, vbl, logm2, segs, cinfo, comp, tstart, rowbuf + (size_t)blockIdx.x * Nk, Nq,
+                      Nk, Cq, Ck, tiles_per_head, scale2, O);
         }
     }
 }
@@ -775,15 +806,12 @@ SVG_HIDDEN hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t st)
     float* logm2 = (float*)(s + L.at_logm);
     int* tstart = (int*)(s + L.at_tiles);
     int2* segs = (int2*)(s + L.at_segs);
-    int* nsegs = (int*)(s + L.at_nsegs);
-    int* nkeys = (int*)(s + L.at_nkeys);
+    int4* cinfo = (int4*)(s + L.at_cinfo);
     int* comp = (int*)(s + L.at_comp);
-    int* ncomp = (int*)(s + L.at_ncomp);
-    int* rowmap = (int*)(s + L.at_rowmap);
     hipLaunchKernelGGL(k_comp_planes, dim3(a.Ck, a.H), dim3(AT_D), 0, st, a.kbar, a.vbar, a.counts_k,
                        a.Ck, kbh, kbl, vbh, vbl, logm2);
     hipLaunchKernelGGL(k_seg_list, dim3(a.Cq, a.H), dim3(256), (2 * a.Ck + 1) * 4, st, a.mask, a.offsets_k, a.Cq,
-                       a.Ck, a.Nk, segs, nsegs, nkeys, comp, ncomp, rowmap);
+                       a.Ck, segs, cinfo, comp);
     hipLaunchKernelGGL(k_tile_prefix, dim3(a.H), dim3(1024), 0, st, a.offsets_q, a.Cq, tstart);
     const int tiles_per_head = (a.Nq + AT_BM - 1) / AT_BM + a.Cq;
     int* qmeta = (int*)(s + L.at_queue);       // [8] lengths, [8] starts, [8] counters
@@ -799,13 +827,14 @@ SVG_HIDDEN hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t st)
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         ncu = 0;
-    const int nwg = ncu > 0 ? ncu : 256;   // one 8-wave workgroup per CU (two waves per SIMD)
+    // one 8-wave workgroup per CU (two waves per SIMD), each with its own row-list slot
+    const int nwg = ncu > 0 && ncu < kAttnSlots ? ncu : kAttnSlots;
     const float scale2 = (float)(1.4426950408889634 / sqrt((double)AT_D));
     hipLaunchKernelGGL(k_attn_mfma, dim3(nwg), dim3(AT_THREADS), AT_LDS, st,
                        (const bf16*)a.Qp, a.offsets_q, a.perm_q, (const bf16*)a.Kp,
-                       (const bf16*)a.Vp, kbh, kbl, vbh, vbl, logm2, rowmap, nkeys, comp, ncomp,
-                       tstart, qmeta, qmeta + 2 * AT_XCD, qlist, a.H, a.Nq, a.Nk, a.Cq, a.Ck,
-                       tiles_per_head, scale2, (bf16*)a.O);
+                       (const bf16*)a.Vp, (const bf16*)kbh, logm2, segs, (const int4*)cinfo, comp, tstart,
+                       qmeta, (int*)(s + L.at_rows), a.H, a.Nq, a.Nk, a.Cq, a.Ck, tiles_per_head, scale2,
+                       (bf16*)a.O);
     return hipGetLastError();
 }
 

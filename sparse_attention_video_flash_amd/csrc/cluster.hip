@@ -5,10 +5,13 @@
 //
 // Exactness strategy.  The assignment picks the nearest centroid in squared
 // Euclidean distance with ties to the lowest index.  Centroids are kept in fp64
-// and are the exact member means: member rows are summed as 64-bit fixed-point
-// integers (every bf16/fp32 input with |x| < 256 and magnitude above 2^-S is an
-// exact multiple of 2^-S), so the sum does not depend on the order of the rows;
-// one rounding to fp64 and one fp64 division follow.  Each update buckets the
+// and are the exact member means: member rows are summed as pairs of 64-bit
+// fixed-point integers at a power-of-two scale chosen per head from the
+// largest input magnitude (internal.h, fix_add), so the sum does not depend on
+// the order of the rows; one rounding to fp64 and one fp64 division follow.
+// The kernels that first read a tensor (the first assignment, the scatter)
+// record its per-head range; a head whose values cannot all be captured
+// exactly (or that holds a non-finite value) raises ERR_RANGE.  Each update buckets the
 // token ids by label and one block per cluster sums its rows (no atomics).
 // Distances are either evaluated directly in fp64 (generic kernel) or screened
 // with bf16 MFMA and re-evaluated in fp64 whenever the screen cannot separate
@@ -54,7 +57,8 @@ __global__ void k_init_centroids(const T* __restrict__ X, const int32_t* __restr
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_assign_exact(const T* __restrict__ X,
                                                       const double* __restrict__ cent64, int N,
-                                                      int C, int32_t* __restrict__ labels)
+                                                      int C, int32_t* __restrict__ labels,
+                                                      unsigned* __restrict__ range)
 {
 #pragma clang fp contract(off)
     constexpr int CH = 32768 / (D * 8);  // centroids per 32 KB chunk
@@ -62,11 +66,16 @@ __global__ __launch_bounds__(256) void k_assign_exact(const T* __restrict__ X,
     const int h = blockIdx.y;
     const int i = blockIdx.x * 256 + threadIdx.x;
     float xr[D];  // exact copies of the inputs
+    unsigned rmx = 0u;
     if (i < N) {
         const T* x = X + ((size_t)h * N + i) * D;
 #pragma unroll
-        for (int t = 0; t < D; ++t) xr[t] = to_f32<T>(x[t]);
+        for (int t = 0; t < D; ++t) {
+            xr[t] = to_f32<T>(x[t]);
+            rmx = max(rmx, __float_as_uint(xr[t]) & 0x7FFFFFFFu);
+        }
     }
+    if (range) range_commit(rmx, 0u, range + kRangeStride * h, false);   // largest magnitude (sets the scale)
     double best = __builtin_inf();
     int bi = 0;
     const double* cb = cent64 + (size_t)h * C * D;
@@ -223,35 +232,53 @@ __global__ __launch_bounds__(256) void k_bucket(const int32_t* __restrict__ labe
 
 // Cluster means from exact fixed-point sums.  The bucketed token order is cut
 // into chunks of MC_ROWS positions, one block each; a block sums the rows of
-// every cluster segment in its chunk as 64-bit integers (scale 2^shift) and adds
-// them to the cluster's running sums with integer atomics (exact, so the order
-// does not matter).  k_cluster_finalize then turns the sums into means.  The
-// fixed-point image of each element is its value times 2^shift rounded to the
-// nearest integer (fixed_bits), exact for every input that is a multiple of
-// 2^-shift.
+// every cluster segment in its chunk as 64-bit integers (fix_hi, or both words
+// of fix_add, at the head's scale) and adds them to the cluster's running sums
+// with integer atomics (exact, so the order does not matter).
+// k_cluster_finalize then turns the sums into means.
+//
+// MODE selects the instantiation: the one-word kernel serves the heads whose
+// values are all captured by the first word (fix_need_lo false; the usual
+// case), the two-word kernel the others, each returning at once for a head the
+// other serves; both are launched.  With collect (a pass that reads every row
+// while the smallest magnitude is not yet known: the first update of the
+// k-means, or the only pass of a tensor) the one-word kernel runs for every
+// head and records the smallest non-zero magnitude; a head that then turns out
+// to need the second word has its sums cleared (k_clear_two_word_heads) and
+// redone by the two-word kernel.
 constexpr int MC_ROWS = 512;
 
-template <typename T, int D>
+enum : int { CH_ONE = 0, CH_ONE_COLLECT = 1, CH_TWO = 2 };
+template <typename T, int D, int MODE>
 __global__ __launch_bounds__(256) void k_cluster_chunks(const T* __restrict__ X,
                                                         const int32_t* __restrict__ perm,
                                                         const int32_t* __restrict__ offsets, int N,
-                                                        int C, int shift,
+                                                        int C, unsigned* __restrict__ range,
                                                         unsigned long long* __restrict__ sums,
                                                         const int* __restrict__ changed)
 {
+    constexpr bool TWO = MODE == CH_TWO, COLLECT = MODE == CH_ONE_COLLECT;
     constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
     constexpr int CPR = D / EPC;               // chunks per row
     constexpr int RPP = 256 / CPR;             // rows per pass
+    constexpr int PREC = sizeof(T) == 2 ? 8 : 24;
     __shared__ long long s_sum[RPP][D];
     __shared__ int s_idx[MC_ROWS];
     const int h = blockIdx.y;
+    const int base = fix_base(N);
+    unsigned* rg4 = range + kRangeStride * h;
+    if (TWO ? !fix_need_lo(rg4, base, PREC) : (!COLLECT && fix_need_lo(rg4, base, PREC)))
+        return;   // a head the other instantiation serves
     const int p0 = blockIdx.x * MC_ROWS;
     if (p0 >= N) return;
     const int p1 = min(N, p0 + MC_ROWS);
     const int32_t* oh = offsets + (size_t)h * (C + 1);
     const int ch = threadIdx.x % CPR, rg = threadIdx.x / CPR;
     const T* Xh = X + (size_t)h * N * D + ch * EPC;
-    const double scale = ldexp(1.0, shift);
+    const double sc = ldexp(1.0, base - fix_exp(rg4[0])), tc = ldexp(1.0, base);
+    unsigned long long* sums_lo = sums + (size_t)gridDim.y * C * D;
+    using R = typename RangeOf<T>::type;
+    R rgx;
     for (int k = threadIdx.x; k < p1 - p0; k += 256) s_idx[k] = perm[(size_t)h * N + p0 + k];
     // first cluster whose range ends after p0
     int lo_c = 0, hi_c = C - 1;
@@ -265,33 +292,32 @@ __global__ __launch_bounds__(256) void k_cluster_chunks(const T* __restrict__ X,
         const int a0 = max(oh[m], p0) - p0, a1 = min(oh[m + 1], p1) - p0;
         if (a1 <= a0) continue;
         if (chh && !chh[m]) continue;   // membership unchanged: its mean is unchanged
-        unsigned long long acc[EPC];
+        unsigned long long ah[EPC], al[EPC];
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[e] = 0;
+        for (int e = 0; e < EPC; ++e) ah[e] = al[e] = 0;
+        auto add_row = [&](const uint4 w) {
+            const T* v = (const T*)&w;
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) {
+                if (TWO) fix_add<T>(v[e], sc, tc, ah[e], al[e]);
+                else ah[e] += fix_hi<T>(v[e], sc);
+            }
+            if (COLLECT) { rgx.add_min(w.x); rgx.add_min(w.y); rgx.add_min(w.z); rgx.add_min(w.w); }
+        };
         int j = a0 + rg;
         for (; j + 3 * RPP < a1; j += 4 * RPP) {
             uint4 w[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) w[u] = *(const uint4*)(Xh + (size_t)s_idx[j + u * RPP] * D);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const T* v = (const T*)&w[u];
-#pragma unroll
-                for (int e = 0; e < EPC; ++e) acc[e] += fixed_bits<T>(v[e], scale);
-            }
+            for (int u = 0; u < 4; ++u) add_row(w[u]);
         }
-        for (; j < a1; j += RPP) {
-            const uint4 w0 = *(const uint4*)(Xh + (size_t)s_idx[j] * D);
-            const T* v0 = (const T*)&w0;
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) acc[e] += fixed_bits<T>(v0[e], scale);
-        }
-        // remove the offset carried by every accumulated row
+        for (; j < a1; j += RPP) add_row(*(const uint4*)(Xh + (size_t)s_idx[j] * D));
+        // remove the offset carried by every accumulated image; reduce the
+        // first word's row groups, then (if summed) the second word's
         const unsigned long long rows = (unsigned long long)((a1 - a0 - rg + RPP - 1) / RPP);
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[e] -= rows * kFixMagicBits;
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) s_sum[rg][ch * EPC + e] = (long long)acc[e];
+        for (int e = 0; e < EPC; ++e) s_sum[rg][ch * EPC + e] = (long long)(ah[e] - rows * kFixMagicBits);
         __syncthreads();
         if ((int)threadIdx.x < D) {
             long long tot = 0;
@@ -300,11 +326,49 @@ __global__ __launch_bounds__(256) void k_cluster_chunks(const T* __restrict__ X,
             atomicAdd(sums + ((size_t)h * C + m) * D + threadIdx.x, (unsigned long long)tot);
         }
         __syncthreads();
+        if (TWO) {
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) s_sum[rg][ch * EPC + e] = (long long)(al[e] - rows * kFixMagicBits);
+            __syncthreads();
+            if ((int)threadIdx.x < D) {
+                long long tot = 0;
+#pragma unroll
+                for (int g = 0; g < RPP; ++g) tot += s_sum[g][threadIdx.x];
+                atomicAdd(sums_lo + ((size_t)h * C + m) * D + threadIdx.x, (unsigned long long)tot);
+            }
+            __syncthreads();
+        }
     }
+    if (COLLECT) range_commit(0u, rgx.min_word(), rg4, true);
 }
 
-// centroid = (double)sum * 2^-shift / count for every non-empty cluster (one
-// wave per cluster); an empty cluster keeps its centroid (k-means) or becomes
+// After a collecting one-word pass: clears the sums of every head that needs
+// the second word (they are then summed again by the two-word kernel).
+__global__ __launch_bounds__(256) void k_clear_two_word_heads(const unsigned* __restrict__ range, int N,
+                                                              int prec, size_t per_head,
+                                                              unsigned long long* __restrict__ sums)
+{
+    const int h = blockIdx.y;
+    if (!fix_need_lo(range + kRangeStride * h, fix_base(N), prec)) return;
+    unsigned long long* p = sums + (size_t)h * per_head;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < per_head; i += (size_t)gridDim.x * 256) p[i] = 0ull;
+}
+
+// Value of the two fixed-point sums of one element: (hi + lo 2^-B) 2^-S,
+// rounded once in all but pathological cases (hi's fp64 rounding error is
+// carried into the small part).
+__device__ __forceinline__ double fix_value(unsigned long long hi, unsigned long long lo, double inv_s,
+                                            double inv_t)
+{
+    const long long hs = (long long)hi;
+    const double hd = (double)hs;
+    const long long hr = hs - (long long)hd;   // exact: |hr| <= 2^9
+    return (hd + fma((double)(long long)lo, inv_t, (double)hr)) * inv_s;
+}
+
+// centroid = (value of the fixed-point sums) / count for every non-empty
+// cluster (one wave per cluster); with err, also checks the head's range
+// (ERR_RANGE: values the exact sums cannot capture, or out of range); an empty cluster keeps its centroid (k-means) or becomes
 // zero (plain means).  Optionally writes an fp32 copy; with PLANES also the
 // bf16 hi/lo planes, ||c||^2 (fp32, fp64) and the split residual norm that the
 // MFMA screen of the next assignment needs.  Clears the sums for the next pass.
@@ -313,8 +377,10 @@ __global__ __launch_bounds__(256) void k_cluster_chunks(const T* __restrict__ X,
 // a recomputed centroid differs from its previous value in any bit.
 template <int D, bool PLANES>
 __global__ __launch_bounds__(256) void k_cluster_finalize(
-    const int32_t* __restrict__ counts, int C, int shift, int zero_empty,
-    unsigned long long* __restrict__ sums, double* __restrict__ cent64, float* __restrict__ cent_out,
+    const int32_t* __restrict__ counts, int C, int N, const unsigned* __restrict__ range, int prec,
+    int collect, int* __restrict__ err, int zero_empty, unsigned long long* __restrict__ sums,
+    double* __restrict__ cent64,
+    float* __restrict__ cent_out,
     bf16* __restrict__ hi, bf16* __restrict__ lo, float* __restrict__ cn32,
     double* __restrict__ cn64, float* __restrict__ resid, const int* __restrict__ changed,
     int* __restrict__ moved)
@@ -322,7 +388,13 @@ __global__ __launch_bounds__(256) void k_cluster_finalize(
     constexpr int EPL = D / 64;
     const int h = blockIdx.y;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const double inv_scale = ldexp(1.0, -shift);
+    const int base = fix_base(N);
+    const double inv_s = ldexp(1.0, fix_exp(range[kRangeStride * h]) - base), inv_t = ldexp(1.0, -base);
+    unsigned long long* sums_lo = sums + (size_t)gridDim.y * C * D;
+    const bool need_lo = fix_need_lo(range + kRangeStride * h, base, prec);
+    // the head's range is complete here: report values the sums cannot capture
+    if (err && blockIdx.x == 0 && threadIdx.x == 0 && !fix_exact(range + kRangeStride * h, base, prec))
+        atomicOr(err, ERR_RANGE);
     for (int m = blockIdx.x * 4 + wave; m < C; m += gridDim.x * 4) {
         const size_t row = (size_t)h * C + m;
         if (changed && !changed[row]) continue;   // wave-uniform
@@ -334,10 +406,11 @@ __global__ __launch_bounds__(256) void k_cluster_finalize(
             const size_t i = row * D + lane * EPL + e;
             double c;
             if (n > 0) {
-                c = ((double)(long long)sums[i] * inv_scale) / (double)n;
+                c = fix_value(sums[i], need_lo ? sums_lo[i] : 0ull, inv_s, inv_t) / (double)n;
                 mv |= c != cent64[i];
                 cent64[i] = c;
                 sums[i] = 0ull;
+                if (need_lo) sums_lo[i] = 0ull;
             } else if (zero_empty) {
                 c = 0.0;
                 cent64[i] = c;
@@ -463,7 +536,9 @@ __global__ __launch_bounds__(256) void k_plane_stats(int C, const double* __rest
 
 // Stable scatter: position = offset of the label + tokens of that label in
 // earlier tiles + earlier tokens of that label in this tile.  Copies the rows
-// of X (and V) to their reordered positions.
+// of X (and V) to their reordered positions and records the largest magnitude
+// of V and, when range_x is given, of X.
+template <typename T>
 __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ labels, int N, int C,
                                                  int ntiles, const int* __restrict__ hist,
                                                  const int32_t* __restrict__ offsets,
@@ -471,7 +546,9 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ lab
                                                  int32_t* __restrict__ inv_perm,
                                                  const uint4* __restrict__ X, uint4* __restrict__ Xp,
                                                  const uint4* __restrict__ V, uint4* __restrict__ Vp,
-                                                 int row_chunks)
+                                                 int row_chunks,
+                                                 unsigned* __restrict__ range_x,
+                                                 unsigned* __restrict__ range_v)
 {
     __shared__ int s_lab[kTile];
     __shared__ int s_pos[kTile];
@@ -496,15 +573,25 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ lab
     __syncthreads();
     if (!X) return;
     const int rows = min(kTile, N - tile * kTile);
+    using R = typename RangeOf<T>::type;
+    R rx, rv;
     for (int k = threadIdx.x; k < rows * row_chunks; k += 256) {
         const int r = k / row_chunks, ch = k - r * row_chunks;
         const int p = s_pos[r];
         if (p < 0) continue;
         const size_t src = ((size_t)h * N + tile * kTile + r) * row_chunks + ch;
         const size_t dst = ((size_t)h * N + p) * row_chunks + ch;
-        Xp[dst] = X[src];
-        if (V) Vp[dst] = V[src];
+        const uint4 xw = X[src];
+        Xp[dst] = xw;
+        if (range_x) { rx.add_max(xw.x); rx.add_max(xw.y); rx.add_max(xw.z); rx.add_max(xw.w); }
+        if (V) {
+            const uint4 vw = V[src];
+            Vp[dst] = vw;
+            rv.add_max(vw.x); rv.add_max(vw.y); rv.add_max(vw.z); rv.add_max(vw.w);
+        }
     }
+    if (range_x) range_commit(rx.max_word(), 0u, range_x + kRangeStride * h, false);
+    if (V) range_commit(rv.max_word(), 0u, range_v + kRangeStride * h, false);
 }
 
 // ----------------------------------------------------------------------------- driver
@@ -515,7 +602,7 @@ static hipError_t run_cluster(const ClusterArgs& a, hipStream_t st)
 {
     const Layout& L = *a.L;
     char* s = a.scratch;
-    int* err = (int*)(s + L.cl_err);
+    int* err = a.err;
     double* cent64 = (double*)(s + L.cl_cent64);
     int* hist = (int*)(s + L.cl_hist);
     int32_t* pwork = (int32_t*)(s + L.cl_perm);
@@ -525,18 +612,41 @@ static hipError_t run_cluster(const ClusterArgs& a, hipStream_t st)
     const dim3 gtiles(ntiles, H), gcent(C, H), gcols((C + HC_L - 1) / HC_L, H);
     const bool mfma = assign_mfma_supported(a);
     const KmPlanes P = km_planes(a);
-    unsigned long long* sums = (unsigned long long*)(s + L.cl_sums);
+    unsigned long long* sums = (unsigned long long*)(s + L.cl_sums);   // [2][H, C, d]
     float* resid = (float*)(s + L.cl_resid);
+    // per-head range words: [h][0..1] of X, [h][2..3] of V, one line per head (see fix_exact)
+    unsigned* range = (unsigned*)(s + L.cl_range);
+    unsigned* range_x = range;
+    unsigned* range_v = range + 2;
     const dim3 gchunks((N + MC_ROWS - 1) / MC_ROWS, H), gfin((C + 3) / 4 < 64 ? (C + 3) / 4 : 64, H);
-    zero_words(sums, (size_t)H * C * D * 8, st);
+    zero_words(sums, (size_t)2 * H * C * D * 8, st);
+    zero_words(range, (size_t)H * kRangeStride * 4, st);
     // plain mean pass (no planes)
-    auto mean_pass = [&](const T* src, const int32_t* order, int zero_empty, float* out) {
-        hipLaunchKernelGGL((k_cluster_chunks<T, D>), gchunks, dim3(256), 0, st, src, order, a.offsets,
-                           N, C, a.shift, sums, (const int*)nullptr);
-        hipLaunchKernelGGL((k_cluster_finalize<D, false>), gfin, dim3(256), 0, st, a.counts, C,
-                           a.shift, zero_empty, sums, cent64, out, (bf16*)nullptr, (bf16*)nullptr,
-                           (float*)nullptr, (double*)nullptr, (float*)nullptr, (const int*)nullptr,
-                           (int*)nullptr);
+    constexpr int kPrec = sizeof(T) == 2 ? 8 : 24;
+    // Exact sums of the rows of src in `order` (bucketed by label): the
+    // one-word instantiation, then (collect) the clearing of heads that need
+    // two words, then the two-word instantiation for those heads.
+    auto chunk_pass = [&](const T* src, unsigned* rg, const int32_t* order, const int* chg, int collect) {
+        if (collect) {
+            hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_ONE_COLLECT>), gchunks, dim3(256), 0, st, src, order,
+                               a.offsets, N, C, rg, sums, chg);
+            hipLaunchKernelGGL(k_clear_two_word_heads, dim3(16, H), dim3(256), 0, st, rg, N, kPrec,
+                               (size_t)C * D, sums);
+        } else {
+            hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_ONE>), gchunks, dim3(256), 0, st, src, order,
+                               a.offsets, N, C, rg, sums, chg);
+        }
+        hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_TWO>), gchunks, dim3(256), 0, st, src, order,
+                           a.offsets, N, C, rg, sums, chg);
+    };
+    // plain mean pass (no planes); checks the range
+    auto mean_pass = [&](const T* src, unsigned* rg, const int32_t* order, int collect, int zero_empty,
+                         float* out) {
+        chunk_pass(src, rg, order, (const int*)nullptr, collect);
+        hipLaunchKernelGGL((k_cluster_finalize<D, false>), gfin, dim3(256), 0, st, a.counts, C, N,
+                           rg, kPrec, collect, err, zero_empty, sums, cent64, out, (bf16*)nullptr,
+                           (bf16*)nullptr, (float*)nullptr, (double*)nullptr, (float*)nullptr,
+                           (const int*)nullptr, (int*)nullptr);
     };
 
     // counting-sort front half: tile histograms, per-label tile prefixes, counts, offsets
@@ -570,11 +680,11 @@ static hipError_t run_cluster(const ClusterArgs& a, hipStream_t st)
         }
         for (int it = 0; it < a.iters; ++it) {
             if (mfma) {
-                hipError_t e = launch_assign_mfma(a, cent64, P, it > 0, st);
+                hipError_t e = launch_assign_mfma(a, cent64, P, it > 0, it == 0 ? range_x : nullptr, st);
                 if (e != hipSuccess) return e;
             } else {
                 hipLaunchKernelGGL((k_assign_exact<T, D>), dim3((N + 255) / 256, H), dim3(256), 0,
-                                   st, X, cent64, N, C, a.labels);
+                                   st, X, cent64, N, C, a.labels, it == 0 ? range_x : nullptr);
             }
             if (it == a.iters - 1) break;
             // update: unstable bucket order + exact per-cluster means (and next planes)
@@ -586,31 +696,37 @@ static hipError_t run_cluster(const ClusterArgs& a, hipStream_t st)
                                ntiles, hist, a.offsets, pwork);
             if (mfma && D == 128) {
                 const int* chg = it > 0 ? changed : nullptr;
-                hipLaunchKernelGGL((k_cluster_chunks<T, D>), gchunks, dim3(256), 0, st, X, pwork,
-                                   a.offsets, N, C, a.shift, sums, chg);
+                // the first update reads every row: it also records the smallest magnitude
+                chunk_pass(X, range_x, pwork, chg, it == 0 ? 1 : 0);
                 hipLaunchKernelGGL((k_cluster_finalize<D, D == 128>), gfin, dim3(256), 0, st, a.counts,
-                                   C, a.shift, 0, sums, cent64, (float*)nullptr, P.hi, P.lo, P.cn32,
-                                   P.cn64, resid, chg, moved);
+                                   C, N, range_x, kPrec, it == 0 ? 1 : 0, it == 0 ? err : nullptr, 0, sums,
+                                   cent64, (float*)nullptr, P.hi, P.lo, P.cn32, P.cn64, resid, chg, moved);
                 hipLaunchKernelGGL(k_plane_stats, dim3(H), dim3(256), 0, st, C, P.cn64, resid,
                                    P.stats);
                 hipLaunchKernelGGL(k_moved_list, dim3(H), dim3(1024), 0, st, C, changed, moved,
                                    P.mlist, P.mpos, P.mcount);
             } else {
-                mean_pass(X, pwork, 0, (float*)nullptr);
+                // the first update reads every row: it also records the smallest magnitude
+                mean_pass(X, range_x, pwork, it == 0 ? 1 : 0, 0, (float*)nullptr);
             }
         }
     }
 
     // Final reorder (stable counting sort), rows gathered, means of the final labels.
     sort_front(nullptr, nullptr);
+    // The scatter records the largest magnitude of V, and of X unless the k-means
+    // has its range (its first assignment the largest, its first update the
+    // smallest magnitude); a mean pass that collects records the smallest.
     const int row_chunks = (int)(D * sizeof(T) / 16);
-    hipLaunchKernelGGL(k_scatter, gtiles, dim3(256), 0, st, a.labels, N, C, ntiles, hist, a.offsets,
+    const bool given = (a.flags & SVGEAR_LABELS_GIVEN) != 0;
+    const bool x_known = !given && a.iters >= 2;
+    hipLaunchKernelGGL((k_scatter<T>), gtiles, dim3(256), 0, st, a.labels, N, C, ntiles, hist, a.offsets,
                        a.perm, a.inv_perm, (const uint4*)a.X, (uint4*)a.Xp, (const uint4*)a.V,
-                       (uint4*)a.Vp, row_chunks);
-    mean_pass(X, a.perm, (a.flags & SVGEAR_LABELS_GIVEN) ? 1 : 0, a.cent);
+                       (uint4*)a.Vp, row_chunks, x_known ? nullptr : range_x, range_v);
+    mean_pass(X, range_x, a.perm, x_known ? 0 : 1, given ? 1 : 0, a.cent);
     // V-bar: mean of V over the key clusters (zero for an empty cluster).  cent64
     // is no longer needed and serves as scratch.
-    if (a.side == 1) mean_pass((const T*)a.V, a.perm, 1, a.vbar);
+    if (a.side == 1) mean_pass((const T*)a.V, range_v, a.perm, 1, 1, a.vbar);
     return hipGetLastError();
 }
 

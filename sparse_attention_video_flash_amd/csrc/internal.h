@@ -36,20 +36,158 @@ template <typename T> __device__ __forceinline__ float to_f32(T x);
 template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ float to_f32<bf16>(bf16 x) { return bf16_to_f32(x); }
 
-// Exact fixed-point image of an input value.  x * 2^S is formed exactly in
-// fp64 and added to 1.5 * 2^52, which rounds it to the nearest integer (an exact
-// operation whenever x is a multiple of 2^-S, i.e. every input of magnitude at
-// least 2^(-S+7) for bf16 or 2^(-S+23) for fp32, and |x| < 2^(51 - S)); the
-// integer is read from the low bits.  Accumulating the raw bit patterns and
-// subtracting count * bits(1.5 * 2^52) once at the end gives the sum of the
-// integers modulo 2^64, which is the exact sum while it fits in 63 bits.
+// Exact centroid sums.  For a head whose largest input magnitude is below 2^E,
+// every value is scaled by 2^S (S = B - E, B = min(51, 62 - ceil(log2(N+1))))
+// and split exactly into the nearest integer a and the remainder r = x 2^S - a
+// (|r| <= 1/2); a and r 2^B are each turned into a 64-bit integer by the fp64
+// magic-number add (exact: |a| < 2^51 and |r 2^B| < 2^51).  The second integer
+// is exact whenever x is a multiple of 2^-(S+B), which holds for every value
+// whose unit in the last place is at least that (checked once per head from the
+// smallest non-zero magnitude; see fix_exact).  Both integers are summed
+// modulo 2^64 in any order; the sums stay below 2^62 in magnitude, so they are
+// the exact sums of the images, and the total is (hi + lo 2^-B) 2^-S.
 constexpr double kFixMagic = 6755399441055744.0;               // 1.5 * 2^52
 constexpr unsigned long long kFixMagicBits = 0x4338000000000000ull;
-template <typename T>
-__device__ __forceinline__ unsigned long long fixed_bits(T x, double scale)
+constexpr int kFixMaxExp = 56;   // supported inputs: finite with |x| < 2^56
+
+// B for N tokens (host and device).
+__host__ __device__ __forceinline__ int fix_base(int N)
 {
-    return (unsigned long long)__double_as_longlong(fma((double)to_f32<T>(x), scale, kFixMagic));
+    int lg = 0;
+    while (lg < 31 && (1 << lg) <= N) ++lg;   // N < 2^lg
+    return (62 - lg) < 51 ? (62 - lg) : 51;
 }
+
+// Smallest E with |x| < 2^E from the largest magnitude's fp32 bits (0 for an
+// all-zero head; capped at kFixMaxExp, which fix_exact reports as out of range).
+__device__ __forceinline__ int fix_exp(unsigned maxbits)
+{
+    if (maxbits == 0u) return 0;
+    const int ef = (int)(maxbits >> 23);
+    const int e = ef == 0 ? -126 : ef - 126;
+    return e > kFixMaxExp ? kFixMaxExp : e;
+}
+
+// Per-head range words (fp32 bit patterns of magnitudes, updated with
+// atomicMax on zero-initialised memory): w[0] = largest |x|, w[1] = ~(smallest
+// non-zero |x| - 1) (0 while no non-zero value was seen).
+// Whether the split above is exact for every value of the head, and the head
+// is inside the supported range (finite, |x| < 2^kFixMaxExp).  prec: 8 (bf16)
+// or 24 (fp32) significant bits.
+__device__ __forceinline__ bool fix_exact(const unsigned* w, int base, int prec)
+{
+    const unsigned mx = w[0];
+    if (mx >= 0x7F800000u) return false;                       // inf or NaN
+    if (mx != 0u && (int)(mx >> 23) - 127 >= kFixMaxExp) return false;
+    if (w[1] == 0u) return true;                               // all zeros
+    const unsigned mn = ~w[1] + 1u;                            // smallest non-zero |x|
+    const int ef = (int)(mn >> 23);
+    const int ulp_e = (ef == 0 ? -126 : ef - 127) - (prec - 1);
+    const int S = base - fix_exp(mx);
+    return ulp_e >= -(S + base);
+}
+
+// The first integer image alone (magic-offset bits), for a head whose values
+// all have a unit in the last place of at least 2^-S.
+template <typename T>
+__device__ __forceinline__ unsigned long long fix_hi(T x, double s)
+{
+    return (unsigned long long)__double_as_longlong(fma((double)to_f32<T>(x), s, kFixMagic));
+}
+
+// Adds the two integer images of x (scale s = 2^S, t = 2^B) to hi and lo.
+template <typename T>
+__device__ __forceinline__ void fix_add(T x, double s, double t, unsigned long long& hi,
+                                        unsigned long long& lo)
+{
+    const double xv = (double)to_f32<T>(x);
+    const double a = fma(xv, s, kFixMagic);          // magic + nearest integer of x 2^S
+    const double r = fma(xv, s, kFixMagic - a);      // x 2^S - that integer, exactly
+    hi += (unsigned long long)__double_as_longlong(a);
+    lo += (unsigned long long)__double_as_longlong(fma(r, t, kFixMagic));
+}
+
+// Whether a head needs the remainder word at all: some non-zero value's unit in
+// the last place lies below 2^-S (otherwise every image is exact in the first
+// word and the second stays zero).  Needs the complete range words.
+__device__ __forceinline__ bool fix_need_lo(const unsigned* w, int base, int prec)
+{
+    if (w[1] == 0u) return false;
+    const unsigned mn = ~w[1] + 1u;
+    const int ef = (int)(mn >> 23);
+    const int ulp_e = (ef == 0 ? -126 : ef - 127) - (prec - 1);
+    return ulp_e < fix_exp(w[0]) - base;
+}
+
+// Running range of bf16 data, two values per 32-bit word with packed 16-bit
+// integer max/min: mx = largest magnitude, mn = smallest (magnitude - 1), so a
+// zero (0xFFFF after the wrap) never wins the minimum.
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+struct RangeBf16 {
+    u16x2_t mx = {0, 0}, mn = {0xFFFF, 0xFFFF};
+    __device__ __forceinline__ void add_max(unsigned w)
+    {
+        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2_t, w & 0x7FFF7FFFu));
+    }
+    __device__ __forceinline__ void add_min(unsigned w)
+    {
+        mn = __builtin_elementwise_min(mn, __builtin_bit_cast(u16x2_t, w & 0x7FFF7FFFu) - u16x2_t{1, 1});
+    }
+    __device__ __forceinline__ void add(unsigned w)
+    {
+        const u16x2_t a = __builtin_bit_cast(u16x2_t, w & 0x7FFF7FFFu);
+        mx = __builtin_elementwise_max(mx, a);
+        mn = __builtin_elementwise_min(mn, a - u16x2_t{1, 1});
+    }
+    // fp32-bit range words (see fix_exact)
+    __device__ __forceinline__ unsigned max_word() const { return (unsigned)max(mx[0], mx[1]) << 16; }
+    __device__ __forceinline__ unsigned min_word() const
+    {
+        const unsigned m = min(mn[0], mn[1]);
+        return m == 0xFFFFu ? 0u : ~(((m + 1u) << 16) - 1u);
+    }
+};
+// The same for fp32 data.
+struct RangeF32 {
+    unsigned mx = 0u, mn = 0u;
+    __device__ __forceinline__ void add_max(unsigned w) { mx = max(mx, w & 0x7FFFFFFFu); }
+    __device__ __forceinline__ void add_min(unsigned w) { mn = max(mn, ~((w & 0x7FFFFFFFu) - 1u)); }
+    __device__ __forceinline__ void add(unsigned w)
+    {
+        const unsigned a = w & 0x7FFFFFFFu;
+        mx = max(mx, a);
+        mn = max(mn, ~(a - 1u));
+    }
+    __device__ __forceinline__ unsigned max_word() const { return mx; }
+    __device__ __forceinline__ unsigned min_word() const { return mn; }
+};
+template <typename T> struct RangeOf;
+template <> struct RangeOf<bf16> { using type = RangeBf16; };
+template <> struct RangeOf<float> { using type = RangeF32; };
+
+// Wave maxima of both words, then at most one atomic per wave and word (the
+// minimum word only when the caller collected it).  The word is read first and
+// the atomic issued only if it would raise it: once the first waves of a pass
+// have recorded the head's extremes, the rest issue none (thousands of waves
+// per head would otherwise serialise on the word in L2).
+__device__ __forceinline__ void range_max_word(unsigned* w, unsigned v)
+{
+    if (v > __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(w, v);
+}
+__device__ __forceinline__ void range_commit(unsigned mx, unsigned mn, unsigned* w, bool with_min)
+{
+    for (int o = 32; o >= 1; o >>= 1) {
+        mx = max(mx, (unsigned)__shfl_xor((int)mx, o));
+        if (with_min) mn = max(mn, (unsigned)__shfl_xor((int)mn, o));
+    }
+    if ((threadIdx.x & 63) == 0) {
+        range_max_word(w, mx);
+        if (with_min) range_max_word(w + 1, mn);
+    }
+}
+
+// Per-head range words: one 128-byte line per head ([0..1] of X, [2..3] of V).
+constexpr int kRangeStride = 32;
 
 // One probe term in log form: e = e^{2s} [em^2 P + 2 em Qd + R] with
 // s = sbar - D, em = expm1(D), P = ||vbar||^2, Qd = vbar.(vbar - v),
@@ -78,16 +216,8 @@ constexpr int kTile = 256;          // tokens per counting-sort / run-length til
 constexpr int kMaxC = 4096;         // largest cluster count
 constexpr int kAttnRows = 256;      // query rows per attention tile (bf16, d = 128 kernel)
 constexpr int kXcd = 8;             // XCDs per device: attention work queues
+constexpr int kAttnSlots = 256;     // attention workgroups at most (one per CU), each with a row-list slot
 constexpr int kMaxN = 1 << 20;      // largest token count
-
-// Fixed-point scale 2^S of the exact centroid sums: |x| < 2^8 and N < 2^lgN give
-// |sum| < 2^(8 + lgN + S) <= 2^62.
-inline int fixed_point_shift(int N)
-{
-    int lg = 0;
-    while ((1 << lg) <= N) ++lg;   // N < 2^lg
-    return 62 - 8 - lg;
-}
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -101,19 +231,18 @@ struct Layout {
     // forward intermediates
     size_t labels_q, qbar, counts_q, offsets_q, perm_q, inv_perm_q, Qp;
     size_t labels_k, kbar, vbar, counts_k, offsets_k, perm_k, inv_perm_k, Kp, Vp;
-    size_t log_ratio, mask, sel_cost;
+    size_t log_ratio, mask, sel_cost, errs;
     size_t scratch;  // start of the per-stage scratch
     // cluster scratch (relative to scratch)
-    size_t cl_err, cl_cent64, cl_hi, cl_lo, cl_cnorm, cl_cn64, cl_stats, cl_flag, cl_nflag,
-        cl_hist, cl_perm, cl_sums, cl_resid, cl_labprev, cl_bounds, cl_changed, cl_moved,
+    size_t cl_cent64, cl_hi, cl_lo, cl_cnorm, cl_cn64, cl_stats, cl_flag, cl_nflag,
+        cl_hist, cl_perm, cl_sums, cl_range, cl_resid, cl_labprev, cl_bounds, cl_changed, cl_moved,
         cl_mlist, cl_mpos, cl_mcount;
     size_t cl_end;
     // probe scratch (relative to scratch)
-    size_t pr_err, pr_qplanes, pr_sbar, pr_keys, pr_pg;
+    size_t pr_sbar, pr_keys, pr_pg;
     size_t pr_end;
     // attention scratch (relative to scratch)
-    size_t at_err, at_kvplanes, at_logm, at_tiles, at_segs, at_nsegs, at_nkeys, at_comp, at_ncomp,
-        at_rowmap, at_queue;
+    size_t at_kvplanes, at_logm, at_tiles, at_segs, at_cinfo, at_comp, at_rows, at_queue;
     size_t at_end;
     size_t scratch2;  // second cluster scratch (absolute offset)
     size_t total;
@@ -125,7 +254,7 @@ SVG_HIDDEN size_t elem_bytes(int dtype);
 // ----------------------------------------------------------------------------- launchers
 
 struct ClusterArgs {
-    int H, N, d, C, iters, dtype, side, flags, shift;
+    int H, N, d, C, iters, dtype, side, flags;
     const void* X;
     const void* V;
     const int32_t* init;
@@ -139,6 +268,7 @@ struct ClusterArgs {
     void* Xp;
     void* Vp;
     char* scratch;      // cluster scratch base
+    int* err;           // device error word (ERR_*), cleared by the caller
     const Layout* L;
 };
 SVG_HIDDEN hipError_t launch_cluster(const ClusterArgs& a, hipStream_t st);
@@ -162,8 +292,10 @@ struct KmPlanes {
 SVG_HIDDEN KmPlanes km_planes(const ClusterArgs& a);
 SVG_HIDDEN hipError_t launch_km_prep(const ClusterArgs& a, const double* cent64, const KmPlanes& P,
                                      hipStream_t st);
+// range: when non-NULL, the screen also records the per-head range words of X.
 SVG_HIDDEN hipError_t launch_assign_mfma(const ClusterArgs& a, const double* cent64,
-                                         const KmPlanes& P, bool partial, hipStream_t st);
+                                         const KmPlanes& P, bool partial, unsigned* range,
+                                         hipStream_t st);
 SVG_HIDDEN bool assign_mfma_supported(const ClusterArgs& a);
 
 struct ProbeArgs {

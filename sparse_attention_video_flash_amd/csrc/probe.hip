@@ -15,7 +15,8 @@
 namespace svg {
 
 // Per key (reordered order): (vbar_g.delta_j, ||delta_j||^2), and per key
-// cluster ||vbar_g||^2.  One block per key cluster; 16 lanes per key row.
+// cluster ||vbar_g||^2, for the generic probe (the MFMA probe forms them while
+// it stages its keys).  One block per key cluster; 16 lanes per key row.
 // With logit_only the values drop out: (0, 0) per key and 1 per cluster, which
 // turns the bracket into expm1(D)^2, i.e. e = (e^sbar - e^s)^2.
 template <typename T, int D>
@@ -228,8 +229,7 @@ __global__ __launch_bounds__(256) void k_probe_generic(
     }
 }
 
-SVG_HIDDEN hipError_t launch_probe_mfma(const ProbeArgs& a, const float* sbar, const float2* keys,
-                                        const float* pg, hipStream_t st);
+SVG_HIDDEN hipError_t launch_probe_mfma(const ProbeArgs& a, const float* sbar, hipStream_t st);
 SVG_HIDDEN bool probe_mfma_supported(const ProbeArgs& a);
 
 template <typename T, int D>
@@ -247,11 +247,12 @@ static hipError_t run_probe(const ProbeArgs& a, hipStream_t st)
                            a.counts_k, a.Cq, a.Ck, a.log_ratio);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((k_key_scalars<T, D>), dim3(a.Ck, a.H), dim3(256), 0, st, (const T*)a.Vp,
-                       a.vbar, a.offsets_k, a.Nk, a.Ck, keys, pg, (a.flags & SVGEAR_PROBE_LOGIT) ? 1 : 0);
     hipLaunchKernelGGL((k_sbar<D>), dim3((a.Cq + 3) / 4, (a.Ck + 63) / 64, a.H), dim3(256), 0, st, a.qbar,
                        a.kbar, a.Cq, a.Ck, 1.0 / sqrt((double)D), sbar);
-    if (probe_mfma_supported(a)) return launch_probe_mfma(a, sbar, keys, pg, st);
+    // the MFMA probe forms its per-key value terms itself (one read of K_p and V_p)
+    if (probe_mfma_supported(a)) return launch_probe_mfma(a, sbar, st);
+    hipLaunchKernelGGL((k_key_scalars<T, D>), dim3(a.Ck, a.H), dim3(256), 0, st, (const T*)a.Vp,
+                       a.vbar, a.offsets_k, a.Nk, a.Ck, keys, pg, (a.flags & SVGEAR_PROBE_LOGIT) ? 1 : 0);
     hipLaunchKernelGGL((k_probe_generic<T, D>), dim3(a.Ck, a.H), dim3(256), 0, st, a.qbar,
                        a.counts_q, (const T*)a.Kp, a.kbar, sbar, keys, pg, a.offsets_k, a.Nk, a.Cq, a.Ck,
                        tau, a.log_ratio, (a.flags & SVGEAR_DEBUG_EPS) ? a.log_eps2 : nullptr);

@@ -13,7 +13,7 @@ from typing import Dict, Optional
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libsvgear.so")
 
-OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_WORKSPACE, E_RHO, E_HIP, E_ARG = 0, -1, -2, -3, -4, -5, -6, -7, -8
+OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_WORKSPACE, E_RHO, E_HIP, E_ARG, E_RANGE = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 F32, BF16 = 0, 1
 LABELS_GIVEN, DEBUG_EPS, DEBUG_SYNC, PROBE_LOGIT, PROBE_SCORE = 1, 2, 4, 8, 16
 
@@ -62,7 +62,7 @@ def load():
         L.svgear_route_rows.argtypes = [sp, f64, vp, vp, vp, vp, vp, vp, sz, vp]
         L.svgear_attention.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.svgear_forward.argtypes = [sp, f64, vp, vp, vp, vp, vp, vp, ctypes.POINTER(Intermediates),
-                                     vp, sz, vp]
+                                     i32, vp, sz, vp]
         L.svgear_status_string.argtypes = [i32]
         L.svgear_status_string.restype = ctypes.c_char_p
         L.svgear_version.argtypes = []
@@ -163,13 +163,13 @@ def attention(shape: Shape, Qp, offsets_q, perm_q, Kp, Vp, kbar, vbar, counts_k,
 
 
 def forward(shape: Shape, rho: float, Q, K, V, init_q, init_k, O, ws, intermediates: Optional[Dict] = None,
-            stream=None):
+            stream=None, flags=0):
     im = None
     if intermediates:
         im = Intermediates(**{k: _ptr(v) for k, v in intermediates.items()})
     rc = load().svgear_forward(ctypes.byref(shape), float(rho), _ptr(Q), _ptr(K), _ptr(V), _ptr(init_q),
                                _ptr(init_k), _ptr(O), ctypes.byref(im) if im is not None else None,
-                               _ptr(ws), ws.numel(), _stream(stream))
+                               int(flags), _ptr(ws), ws.numel(), _stream(stream))
     _check(rc, "svgear_forward")
 
 

@@ -23,12 +23,12 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(sv.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.svgear_version() == 10000
+    assert lib.svgear_version() == 20000
 
 
 def test_status_strings():
     assert sv.status_string(0) == "ok"
-    for c in range(-8, 0):
+    for c in range(-9, 0):
         assert sv.status_string(c) != "unknown status"
 
 
@@ -103,12 +103,16 @@ def test_probe_route_attention_forward_validation():
                               None) == sv.E_NULL
     assert L.svgear_attention(r(s), FAKE, FAKE, FAKE, FAKE, FAKE + 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big,
                               None) == sv.E_ALIGN
-    assert L.svgear_forward(r(s), 2.0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, big, None) == sv.E_RHO
-    assert L.svgear_forward(r(s), 0.2, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, FAKE, big, None) == sv.E_NULL
-    assert L.svgear_forward(r(s), 0.2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, big - 256, None) \
+    assert L.svgear_forward(r(s), 2.0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, big, None) == sv.E_RHO
+    assert L.svgear_forward(r(s), 0.2, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, 0, FAKE, big, None) == sv.E_NULL
+    assert L.svgear_forward(r(s), 0.2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, big - 256, None) \
         == sv.E_WORKSPACE
+    # forward takes SVGEAR_DEBUG_SYNC only
+    for flags in (sv.LABELS_GIVEN, sv.DEBUG_EPS, sv.PROBE_LOGIT, 1 << 10):
+        assert L.svgear_forward(r(s), 0.2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, flags, FAKE, big, None) \
+            == sv.E_ARG
     bad = _shape(d=32)
-    assert L.svgear_forward(r(bad), 0.2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, big, None) == sv.E_SHAPE
+    assert L.svgear_forward(r(bad), 0.2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, big, None) == sv.E_SHAPE
 
 
 def test_route_rows_and_probe_variant_validation():
@@ -125,3 +129,19 @@ def test_route_rows_and_probe_variant_validation():
     for flags in (sv.PROBE_SCORE | sv.PROBE_LOGIT, sv.PROBE_SCORE | sv.DEBUG_EPS, 32):
         assert L.svgear_probe(r(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, flags, FAKE, FAKE, FAKE, big,
                               None) == sv.E_ARG
+
+
+@pytest.mark.parametrize("H", [1, 40])
+def test_workspace_at_the_maximum_shape_scales_with_the_inputs(H):
+    """At the largest declared shape (N = 2^20 tokens, 4096 clusters per side)
+    the workspace stays within twice the bytes of Q, K and V themselves (it
+    holds their reordered copies) plus one routed-key row list of N entries per
+    attention workgroup (256), so the declared limits fit one device."""
+    N, C, d = 1 << 20, 4096, 128
+    for dtype, eb in ((sv.BF16, 2), (sv.F32, 4)):
+        s = sv.make_shape(H, N, N, d, C, C, 10, dtype)
+        inputs = 3 * H * N * d * eb
+        assert sv.workspace_bytes(s) <= 2 * inputs + 256 * N * 4
+    # and at the benchmark shape (40 heads x 75,600 tokens, 100 / 500 clusters)
+    s = sv.make_shape(40, 75600, 75600, 128, 100, 500, 10, sv.BF16)
+    assert sv.workspace_bytes(s) <= 3 * 2 ** 30

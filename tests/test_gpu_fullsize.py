@@ -9,7 +9,9 @@ defined row by row, so the sampled rows are exact).  Bars: labels, counts,
 offsets and permutations bit-exact; centroids equal to the fp32 rounding of the
 oracle's fp64 means; ratios within 1e-3 relative (with the floor of the small
 parity tests); mask bit-exact except blocks within 1e-5 relative of the
-threshold; output rel-L2 <= 5e-3 and max-abs <= 2e-2 (bf16)."""
+threshold; output rel-L2 <= 5e-3 and max-abs <= 2e-2 (bf16, scaled by max|o|/4
+above 4) on every sampled row: a row whose query cluster's mask row flipped
+near the threshold is compared with the oracle evaluated with that mask."""
 from __future__ import annotations
 
 import os
@@ -22,7 +24,8 @@ import oracle
 from sparse_attention_video_flash_amd import svgear as sv
 from sparse_attention_video_flash_amd.inputs import WORKLOADS, generate_head
 
-from gpu_common import check_output, log, log_close, near_threshold_ok, probe_log_floors, shape_of, torch_gpu
+from gpu_common import (check_output, log, log_close, near_threshold_ok, probe_log_floors, reference_rows,
+                        shape_of, torch_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -110,11 +113,10 @@ def _check_head(w, parts, got, rho, rows, ref_cluster=None):
     if nd == 0:
         assert int(got["sel_cost"]) == int(used)
     assert int(got["sel_cost"]) <= int(oracle.budget(rho, w.N, w.N))
-    # step 4: output on the sampled rows whose cluster's mask row agrees
-    same = (got["mask"] == mask).all(axis=1)[lq[rows]]
-    O = oracle.hybrid(q, k, v, lq, lk, kbar, vbar, ck, mask, rows[same])
-    check_output(got["O"][same], O, w.dtype, "rho=%g, %d sampled rows" % (rho, int(same.sum())))
-    assert same.mean() > 0.9
+    # step 4: output on every sampled row (rows of a query cluster whose mask row
+    # flipped near the threshold against the oracle run with the library's mask)
+    O, nflip = reference_rows(q, k, v, lq, lk, kbar, vbar, ck, mask, got["mask"], rows)
+    check_output(got["O"], O, w.dtype, "rho=%g, %d sampled rows (%d on flipped rows)" % (rho, len(rows), nflip))
     log("  mask differs on %d near-threshold blocks; max ratio dev %.2e" % (nd, float(dev.max())))
     return ref_cluster
 

@@ -7,8 +7,9 @@ the per-stage entry points; the oracle does the same steps in fp64.
 Bars: ratios as in the probe tests (the score ratio to 1e-4 in ln r); the mask
 exact except blocks near the selection threshold (1e-5 relative; 3e-3 for the
 logit-only ratio and 1e-4 for the score ratio, as wide as their ratio bars); selected cost within the budget;
-output within the dtype's tolerance on the sampled rows whose mask row agrees
-with the oracle's (at least 90% of them)."""
+output within the dtype's tolerance on every sampled row (against the oracle
+run with the library's mask on query clusters where a near-threshold block
+flipped)."""
 import numpy as np
 import pytest
 
@@ -16,7 +17,7 @@ import oracle
 from sparse_attention_video_flash_amd import svgear as sv
 from sparse_attention_video_flash_amd.inputs import WORKLOADS
 
-from gpu_common import RAGGED, check_output, log, near_threshold_ok, shape_of, torch_gpu, upload
+from gpu_common import RAGGED, check_output, log, near_threshold_ok, reference_rows, shape_of, torch_gpu, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -96,8 +97,7 @@ def test_variant_matches_oracle(case, mode, per_row):
             if nd == 0:
                 assert int(got["sel_cost"][hi]) == used
             rows = np.arange(0, w.N, stride)
-            same = (got["mask"][hi] == mask).all(axis=1)[lq[rows]]
-            assert same.mean() > 0.9
-            ref = oracle.hybrid(q[hi], k[hi], v[hi], lq, lk, kbar, vbar, ck, mask, rows[same])
-            check_output(got["O"][hi][rows[same]], ref, w.dtype, "%s head %d rho=%g" % (case, hi, rho))
+            ref, nflip = reference_rows(q[hi], k[hi], v[hi], lq, lk, kbar, vbar, ck, mask, got["mask"][hi], rows)
+            check_output(got["O"][hi][rows], ref, w.dtype,
+                         "%s head %d rho=%g (%d rows on flipped clusters)" % (case, hi, rho, nflip))
             log("  head %d: %d near-threshold mask differences" % (hi, nd))
