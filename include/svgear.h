@@ -172,6 +172,20 @@ int svgear_probe(const svgear_shape* shape, const float* qbar, const int32_t* co
                  const int32_t* counts_k, const int32_t* offsets_k, int flags, float* log_ratio,
                  float* log_eps2, void* ws, size_t ws_bytes, void* stream);
 
+/* svgear_probe without a workspace, for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, operation and errors as svgear_probe, minus
+ * ws / ws_bytes: the probe's scratch is a device array inside the library of
+ * 64 MiB, one per device, held until the process ends.  A shape whose probe scratch exceeds it (about
+ * 4 H Cq Ck + 8 H Nk + 4 H Ck bytes) returns SVGEAR_E_WORKSPACE before anything
+ * is enqueued.  The call allocates nothing.  All calls on one device share that
+ * array: two calls that overlap in time on one device (on different streams
+ * or from different threads) race and must be serialised by the caller. */
+int svgear_probe_noalloc(const svgear_shape* shape, const float* qbar, const int32_t* counts_q,
+                         const void* Kp, const void* Vp, const float* kbar, const float* vbar,
+                         const int32_t* counts_k, const int32_t* offsets_k, int flags,
+                         float* log_ratio, float* log_eps2, void* stream);
+
 /* Step 3 of [R] with its weaknesses paragraph (greedy 0-1 knapsack heuristic):
  * per head, blocks are ordered by ratio, largest first (equal log_ratio: lower
  * block index first); with cost w = counts_q[c] * counts_k[g] and budget

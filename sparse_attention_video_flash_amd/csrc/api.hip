@@ -294,7 +294,7 @@ SVG_API int svgear_cluster(const svgear_shape* shape, int side, const void* X, c
 static int probe_impl(const svgear_shape* shape, const float* qbar, const int32_t* counts_q,
                       const void* Kp, const void* Vp, const float* kbar, const float* vbar,
                       const int32_t* counts_k, const int32_t* offsets_k, int flags,
-                      float* log_ratio, float* log_eps2, void* ws, const Layout& L,
+                      float* log_ratio, float* log_eps2, char* scratch, const Layout& L,
                       hipStream_t st)
 {
     ProbeArgs a;
@@ -315,17 +315,16 @@ static int probe_impl(const svgear_shape* shape, const float* qbar, const int32_
     a.offsets_k = offsets_k;
     a.log_ratio = log_ratio;
     a.log_eps2 = log_eps2;
-    a.scratch = (char*)ws + L.scratch;
+    a.scratch = scratch;
     a.L = &L;
     hipError_t e = launch_probe(a, st);
     return finish(e, flags, st, nullptr);
 }
 
-SVG_API int svgear_probe(const svgear_shape* shape, const float* qbar, const int32_t* counts_q,
-                         const void* Kp, const void* Vp, const float* kbar, const float* vbar,
-                         const int32_t* counts_k, const int32_t* offsets_k, int flags,
-                         float* log_ratio, float* log_eps2, void* ws, size_t ws_bytes,
-                         void* stream)
+static int check_probe_args(const svgear_shape* shape, const float* qbar, const int32_t* counts_q,
+                            const void* Kp, const void* Vp, const float* kbar, const float* vbar,
+                            const int32_t* counts_k, const int32_t* offsets_k, int flags,
+                            const float* log_ratio, const float* log_eps2)
 {
     int rc = check_shape(shape);
     if (rc) return rc;
@@ -339,11 +338,65 @@ SVG_API int svgear_probe(const svgear_shape* shape, const float* qbar, const int
         rc = check_ptrs({log_eps2});
         if (rc) return rc;
     }
+    return SVGEAR_OK;
+}
+
+SVG_API int svgear_probe(const svgear_shape* shape, const float* qbar, const int32_t* counts_q,
+                         const void* Kp, const void* Vp, const float* kbar, const float* vbar,
+                         const int32_t* counts_k, const int32_t* offsets_k, int flags,
+                         float* log_ratio, float* log_eps2, void* ws, size_t ws_bytes,
+                         void* stream)
+{
+    int rc = check_probe_args(shape, qbar, counts_q, Kp, Vp, kbar, vbar, counts_k, offsets_k, flags,
+                              log_ratio, log_eps2);
+    if (rc) return rc;
     Layout L;
     rc = check_ws(shape, ws, ws_bytes, &L);
     if (rc) return rc;
     return probe_impl(shape, qbar, counts_q, Kp, Vp, kbar, vbar, counts_k, offsets_k, flags,
-                      log_ratio, log_eps2, ws, L, (hipStream_t)stream);
+                      log_ratio, log_eps2, (char*)ws + L.scratch, L, (hipStream_t)stream);
+}
+
+// ----------------------------------------------------------------------------- svgear_probe_noalloc
+//
+// The probe's scratch (its sbar table and, on the generic path, the per-key
+// value terms) in a file-scope device array instead of a caller workspace.
+// Each device that runs the library holds its own copy until the process ends.
+// Its address on a device is fetched once, with that device current, and kept
+// per device: host code never passes the array's own name to a kernel.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+static char* noalloc_scratch()
+{
+    constexpr int kMaxDev = 64;
+    static char* g_ptr[kMaxDev];
+    static std::mutex g_mu;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nullptr;
+    std::lock_guard<std::mutex> lock(g_mu);
+    if (!g_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_ptr[dev] = (char*)p;
+    }
+    return g_ptr[dev];
+}
+
+SVG_API int svgear_probe_noalloc(const svgear_shape* shape, const float* qbar, const int32_t* counts_q,
+                                 const void* Kp, const void* Vp, const float* kbar, const float* vbar,
+                                 const int32_t* counts_k, const int32_t* offsets_k, int flags,
+                                 float* log_ratio, float* log_eps2, void* stream)
+{
+    int rc = check_probe_args(shape, qbar, counts_q, Kp, Vp, kbar, vbar, counts_k, offsets_k, flags,
+                              log_ratio, log_eps2);
+    if (rc) return rc;
+    const Layout L = make_layout(*shape);
+    if (L.pr_end > kNoAllocScratchBytes) return SVGEAR_E_WORKSPACE;
+    char* base = noalloc_scratch();
+    if (!base) return SVGEAR_E_HIP;
+    return probe_impl(shape, qbar, counts_q, Kp, Vp, kbar, vbar, counts_k, offsets_k, flags, log_ratio,
+                      log_eps2, base, L, (hipStream_t)stream);
 }
 
 static int64_t budget_of(double rho, int Nq, int Nk)
@@ -518,7 +571,7 @@ SVG_API int svgear_forward(const svgear_shape* shape, double rho, const void* Q,
         if (rc) return rc;
     }
     rc = probe_impl(shape, qbar, counts_q, Kp, Vp, kbar, vbar, counts_k, offsets_k, 0, log_ratio,
-                    nullptr, ws, L, st);
+                    nullptr, w + L.scratch, L, st);
     if (rc) return rc;
     RouteArgs ra;
     ra.H = shape->H;

@@ -17,8 +17,10 @@ OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_WORKSPACE, E_RHO, E_HIP, E_ARG, E_RANGE
 F32, BF16 = 0, 1
 LABELS_GIVEN, DEBUG_EPS, DEBUG_SYNC, PROBE_LOGIT, PROBE_SCORE = 1, 2, 4, 8, 16
 
-EXPORTS = ("svgear_workspace_bytes", "svgear_cluster", "svgear_probe", "svgear_route", "svgear_route_rows",
-           "svgear_attention", "svgear_forward", "svgear_status_string", "svgear_version")
+EXPORTS = ("svgear_workspace_bytes", "svgear_cluster", "svgear_probe", "svgear_probe_noalloc", "svgear_route",
+           "svgear_route_rows", "svgear_attention", "svgear_forward", "svgear_status_string", "svgear_version")
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # svgear_probe_noalloc's per-device scratch array
 
 
 class Shape(ctypes.Structure):
@@ -58,6 +60,7 @@ def load():
         L.svgear_cluster.argtypes = [sp, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                      vp, sz, vp]
         L.svgear_probe.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
+        L.svgear_probe_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp]
         L.svgear_route.argtypes = [sp, f64, vp, vp, vp, vp, vp, vp, sz, vp]
         L.svgear_route_rows.argtypes = [sp, f64, vp, vp, vp, vp, vp, vp, sz, vp]
         L.svgear_attention.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -138,6 +141,18 @@ def probe(shape: Shape, qbar, counts_q, Kp, Vp, kbar, vbar, counts_k, offsets_k,
                              _ptr(vbar), _ptr(counts_k), _ptr(offsets_k), int(flags), _ptr(log_ratio),
                              _ptr(log_eps2), _ptr(ws), ws.numel(), _stream(stream))
     _check(rc, "svgear_probe")
+
+
+def probe_noalloc(shape: Shape, qbar, counts_q, Kp, Vp, kbar, vbar, counts_k, offsets_k, log_ratio,
+                  log_eps2=None, flags=0, stream=None):
+    """svgear_probe without a workspace (the library's per-device scratch array)."""
+    if log_eps2 is not None:
+        flags |= DEBUG_EPS
+    rc = load().svgear_probe_noalloc(ctypes.byref(shape), _ptr(qbar), _ptr(counts_q), _ptr(Kp), _ptr(Vp),
+                                     _ptr(kbar), _ptr(vbar), _ptr(counts_k), _ptr(offsets_k), int(flags),
+                                     _ptr(log_ratio), _ptr(log_eps2), _stream(stream))
+    _check(rc, "svgear_probe_noalloc")
+
 
 
 def route(shape: Shape, rho: float, log_ratio, counts_q, counts_k, mask, sel_cost, ws, stream=None):

@@ -145,3 +145,26 @@ def test_workspace_at_the_maximum_shape_scales_with_the_inputs(H):
     # and at the benchmark shape (40 heads x 75,600 tokens, 100 / 500 clusters)
     s = sv.make_shape(40, 75600, 75600, 128, 100, 500, 10, sv.BF16)
     assert sv.workspace_bytes(s) <= 3 * 2 ** 30
+
+
+def test_probe_noalloc_validation():
+    """svgear_probe_noalloc validates like svgear_probe, and rejects a shape whose
+    probe scratch exceeds its 64 MiB device array, before any device call."""
+    L = sv.load()
+    s = _shape()
+    r = ctypes.byref
+    assert L.svgear_probe_noalloc(r(s), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, None, None) \
+        == sv.E_NULL
+    assert L.svgear_probe_noalloc(r(s), FAKE, FAKE, FAKE + 4, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, None, None) \
+        == sv.E_ALIGN
+    for flags in (sv.LABELS_GIVEN, sv.PROBE_SCORE | sv.PROBE_LOGIT, 32):
+        assert L.svgear_probe_noalloc(r(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, flags, FAKE, FAKE,
+                                      None) == sv.E_ARG
+    assert L.svgear_probe_noalloc(r(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, sv.DEBUG_EPS, FAKE, None,
+                                  None) == sv.E_NULL
+    big = sv.make_shape(40, 75600, 75600, 128, 1000, 1000, 10, sv.BF16)   # 160 MB of sbar alone
+    assert L.svgear_probe_noalloc(r(big), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, None, None) \
+        == sv.E_WORKSPACE
+    bad = _shape(d=32)
+    assert L.svgear_probe_noalloc(r(bad), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, None, None) \
+        == sv.E_SHAPE
