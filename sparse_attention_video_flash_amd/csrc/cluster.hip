@@ -255,7 +255,7 @@ __global__ __launch_bounds__(256) void k_cluster_chunks(const T* __restrict__ X,
                                                         const int32_t* __restrict__ offsets, int N,
                                                         int C, unsigned* __restrict__ range,
                                                         unsigned long long* __restrict__ sums,
-                                                        const int* __restrict__ changed)
+                                                        const int* __restrict__ changed, int rev)
 {
     constexpr bool TWO = MODE == CH_TWO, COLLECT = MODE == CH_ONE_COLLECT;
     constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
@@ -264,7 +264,7 @@ __global__ __launch_bounds__(256) void k_cluster_chunks(const T* __restrict__ X,
     constexpr int PREC = sizeof(T) == 2 ? 8 : 24;
     __shared__ long long s_sum[RPP][D];
     __shared__ int s_idx[MC_ROWS];
-    const int h = blockIdx.y;
+    const int h = rev ? (int)gridDim.y - 1 - (int)blockIdx.y : (int)blockIdx.y;
     const int base = fix_base(N);
     unsigned* rg4 = range + kRangeStride * h;
     if (TWO ? !fix_need_lo(rg4, base, PREC) : (!COLLECT && fix_need_lo(rg4, base, PREC)))
@@ -548,11 +548,12 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ lab
                                                  const uint4* __restrict__ V, uint4* __restrict__ Vp,
                                                  int row_chunks,
                                                  unsigned* __restrict__ range_x,
-                                                 unsigned* __restrict__ range_v)
+                                                 unsigned* __restrict__ range_v, int rev)
 {
     __shared__ int s_lab[kTile];
     __shared__ int s_pos[kTile];
-    const int tile = blockIdx.x, h = blockIdx.y;
+    const int tile = blockIdx.x;
+    const int h = rev ? (int)gridDim.y - 1 - (int)blockIdx.y : (int)blockIdx.y;
     const int i = tile * kTile + threadIdx.x;
     int l = -1;
     if (i < N) {
@@ -626,23 +627,28 @@ static hipError_t run_cluster(const ClusterArgs& a, hipStream_t st)
     // Exact sums of the rows of src in `order` (bucketed by label): the
     // one-word instantiation, then (collect) the clearing of heads that need
     // two words, then the two-word instantiation for those heads.
-    auto chunk_pass = [&](const T* src, unsigned* rg, const int32_t* order, const int* chg, int collect) {
+    // rev: heads in reverse order.  Consecutive passes over X alternate the
+    // direction (screens forward, updates and the scatter backward, the final
+    // means forward), so each starts on the heads the previous one just read,
+    // which the last-level cache still holds.
+    auto chunk_pass = [&](const T* src, unsigned* rg, const int32_t* order, const int* chg, int collect,
+                          int rev) {
         if (collect) {
             hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_ONE_COLLECT>), gchunks, dim3(256), 0, st, src, order,
-                               a.offsets, N, C, rg, sums, chg);
+                               a.offsets, N, C, rg, sums, chg, rev);
             hipLaunchKernelGGL(k_clear_two_word_heads, dim3(16, H), dim3(256), 0, st, rg, N, kPrec,
                                (size_t)C * D, sums);
         } else {
             hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_ONE>), gchunks, dim3(256), 0, st, src, order,
-                               a.offsets, N, C, rg, sums, chg);
+                               a.offsets, N, C, rg, sums, chg, rev);
         }
         hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_TWO>), gchunks, dim3(256), 0, st, src, order,
-                           a.offsets, N, C, rg, sums, chg);
+                           a.offsets, N, C, rg, sums, chg, rev);
     };
     // plain mean pass (no planes); checks the range
     auto mean_pass = [&](const T* src, unsigned* rg, const int32_t* order, int collect, int zero_empty,
-                         float* out) {
-        chunk_pass(src, rg, order, (const int*)nullptr, collect);
+                         float* out, int rev) {
+        chunk_pass(src, rg, order, (const int*)nullptr, collect, rev);
         hipLaunchKernelGGL((k_cluster_finalize<D, false>), gfin, dim3(256), 0, st, a.counts, C, N,
                            rg, kPrec, collect, err, zero_empty, sums, cent64, out, (bf16*)nullptr,
                            (bf16*)nullptr, (float*)nullptr, (double*)nullptr, (float*)nullptr,
@@ -697,7 +703,7 @@ static hipError_t run_cluster(const ClusterArgs& a, hipStream_t st)
             if (mfma && D == 128) {
                 const int* chg = it > 0 ? changed : nullptr;
                 // the first update reads every row: it also records the smallest magnitude
-                chunk_pass(X, range_x, pwork, chg, it == 0 ? 1 : 0);
+                chunk_pass(X, range_x, pwork, chg, it == 0 ? 1 : 0, 1);
                 hipLaunchKernelGGL((k_cluster_finalize<D, D == 128>), gfin, dim3(256), 0, st, a.counts,
                                    C, N, range_x, kPrec, it == 0 ? 1 : 0, it == 0 ? err : nullptr, 0, sums,
                                    cent64, (float*)nullptr, P.hi, P.lo, P.cn32, P.cn64, resid, chg, moved);
@@ -707,7 +713,7 @@ static hipError_t run_cluster(const ClusterArgs& a, hipStream_t st)
                                    P.mlist, P.mpos, P.mcount);
             } else {
                 // the first update reads every row: it also records the smallest magnitude
-                mean_pass(X, range_x, pwork, it == 0 ? 1 : 0, 0, (float*)nullptr);
+                mean_pass(X, range_x, pwork, it == 0 ? 1 : 0, 0, (float*)nullptr, 1);
             }
         }
     }
@@ -722,11 +728,11 @@ static hipError_t run_cluster(const ClusterArgs& a, hipStream_t st)
     const bool x_known = !given && a.iters >= 2;
     hipLaunchKernelGGL((k_scatter<T>), gtiles, dim3(256), 0, st, a.labels, N, C, ntiles, hist, a.offsets,
                        a.perm, a.inv_perm, (const uint4*)a.X, (uint4*)a.Xp, (const uint4*)a.V,
-                       (uint4*)a.Vp, row_chunks, x_known ? nullptr : range_x, range_v);
-    mean_pass(X, range_x, a.perm, x_known ? 0 : 1, given ? 1 : 0, a.cent);
+                       (uint4*)a.Vp, row_chunks, x_known ? nullptr : range_x, range_v, 1);
+    mean_pass(X, range_x, a.perm, x_known ? 0 : 1, given ? 1 : 0, a.cent, 0);
     // V-bar: mean of V over the key clusters (zero for an empty cluster).  cent64
     // is no longer needed and serves as scratch.
-    if (a.side == 1) mean_pass((const T*)a.V, range_v, a.perm, 1, 1, a.vbar);
+    if (a.side == 1) mean_pass((const T*)a.V, range_v, a.perm, 1, 1, a.vbar, 0);
     return hipGetLastError();
 }
 

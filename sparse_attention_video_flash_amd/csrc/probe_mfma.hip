@@ -17,11 +17,12 @@
 // (so f never overflows); sum_j e^{u} f is accumulated per (c, g) against a
 // shift on u that moves only when some u outgrows it by 2^64.
 //
-// Work split: a workgroup (4 waves) takes one key cluster at a time.  Per chunk
-// of 64 keys its threads load the K and V rows once: the K rows go to LDS (the
-// MFMA A operand), and from the V rows they form the per-key scalars
-// vbar.delta_j and ||delta_j||^2 (16 lanes per row), so K_p and V_p are each
-// read once by the whole probe.  Wave w owns the query-centroid column blocks
+// Work split: a workgroup (4 waves) walks its key clusters in chunks of 64
+// keys.  The K and V rows of a chunk go straight from device memory into one of
+// two LDS buffers (the next chunk's loads land during the current chunk's math);
+// the K rows are the MFMA A operand, and from the V rows the threads form the
+// per-key scalars vbar.delta_j and ||delta_j||^2 (16 lanes per row, DPP sums),
+// so K_p and V_p are each read once by the whole probe.  Wave w owns the query-centroid column blocks
 // cb = w, w + 4, ... whose bf16 planes stay in its registers for the whole
 // launch.  Keys are the MFMA rows, so each lane's partial sums stay in-lane
 // until one exchange across the four row groups.
@@ -36,21 +37,19 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int PR_D = 128;
 constexpr int PR_MAXCQ = 256;
 constexpr int PR_KC = 64;                   // keys per staged chunk
-constexpr int PR_PITCH = PR_D * 2 + 16;     // bytes per key row in LDS (272)
-constexpr int PR_LDS = PR_KC * PR_PITCH + PR_KC * 16;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kShiftStep = 64.f;          // log2 headroom before the shift moves
 
 __device__ __forceinline__ bf16x8_t pr_as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-// expm1(a) for a <= 0, given w = e^a: a degree-5 Taylor polynomial near 0
-// (truncation below 1.3e-9 relative for |a| <= 1/16), w - 1 elsewhere.
+// expm1(a) for a <= 0, given w = e^a: the degree-3 Taylor polynomial for
+// |a| < 2^-8 (truncation below a^3 / 24, under 2^-27 relative), w - 1 elsewhere
+// (the rounding of w, 2^-24, is then at most 2^-16 of |w - 1|).
 __device__ __forceinline__ float expm1_nonpos(float a, float w)
 {
-    const float p =
-        a * fmaf(a, fmaf(a, fmaf(a, fmaf(a, 1.f / 120.f, 1.f / 24.f), 1.f / 6.f), 0.5f), 1.f);
-    return a > -0.0625f ? p : w - 1.f;
+    const float p = a * fmaf(a, fmaf(a, 1.f / 6.f, 0.5f), 1.f);
+    return a > -0x1p-8f ? p : w - 1.f;
 }
 
 // Splits 8 fp32 values exactly into three packed bf16 planes, x = h + m + l
@@ -70,32 +69,61 @@ __device__ __forceinline__ void split8x3(const float x[8], u32x4_t& h, u32x4_t& 
     l = __builtin_bit_cast(u32x4_t, c);
 }
 
-// Sum over the 16 lanes of a row group (lanes 16 k .. 16 k + 15).
+// Sum over the 16 lanes of a row group (lanes 16 k .. 16 k + 15), left in every
+// lane of the group: rotations by 8 and 4 within the row, then the two quad
+// swaps, all as DPP moves (no LDS traffic).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float sum16(float v)
 {
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, 16);
+    v += dpp<0x128>(v);   // row_ror:8
+    v += dpp<0x124>(v);   // row_ror:4
+    v += dpp<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+    v += dpp<0xB1>(v);    // quad_perm [1, 0, 3, 2]
     return v;
 }
 
-// With one column block per wave the kernel fits three waves per SIMD (at most
-// 168 VGPRs), with two (the three bf16 planes of two blocks stay in registers)
-// two waves per SIMD.  A workgroup covers a slice of 4 NCBW column blocks
-// (blockIdx.z); with more query clusters than one slice holds, the slices are
-// separate workgroups over the same keys (the key-side staging is repeated per
-// slice).
+// Chunk buffers (two): the K and V rows of 64 keys (256 B each, the 16-B chunk
+// c of row r at position c ^ (r mod 16), so that the fragment reads of 16 rows
+// at one chunk and the per-key reads of one row's 16 chunks are both free of
+// bank conflicts), then, for the first chunk of a key cluster, k-bar and v-bar
+// of the cluster (fp32) and the sbar column of the workgroup's query clusters.
+constexpr int PR_T = PR_KC * 256;
+constexpr int PR_KB = 2 * PR_T, PR_VB = PR_KB + PR_D * 4, PR_SB = PR_VB + PR_D * 4;
+constexpr int PR_BUF = PR_SB + PR_MAXCQ * 4;
+constexpr int PR_LDS2 = 2 * PR_BUF + PR_KC * 16;
+
+typedef __attribute__((address_space(3))) void* pr_lds_ptr;
+
+__device__ __forceinline__ int pr_pos(int r, int c) { return c ^ (r & 15); }
+
+// The chunk a workgroup works on: key cluster g (g >= Ck: none left), keys
+// jc .. min(jc + 64, j1) - 1, j0 the cluster's first key.
+struct PrChunk {
+    int g, j0, jc, j1;
+};
+
+// With one column block per wave the kernel fits three waves per SIMD by its
+// registers, with two (the three bf16 planes of two blocks stay in registers)
+// two; its LDS (two chunk buffers, 68 KB) allows two workgroups per CU.  A
+// workgroup covers a slice of 4 NCBW column blocks (blockIdx.z); with more
+// query clusters than one slice holds, the slices are separate workgroups over
+// the same keys (the key-side loads are repeated per slice).
 template <int NCBW, bool EPS>
-__global__ __launch_bounds__(256, NCBW == 1 ? 3 : 2) void k_probe_mfma(
+__global__ __launch_bounds__(256, 2) void k_probe_mfma(
     const float* __restrict__ qbar, const int32_t* __restrict__ counts_q, const bf16* __restrict__ Kp,
     const bf16* __restrict__ Vp, const float* __restrict__ kbar, const float* __restrict__ vbar,
     const float* __restrict__ sbar, const int32_t* __restrict__ offsets_k, int Nk, int Cq, int Ck,
     float tau, int logit_only, float* __restrict__ log_ratio, float* __restrict__ log_eps2)
 {
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    char* const a_k = smem;
-    float4* const s_ks = (float4*)(smem + PR_KC * PR_PITCH);   // (vbar.delta, ||delta||^2, equal, -)
+    float4* const s_ks = (float4*)(smem + 2 * PR_BUF);   // (2 vbar.delta, ||delta||^2, not equal, -)
     const int h = blockIdx.y;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
     const int col = lane & 15, grp = lane >> 4;   // A row / D column, and row group
     const int ncb = (Cq + 15) / 16;
     const int cbw = blockIdx.z * 4 * NCBW + wave;   // this wave's first column block
@@ -122,153 +150,210 @@ __global__ __launch_bounds__(256, NCBW == 1 ? 3 : 2) void k_probe_mfma(
         }
     }
 
-    const int sch = tid & 15, srow = tid >> 4;   // staging: dims 8 sch.., rows srow + 16 i
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(Kp + (size_t)h * Nk * PR_D), (short)0, Nk * PR_D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(Vp + (size_t)h * Nk * PR_D), (short)0, Nk * PR_D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rkb = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kbar + (size_t)h * Ck * PR_D), (short)0, Ck * PR_D * 4, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rvb = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vbar + (size_t)h * Ck * PR_D), (short)0, Ck * PR_D * 4, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(sbar + (size_t)h * Cq * Ck), (short)0, Cq * Ck * 4, 0x00020000);
     const int32_t* ok = offsets_k + (size_t)h * (Ck + 1);
-    for (int g = blockIdx.x; g < Ck; g += gridDim.x) {
-        const int j0 = ok[g], j1 = ok[g + 1];
-        const int mg = j1 - j0;
-        if (mg == 0) {
+
+    // Next non-empty key cluster from g on (this workgroup's stride); the
+    // empty ones get ln r = -inf.
+    auto next_cluster = [&](int g) -> PrChunk {
+        for (; g < Ck; g += gridDim.x) {
+            const int j0 = ok[g], j1 = ok[g + 1];
+            if (j1 > j0) return PrChunk{g, j0, j0, j1};
             for (int c = c_lo + tid; c < c_hi; c += 256) log_ratio[((size_t)h * Cq + c) * Ck + g] = -__builtin_inff();
-            continue;
         }
-        // this thread's 8 dims of kbar_g and vbar_g; P = ||vbar_g||^2 (1 for the
-        // logit-only estimate, whose value terms vanish)
-        float kb8[8], vb8[8];
-        {
-            const float* kbp = kbar + ((size_t)h * Ck + g) * PR_D + 8 * sch;
-            const float* vbp = vbar + ((size_t)h * Ck + g) * PR_D + 8 * sch;
+        return PrChunk{Ck, 0, 0, 0};
+    };
+    // Loads of a chunk straight into LDS buffer b: wave w fills rows
+    // 16 w .. 16 w + 15 of K and V (4 rows per instruction; rows past the
+    // cluster repeat its last key); with the cluster's first chunk, waves 0-3
+    // also fetch k-bar, v-bar and the sbar column.
+    auto issue = [&](char* b, const PrChunk& it) {
+        const int nv = min(PR_KC, it.j1 - it.jc);
+        const int p = lane & 15;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * wv + 4 * i + (lane >> 4);
+            const int off = (it.jc + min(r, nv - 1)) * 256 + pr_pos(r, p) * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (pr_lds_ptr)(b + (16 * wv + 4 * i) * 256), 16, off, 0, 0, 0);
+            if (!logit_only)   // the logit-only estimate reads no values
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (pr_lds_ptr)(b + PR_T + (16 * wv + 4 * i) * 256), 16, off,
+                                                         0, 0, 0);
+        }
+        if (it.jc == it.j0) {
+            if (wv == 0 && lane < 32)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rkb, (pr_lds_ptr)(b + PR_KB), 16, it.g * PR_D * 4 + lane * 16, 0, 0, 0);
+            if (wv == 1 && lane < 32)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rvb, (pr_lds_ptr)(b + PR_VB), 16, it.g * PR_D * 4 + lane * 16, 0, 0, 0);
+            if (wv >= 2) {
+                const int c = c_lo + (wv - 2) * 64 + lane;
+                const int cc = min(c, Cq - 1);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (pr_lds_ptr)(b + PR_SB + (wv - 2) * 256), 4,
+                                                         (cc * Ck + it.g) * 4, 0, 0, 0);
+            }
+        }
+    };
+
+    const int sch = tid & 15, srow = tid >> 4;   // per-key terms: dims 8 sch.., rows srow + 16 i
+    float kb8[8], vb8[8], P = 0.f;
+    float sb[NCBW], sh[NCBW], S[NCBW];
+    PrChunk cur = next_cluster(blockIdx.x);
+    if (cur.g < Ck) issue(smem, cur);
+    int bsel = 0;
+    while (cur.g < Ck) {
+        char* const b = smem + bsel * PR_BUF;
+        __builtin_amdgcn_s_waitcnt(0x0F70 | 0);   // this wave's loads of the current chunk landed
+        __syncthreads();                           // every wave's; the other buffer's readers are done
+        PrChunk nxt = cur;
+        nxt.jc += PR_KC;
+        if (nxt.jc >= nxt.j1) nxt = next_cluster(cur.g + gridDim.x);
+        if (nxt.g < Ck) issue(smem + (bsel ^ 1) * PR_BUF, nxt);   // lands during this chunk's math
+
+        const int nv = min(PR_KC, cur.j1 - cur.jc);
+        if (cur.jc == cur.j0) {   // a new cluster: its centroids, P = ||vbar||^2, sbar; sums restart
+            const float* kbl = (const float*)(b + PR_KB) + 8 * sch;
+            const float* vbl = (const float*)(b + PR_VB) + 8 * sch;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                kb8[e] = kbp[e];
-                vb8[e] = logit_only ? 0.f : vbp[e];
+                kb8[e] = kbl[e];
+                vb8[e] = logit_only ? 0.f : vbl[e];
+            }
+            P = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) P = fmaf(vb8[e], vb8[e], P);
+            P = logit_only ? 1.f : sum16(P);
+            const float* sbl = (const float*)(b + PR_SB);
+#pragma unroll
+            for (int i = 0; i < NCBW; ++i) {
+                const int c = (cbw + 4 * i) * 16 + col;
+                sb[i] = c < Cq ? sbl[c - c_lo] : 0.f;
+                sh[i] = 0.f;
+                S[i] = 0.f;
             }
         }
-        float P = 0.f;
+        // per-key value terms and the equal-to-centroid flag, from the LDS rows
 #pragma unroll
-        for (int e = 0; e < 8; ++e) P = fmaf(vb8[e], vb8[e], P);
-        P = logit_only ? 1.f : sum16(P);
-        float sb[NCBW], sh[NCBW], S[NCBW];
+        for (int i = 0; i < 4; ++i) {
+            const int r = srow + 16 * i;
+            const u32x4_t kw = *(const u32x4_t*)(b + r * 256 + pr_pos(r, sch) * 16);
+            const u32x4_t vw = *(const u32x4_t*)(b + PR_T + r * 256 + pr_pos(r, sch) * 16);
+            float qd = 0.f, rr = 0.f, ne = 0.f;
 #pragma unroll
-        for (int i = 0; i < NCBW; ++i) {
-            const int c = (cbw + 4 * i) * 16 + col;
-            sb[i] = c < Cq ? sbar[((size_t)h * Cq + c) * Ck + g] : 0.f;
-            sh[i] = 0.f;
-            S[i] = 0.f;
+            for (int e = 0; e < 8; ++e) {
+                const unsigned kb = (e & 1) ? (kw[e >> 1] & 0xFFFF0000u) : (kw[e >> 1] << 16);
+                const unsigned vb = (e & 1) ? (vw[e >> 1] & 0xFFFF0000u) : (vw[e >> 1] << 16);
+                ne += __uint_as_float(kb) != kb8[e] ? 1.f : 0.f;
+                const float dl = logit_only ? 0.f : vb8[e] - __uint_as_float(vb);
+                qd = fmaf(vb8[e], dl, qd);
+                rr = fmaf(dl, dl, rr);
+            }
+            qd = sum16(qd);
+            rr = sum16(rr);
+            ne = sum16(ne);
+            if (sch == 0) s_ks[r] = make_float4(2.f * qd, rr, ne == 0.f ? 0.f : 1.f, 0.f);
         }
-        for (int jc = j0; jc < j1; jc += PR_KC) {
-            const int nv = min(PR_KC, j1 - jc);
-            // rows of this chunk: K to LDS as is; per-key scalars from V
-            u32x4_t kw[4], vw[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int j = jc + min(srow + 16 * i, nv - 1);
-                kw[i] = *(const u32x4_t*)(Kp + ((size_t)h * Nk + j) * PR_D + 8 * sch);
-                vw[i] = logit_only ? u32x4_t{0, 0, 0, 0} : *(const u32x4_t*)(Vp + ((size_t)h * Nk + j) * PR_D + 8 * sch);
-            }
-            __syncthreads();   // the previous chunk's readers are done
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = srow + 16 * i;
-                *(u32x4_t*)(a_k + r * PR_PITCH + sch * 16) = kw[i];
-                float qd = 0.f, rr = 0.f, ne = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const unsigned kb = (e & 1) ? (kw[i][e >> 1] & 0xFFFF0000u) : (kw[i][e >> 1] << 16);
-                    const unsigned vb = (e & 1) ? (vw[i][e >> 1] & 0xFFFF0000u) : (vw[i][e >> 1] << 16);
-                    ne += __uint_as_float(kb) != kb8[e] ? 1.f : 0.f;
-                    const float dl = vb8[e] - __uint_as_float(vb);
-                    qd = fmaf(vb8[e], dl, qd);
-                    rr = fmaf(dl, dl, rr);
-                }
-                qd = sum16(qd);
-                rr = sum16(rr);
-                ne = sum16(ne);
-                if (sch == 0) s_ks[r] = make_float4(qd, rr, ne == 0.f ? 1.f : 0.f, 0.f);
-            }
-            __syncthreads();
+        __syncthreads();
 
-            const int ntile = (nv + 15) / 16;
-            for (int kt = 0; kt < ntile; ++kt) {
-                bf16x8_t ak[4];
-                const int arow = kt * 16 + col;
+        const int ntile = (nv + 15) / 16;
+        for (int kt = 0; kt < ntile; ++kt) {
+            bf16x8_t ak[4];
+            const int arow = kt * 16 + col;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                ak[ks] = pr_as_bf16x8(*(const u32x4_t*)(b + arow * 256 + pr_pos(arow, 4 * ks + grp) * 16));
+            const int kr0 = kt * 16 + 4 * grp;   // this lane's rows kr0 .. kr0 + 3
+            float4 kq[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) kq[r] = s_ks[kr0 + r];
+#pragma unroll
+            for (int i = 0; i < NCBW; ++i) {
+                if (cbw + 4 * i >= ncb) continue;   // wave-uniform
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks)
-                    ak[ks] = pr_as_bf16x8(*(const u32x4_t*)(a_k + arow * PR_PITCH + (32 * ks + 8 * grp) * 2));
-                const int kr0 = kt * 16 + 4 * grp;   // this lane's rows kr0 .. kr0 + 3
-                float4 kq[4];
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[ks], bh[i][ks], acc, 0, 0, 0);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) kq[r] = s_ks[kr0 + r];
+                for (int ks = 0; ks < 4; ++ks)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[ks], bm[i][ks], acc, 0, 0, 0);
 #pragma unroll
-                for (int i = 0; i < NCBW; ++i) {
-                    if (cbw + 4 * i >= ncb) continue;   // wave-uniform
-                    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+                for (int ks = 0; ks < 4; ++ks)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[ks], bl[i][ks], acc, 0, 0, 0);
+                // Per pair, with D = sbar - s (exactly 0 for a key equal to its
+                // centroid), w = e^{-|D|}, em = w - 1 and sigma = -w if D > 0
+                // else 1:  e = e^{2 sbar} e^{2 max(-D, 0)} f with
+                //   f = em^2 P + 2 em sigma vbar.delta + sigma^2 ||delta||^2,
+                // the bracket with the larger exponential factored out (no
+                // intermediate overflows however far the key lies from its
+                // centroid).  S sums f e^{u'} with u' = log2 e^{2 max(-D, 0)} - sh.
+                const bool tail = kt * 16 + 16 > nv;   // wave-uniform
+                float f[4], u[4];
+                float umax = -__builtin_inff();
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks)
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[ks], bh[i][ks], acc, 0, 0, 0);
+                for (int r = 0; r < 4; ++r) {
+                    const float D = kq[r].z * fmaf(-tau, acc[r], sb[i]);
+                    const float ad = fabsf(D);
+                    const float w = __builtin_amdgcn_exp2f(-ad * kLog2e);   // e^{-|D|}
+                    const float em = expm1_nonpos(-ad, w);
+                    const float sg = D > 0.f ? -w : 1.f;
+                    const float sr = sg * kq[r].y;
+                    const float fr = fmaxf(fmaf(em, fmaf(em, P, sg * kq[r].x), sg * sr), 0.f);
+                    f[r] = (tail && kr0 + r >= nv) ? 0.f : fr;
+                    u[r] = fmaf(2.f * kLog2e, fmaxf(-D, 0.f), -sh[i]);
+                    umax = fmaxf(umax, u[r]);
+                }
+                if (__any(umax > kShiftStep)) {   // rare: raise the shift
+                    const float up = fmaxf(umax, 0.f);
+                    S[i] *= __builtin_amdgcn_exp2f(-up);
+                    sh[i] += up;
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks)
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[ks], bm[i][ks], acc, 0, 0, 0);
+                    for (int r = 0; r < 4; ++r) u[r] -= up;
+                }
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks)
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[ks], bl[i][ks], acc, 0, 0, 0);
-                    float f[4], u[4];
-                    float umax = 0.f;
+                for (int r = 0; r < 4; ++r) S[i] = fmaf(f[r], __builtin_amdgcn_exp2f(u[r]), S[i]);
+                if (EPS) {
+                    const int c = (cbw + 4 * i) * 16 + col;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        // D = sbar - s; exactly 0 for a key equal to its centroid
-                        const float D = kq[r].z != 0.f ? 0.f : sb[i] - tau * acc[r];
-                        const float ad = fabsf(D);
-                        const float w = __builtin_amdgcn_exp2f(-ad * kLog2e);   // e^{-|D|}
-                        const float em = expm1_nonpos(-ad, w);
-                        const bool pos = D > 0.f;
-                        const float c1 = pos ? -2.f * em * w : 2.f * em;
-                        const float c2 = pos ? w * w : 1.f;
-                        const float fr = fmaxf(fmaf(em, em * P, fmaf(c1, kq[r].x, c2 * kq[r].y)), 0.f);
-                        f[r] = kr0 + r < nv ? fr : 0.f;
-                        // log2 e^{2|D|} for D <= 0; 0 where the term vanishes, so no
-                        // exponent of a zero term can overflow
-                        u[r] = (pos || !(f[r] > 0.f)) ? 0.f : (2.f * kLog2e) * ad;
-                        umax = fmaxf(umax, u[r]);
-                    }
-                    if (__any(umax > sh[i] + kShiftStep)) {
-                        const float ns = fmaxf(sh[i], umax);
-                        S[i] *= __builtin_amdgcn_exp2f(sh[i] - ns);
-                        sh[i] = ns;
-                    }
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) S[i] = fmaf(f[r], __builtin_amdgcn_exp2f(u[r] - sh[i]), S[i]);
-                    if (EPS) {
-                        const int c = (cbw + 4 * i) * 16 + col;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (c < Cq && kr0 + r < nv)
-                                log_eps2[((size_t)h * Cq + c) * Nk + jc + kr0 + r] =
-                                    f[r] > 0.f ? 2.f * sb[i] + kLn2 * u[r] + logf(f[r]) : -__builtin_inff();
-                    }
+                    for (int r = 0; r < 4; ++r)
+                        if (c < Cq && kr0 + r < nv)
+                            log_eps2[((size_t)h * Cq + c) * Nk + cur.jc + kr0 + r] =
+                                f[r] > 0.f ? 2.f * sb[i] + kLn2 * (u[r] + sh[i]) + logf(f[r]) : -__builtin_inff();
                 }
             }
         }
-        // combine the four row groups (lanes col, col + 16, col + 32, col + 48)
+        if (cur.jc + PR_KC >= cur.j1) {   // the cluster's last chunk: combine the four row groups
+            const int mg = cur.j1 - cur.j0;
 #pragma unroll
-        for (int i = 0; i < NCBW; ++i) {
-            if (cbw + 4 * i >= ncb) continue;
-            float m = sh[i], s = S[i];
+            for (int i = 0; i < NCBW; ++i) {
+                if (cbw + 4 * i >= ncb) continue;
+                float m = sh[i], s2 = S[i];
 #pragma unroll
-            for (int o = 16; o <= 32; o <<= 1) {
-                const float om = __shfl_xor(m, o), os = __shfl_xor(s, o);
-                const float mn = fmaxf(m, om);
-                s = s * __builtin_amdgcn_exp2f(m - mn) + os * __builtin_amdgcn_exp2f(om - mn);
-                m = mn;
-            }
-            const int c = (cbw + 4 * i) * 16 + col;
-            if (grp == 0 && c < Cq) {
-                float lr = -__builtin_inff();
-                if (counts_q[(size_t)h * Cq + c] > 0 && s > 0.f)
-                    lr = 2.f * sb[i] + kLn2 * (m + __log2f(s)) - logf((float)mg);
-                log_ratio[((size_t)h * Cq + c) * Ck + g] = lr;
+                for (int o = 16; o <= 32; o <<= 1) {
+                    const float om = __shfl_xor(m, o), os = __shfl_xor(s2, o);
+                    const float mn = fmaxf(m, om);
+                    s2 = s2 * __builtin_amdgcn_exp2f(m - mn) + os * __builtin_amdgcn_exp2f(om - mn);
+                    m = mn;
+                }
+                const int c = (cbw + 4 * i) * 16 + col;
+                if (grp == 0 && c < Cq) {
+                    float lr = -__builtin_inff();
+                    if (counts_q[(size_t)h * Cq + c] > 0 && s2 > 0.f)
+                        lr = 2.f * sb[i] + kLn2 * (m + __log2f(s2)) - logf((float)mg);
+                    log_ratio[((size_t)h * Cq + c) * Ck + cur.g] = lr;
+                }
             }
         }
+        cur = nxt;
+        bsel ^= 1;
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70 | 0);   // no load is left in flight
 }
 
 SVG_HIDDEN bool probe_mfma_supported(const ProbeArgs& a)
@@ -291,12 +376,12 @@ SVG_HIDDEN hipError_t launch_probe_mfma(const ProbeArgs& a, const float* sbar, h
 #define SVG_PROBE_CASE(n)                                                                          \
     case n:                                                                                        \
         if (eps)                                                                                   \
-            hipLaunchKernelGGL((k_probe_mfma<n, true>), dim3(gx, a.H, slices), dim3(256), PR_LDS, st, \
+            hipLaunchKernelGGL((k_probe_mfma<n, true>), dim3(gx, a.H, slices), dim3(256), PR_LDS2, st, \
                                a.qbar, a.counts_q, (const bf16*)a.Kp, (const bf16*)a.Vp, a.kbar,   \
                                a.vbar, sbar, a.offsets_k, a.Nk, a.Cq, a.Ck, tau, logit_only,       \
                                a.log_ratio, eps);                                                  \
         else                                                                                       \
-            hipLaunchKernelGGL((k_probe_mfma<n, false>), dim3(gx, a.H, slices), dim3(256), PR_LDS, st, \
+            hipLaunchKernelGGL((k_probe_mfma<n, false>), dim3(gx, a.H, slices), dim3(256), PR_LDS2, st, \
                                a.qbar, a.counts_q, (const bf16*)a.Kp, (const bf16*)a.Vp, a.kbar,   \
                                a.vbar, sbar, a.offsets_k, a.Nk, a.Cq, a.Ck, tau, logit_only,       \
                                a.log_ratio, eps);                                                  \
