@@ -78,6 +78,7 @@ SVG_HIDDEN Layout make_layout(const svgear_shape& s)
     L.pr_sbar = take(H * Cq * Ck * 4);
     L.pr_keys = take(H * Nk * 8);
     L.pr_pg = take(H * Ck * 4);
+    L.pr_ctr = take(2 * H * 4);   // claim counters of the MFMA probe, per head and column slice
     L.pr_end = off;
 
     off = 0;

@@ -239,7 +239,7 @@ struct Layout {
         cl_mlist, cl_mpos, cl_mcount;
     size_t cl_end;
     // probe scratch (relative to scratch)
-    size_t pr_sbar, pr_keys, pr_pg;
+    size_t pr_sbar, pr_keys, pr_pg, pr_ctr;
     size_t pr_end;
     // attention scratch (relative to scratch)
     size_t at_kvplanes, at_logm, at_tiles, at_segs, at_cinfo, at_comp, at_rows, at_queue;

@@ -10,12 +10,14 @@
 // only the fp32 accumulation rounds (absolute error about 2^-24 tau
 // sum_t |qbar_t k_t|, independent of how far the key lies from its centroid).
 // D = sbar - s with sbar = tau qbar_c.kbar_g (fp64, rounded once); a key equal
-// to its centroid in every coordinate gets D = 0 exactly.  The estimate
-//     e = e^{2s} [expm1(D)^2 ||vbar_g||^2 + 2 expm1(D) vbar_g.delta_j + ||delta_j||^2],
-// s = sbar - D, delta_j = vbar_g - v_j, is rewritten as e = e^{2 sbar} e^{u} f
-// with u = 2 max(-D, 0) and f the bracket with e^{-2D} moved inside when D > 0
-// (so f never overflows); sum_j e^{u} f is accumulated per (c, g) against a
-// shift on u that moves only when some u outgrows it by 2^64.
+// to its centroid in every coordinate is treated as D = 0 exactly.  The estimate
+//     e = e^{2s} [expm1(D)^2 ||vbar_g||^2 + 2 expm1(D) vbar_g.delta_j + ||delta_j||^2]
+//       = || e^{sbar} vbar_g - e^{s} v_j ||^2,
+// s = sbar - D, delta_j = vbar_g - v_j, is evaluated with the larger of the two
+// exponentials factored out, e = e^{2 sbar} e^{2 max(-D, 0)} f, f a quadratic in
+// expm1(-|D|) with per-key coefficients (so f never overflows); sum_j
+// e^{2 max(-D, 0)} f is accumulated per (c, g) against a shift that moves only
+// when some exponent outgrows it by 2^64.
 //
 // Work split: a workgroup (4 waves) walks its key clusters in chunks of 64
 // keys.  The K and V rows of a chunk go straight from device memory into one of
@@ -43,13 +45,12 @@ constexpr float kShiftStep = 64.f;          // log2 headroom before the shift mo
 
 __device__ __forceinline__ bf16x8_t pr_as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-// expm1(a) for a <= 0, given w = e^a: the degree-3 Taylor polynomial for
-// |a| < 2^-8 (truncation below a^3 / 24, under 2^-27 relative), w - 1 elsewhere
-// (the rounding of w, 2^-24, is then at most 2^-16 of |w - 1|).
-__device__ __forceinline__ float expm1_nonpos(float a, float w)
+// expm1(-x) for x >= 0, given w = e^{-x}: x^2 / 2 - x for x < 2^-8 (the
+// truncation, below x^3 / 6, is under 2^-17 relative), w - 1 elsewhere (the
+// rounding of w, 2^-24, is then at most 2^-16 of |w - 1|).
+__device__ __forceinline__ float expm1_nonpos(float x, float w)
 {
-    const float p = a * fmaf(a, fmaf(a, 1.f / 6.f, 0.5f), 1.f);
-    return a > -0x1p-8f ? p : w - 1.f;
+    return x < 0x1p-8f ? fmaf(0.5f * x, x, -x) : w - 1.f;
 }
 
 // Splits 8 fp32 values exactly into three packed bf16 planes, x = h + m + l
@@ -69,13 +70,26 @@ __device__ __forceinline__ void split8x3(const float x[8], u32x4_t& h, u32x4_t& 
     l = __builtin_bit_cast(u32x4_t, c);
 }
 
-// Sum over the 16 lanes of a row group (lanes 16 k .. 16 k + 15), left in every
+// Sum (bitwise or) over the 16 lanes of a row group (lanes 16 k .. 16 k + 15), left in every
 // lane of the group: rotations by 8 and 4 within the row, then the two quad
 // swaps, all as DPP moves (no LDS traffic).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v)
 {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ unsigned dppu(unsigned v)
+{
+    return (unsigned)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+__device__ __forceinline__ unsigned or16(unsigned v)
+{
+    v |= dppu<0x128>(v);
+    v |= dppu<0x124>(v);
+    v |= dppu<0x4E>(v);
+    v |= dppu<0xB1>(v);
+    return v;
 }
 __device__ __forceinline__ float sum16(float v)
 {
@@ -94,89 +108,126 @@ __device__ __forceinline__ float sum16(float v)
 constexpr int PR_T = PR_KC * 256;
 constexpr int PR_KB = 2 * PR_T, PR_VB = PR_KB + PR_D * 4, PR_SB = PR_VB + PR_D * 4;
 constexpr int PR_BUF = PR_SB + PR_MAXCQ * 4;
-constexpr int PR_LDS2 = 2 * PR_BUF + PR_KC * 16;
+constexpr int PR_LDS2 = 2 * PR_BUF;   // plus the per-key rows, 1.3 KB
 
 typedef __attribute__((address_space(3))) void* pr_lds_ptr;
 
+// A workgroup barrier for LDS only: this wave's LDS accesses complete, then
+// s_barrier (the memory clobber keeps the compiler from moving any access
+// across it).  Unlike __syncthreads it does not wait for outstanding
+// device-memory loads, so the next chunk's loads into LDS stay in flight.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ int pr_pos(int r, int c) { return c ^ (r & 15); }
 
-// The chunk a workgroup works on: key cluster g (g >= Ck: none left), keys
-// jc .. min(jc + 64, j1) - 1, j0 the cluster's first key.
+// The chunk a workgroup works on: key cluster g of head h (g >= Ck: no work
+// left), keys jc .. min(jc + 64, j1) - 1, j0 the cluster's first key.
 struct PrChunk {
-    int g, j0, jc, j1;
+    int h, g, j0, jc, j1;
 };
+
+// Thread 0 only: the first non-empty key cluster from the claim g of head h on.
+// A claim past the head's last cluster moves the workgroup to the next head
+// (left counts the heads still to try); empty clusters get ln r = -inf.
+__device__ __forceinline__ int4 pr_resolve(int g, int& h, int& left, int* __restrict__ ctr,
+                                        const int32_t* __restrict__ offsets_k, int H, int Cq, int Ck,
+                                        int c_lo, int c_hi, float* __restrict__ log_ratio)
+{
+    for (;;) {
+        if (g < Ck) {
+            const int32_t* ok = offsets_k + (size_t)h * (Ck + 1);
+            const int j0 = ok[g], j1 = ok[g + 1];
+            if (j1 > j0) return make_int4(h, g, j0, j1);
+            for (int c = c_lo; c < c_hi; ++c) log_ratio[((size_t)h * Cq + c) * Ck + g] = -__builtin_inff();
+        } else {
+            if (--left <= 0) return make_int4(0, Ck, 0, 0);
+            h = h + 1 == H ? 0 : h + 1;
+        }
+        g = atomicAdd(ctr + h, 1);
+    }
+}
 
 // With one column block per wave the kernel fits three waves per SIMD by its
 // registers, with two (the three bf16 planes of two blocks stay in registers)
-// two; its LDS (two chunk buffers, 68 KB) allows two workgroups per CU.  A
-// workgroup covers a slice of 4 NCBW column blocks (blockIdx.z); with more
+// two; its LDS (two chunk buffers, 69 KB) allows two workgroups per CU.  A
+// workgroup covers a slice of 4 NCBW column blocks (blockIdx.y); with more
 // query clusters than one slice holds, the slices are separate workgroups over
 // the same keys (the key-side loads are repeated per slice).
+//
+// Work distribution: one resident round of workgroups; the (head, key cluster)
+// items are claimed at run time from one counter per head and slice.
+// Workgroup w starts on head w H / G and, once that head's clusters are all
+// claimed, moves on to the following heads, so every workgroup stays busy until
+// the last cluster is claimed, whatever the cluster sizes.  Thread 0 claims the
+// cluster after next while the current chunk is computed (the atomic is in
+// flight during the math).
 template <int NCBW, bool EPS>
 __global__ __launch_bounds__(256, 2) void k_probe_mfma(
     const float* __restrict__ qbar, const int32_t* __restrict__ counts_q, const bf16* __restrict__ Kp,
     const bf16* __restrict__ Vp, const float* __restrict__ kbar, const float* __restrict__ vbar,
-    const float* __restrict__ sbar, const int32_t* __restrict__ offsets_k, int Nk, int Cq, int Ck,
-    float tau, int logit_only, float* __restrict__ log_ratio, float* __restrict__ log_eps2)
+    const float* __restrict__ sbar, const int32_t* __restrict__ offsets_k, int H, int Nk, int Cq, int Ck,
+    float tau, int logit_only, int* __restrict__ ctr, float* __restrict__ log_ratio,
+    float* __restrict__ log_eps2)
 {
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    float4* const s_ks = (float4*)(smem + 2 * PR_BUF);   // (2 vbar.delta, ||delta||^2, not equal, -)
-    const int h = blockIdx.y;
+    // Per-key coefficients of the chunk's rows (see the pair loop) and the
+    // claimed clusters, in arrays of their own: the compiler then knows that
+    // writing them cannot touch the chunk buffers that loads are filling.
+    __shared__ float4 s_ks[PR_KC];   // (alpha1, beta0, beta1, R)
+    __shared__ float s_ka[PR_KC];    // alpha0
+    __shared__ int4 s_item[2];       // [0] first cluster, [1] the next
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     const int col = lane & 15, grp = lane >> 4;   // A row / D column, and row group
     const int ncb = (Cq + 15) / 16;
-    const int cbw = blockIdx.z * 4 * NCBW + wave;   // this wave's first column block
-    const int c_lo = blockIdx.z * 4 * NCBW * 16, c_hi = min(Cq, c_lo + 4 * NCBW * 16);
+    const int cbw = blockIdx.y * 4 * NCBW + wave;   // this wave's first column block
+    const int c_lo = blockIdx.y * 4 * NCBW * 16, c_hi = min(Cq, c_lo + 4 * NCBW * 16);
+    int* const ctr_s = ctr + (size_t)blockIdx.y * H;
 
-    // B fragments of this wave's column blocks: centroid cb*16 + col, dims
-    // 32 ks + 8 grp + 0..7, split exactly into three bf16 planes.
+    // B fragments of this wave's column blocks for head h: centroid cb*16 + col,
+    // dims 32 ks + 8 grp + 0..7, split exactly into three bf16 planes.
     bf16x8_t bh[NCBW][4], bm[NCBW][4], bl[NCBW][4];
+    bool qlive[NCBW];   // query cluster cb*16 + col is non-empty
+    auto load_b = [&](int h) {
 #pragma unroll
-    for (int i = 0; i < NCBW; ++i) {
-        const int c = (cbw + 4 * i) * 16 + col;
-        const bool cv = c < Cq;
-        const float* qp = qbar + ((size_t)h * Cq + (cv ? c : 0)) * PR_D + 8 * grp;
+        for (int i = 0; i < NCBW; ++i) {
+            const int c = (cbw + 4 * i) * 16 + col;
+            const bool cv = c < Cq;
+            qlive[i] = cv && counts_q[(size_t)h * Cq + c] > 0;
+            const float* qp = qbar + ((size_t)h * Cq + (cv ? c : 0)) * PR_D + 8 * grp;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            float x[8];
+            for (int ks = 0; ks < 4; ++ks) {
+                float x[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = cv ? qp[32 * ks + e] : 0.f;
-            u32x4_t p0, p1, p2;
-            split8x3(x, p0, p1, p2);
-            bh[i][ks] = pr_as_bf16x8(p0);
-            bm[i][ks] = pr_as_bf16x8(p1);
-            bl[i][ks] = pr_as_bf16x8(p2);
+                for (int e = 0; e < 8; ++e) x[e] = cv ? qp[32 * ks + e] : 0.f;
+                u32x4_t p0, p1, p2;
+                split8x3(x, p0, p1, p2);
+                bh[i][ks] = pr_as_bf16x8(p0);
+                bm[i][ks] = pr_as_bf16x8(p1);
+                bl[i][ks] = pr_as_bf16x8(p2);
+            }
         }
-    }
-
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(Kp + (size_t)h * Nk * PR_D), (short)0, Nk * PR_D * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(Vp + (size_t)h * Nk * PR_D), (short)0, Nk * PR_D * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rkb = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(kbar + (size_t)h * Ck * PR_D), (short)0, Ck * PR_D * 4, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rvb = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(vbar + (size_t)h * Ck * PR_D), (short)0, Ck * PR_D * 4, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(sbar + (size_t)h * Cq * Ck), (short)0, Cq * Ck * 4, 0x00020000);
-    const int32_t* ok = offsets_k + (size_t)h * (Ck + 1);
-
-    // Next non-empty key cluster from g on (this workgroup's stride); the
-    // empty ones get ln r = -inf.
-    auto next_cluster = [&](int g) -> PrChunk {
-        for (; g < Ck; g += gridDim.x) {
-            const int j0 = ok[g], j1 = ok[g + 1];
-            if (j1 > j0) return PrChunk{g, j0, j0, j1};
-            for (int c = c_lo + tid; c < c_hi; c += 256) log_ratio[((size_t)h * Cq + c) * Ck + g] = -__builtin_inff();
-        }
-        return PrChunk{Ck, 0, 0, 0};
     };
+    auto item = [&](int k) -> PrChunk {
+        const int4 v = s_item[k];
+        const int j0 = __builtin_amdgcn_readfirstlane(v.z);
+        return PrChunk{__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y), j0, j0,
+                       __builtin_amdgcn_readfirstlane(v.w)};
+    };
+
     // Loads of a chunk straight into LDS buffer b: wave w fills rows
     // 16 w .. 16 w + 15 of K and V (4 rows per instruction; rows past the
     // cluster repeat its last key); with the cluster's first chunk, waves 0-3
     // also fetch k-bar, v-bar and the sbar column.
     auto issue = [&](char* b, const PrChunk& it) {
+        const int h = it.h;
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(Kp + (size_t)h * Nk * PR_D), (short)0, Nk * PR_D * 2, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(Vp + (size_t)h * Nk * PR_D), (short)0, Nk * PR_D * 2, 0x00020000);
         const int nv = min(PR_KC, it.j1 - it.jc);
         const int p = lane & 15;
 #pragma unroll
@@ -189,11 +240,19 @@ __global__ __launch_bounds__(256, 2) void k_probe_mfma(
                                                          0, 0, 0);
         }
         if (it.jc == it.j0) {
-            if (wv == 0 && lane < 32)
+            if (wv == 0 && lane < 32) {
+                const __amdgpu_buffer_rsrc_t rkb = __builtin_amdgcn_make_buffer_rsrc(
+                    (void*)(kbar + (size_t)h * Ck * PR_D), (short)0, Ck * PR_D * 4, 0x00020000);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rkb, (pr_lds_ptr)(b + PR_KB), 16, it.g * PR_D * 4 + lane * 16, 0, 0, 0);
-            if (wv == 1 && lane < 32)
+            }
+            if (wv == 1 && lane < 32) {
+                const __amdgpu_buffer_rsrc_t rvb = __builtin_amdgcn_make_buffer_rsrc(
+                    (void*)(vbar + (size_t)h * Ck * PR_D), (short)0, Ck * PR_D * 4, 0x00020000);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rvb, (pr_lds_ptr)(b + PR_VB), 16, it.g * PR_D * 4 + lane * 16, 0, 0, 0);
+            }
             if (wv >= 2) {
+                const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+                    (void*)(sbar + (size_t)h * Cq * Ck), (short)0, Cq * Ck * 4, 0x00020000);
                 const int c = c_lo + (wv - 2) * 64 + lane;
                 const int cc = min(c, Cq - 1);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (pr_lds_ptr)(b + PR_SB + (wv - 2) * 256), 4,
@@ -202,29 +261,64 @@ __global__ __launch_bounds__(256, 2) void k_probe_mfma(
         }
     };
 
+    // the first two clusters, claimed by thread 0 starting at the home head
+    int hh = (int)(((long long)blockIdx.x * H) / gridDim.x), left = H, pend = 0;
+    if (tid == 0) {
+        const int4 a = pr_resolve(atomicAdd(ctr_s + hh, 1), hh, left, ctr_s, offsets_k, H, Cq, Ck, c_lo, c_hi,
+                                  log_ratio);
+        s_item[0] = a;
+        s_item[1] = a.y < Ck ? pr_resolve(atomicAdd(ctr_s + hh, 1), hh, left, ctr_s, offsets_k, H, Cq, Ck, c_lo,
+                                          c_hi, log_ratio)
+                             : a;
+    }
+    __syncthreads();
+    PrChunk cur = item(0);
+    int bhead = -1;   // the head whose planes bh, bm, bl hold
     const int sch = tid & 15, srow = tid >> 4;   // per-key terms: dims 8 sch.., rows srow + 16 i
-    float kb8[8], vb8[8], P = 0.f;
+    float vb8[8], P = 0.f;
+    unsigned kbw[4], kmw[4];   // k-bar as packed bf16 and the bits that decide equality
     float sb[NCBW], sh[NCBW], S[NCBW];
-    PrChunk cur = next_cluster(blockIdx.x);
     if (cur.g < Ck) issue(smem, cur);
     int bsel = 0;
     while (cur.g < Ck) {
         char* const b = smem + bsel * PR_BUF;
-        __builtin_amdgcn_s_waitcnt(0x0F70 | 0);   // this wave's loads of the current chunk landed
-        __syncthreads();                           // every wave's; the other buffer's readers are done
+        // This wave's loads of the current chunk have landed and its LDS
+        // accesses (thread 0's claim above included) are complete -- the
+        // barrier's own fence does not wait for the LDS write -- then every
+        // wave's; the other buffer's readers are done.
+        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+        __syncthreads();
         PrChunk nxt = cur;
         nxt.jc += PR_KC;
-        if (nxt.jc >= nxt.j1) nxt = next_cluster(cur.g + gridDim.x);
+        bool took = false;   // the next cluster taken from s_item[1], which thread 0 refills
+        if (nxt.jc >= nxt.j1) {
+            nxt = item(1);
+            took = nxt.g < Ck;
+        }
+        if (took && tid == 0) pend = atomicAdd(ctr_s + hh, 1);
         if (nxt.g < Ck) issue(smem + (bsel ^ 1) * PR_BUF, nxt);   // lands during this chunk's math
 
         const int nv = min(PR_KC, cur.j1 - cur.jc);
+        const int h = cur.h;
         if (cur.jc == cur.j0) {   // a new cluster: its centroids, P = ||vbar||^2, sbar; sums restart
+            if (h != bhead) {     // (and a new head: its query-centroid planes)
+                load_b(h);
+                bhead = h;
+            }
             const float* kbl = (const float*)(b + PR_KB) + 8 * sch;
             const float* vbl = (const float*)(b + PR_VB) + 8 * sch;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                kb8[e] = kbl[e];
-                vb8[e] = logit_only ? 0.f : vbl[e];
+            for (int e = 0; e < 8; ++e) vb8[e] = logit_only ? 0.f : vbl[e];
+            // A key (bf16) equals k-bar only where every coordinate of k-bar is a
+            // bf16 value; then the packed words are compared, the sign of a
+            // zero ignored.  Otherwise the pattern is a NaN no finite key holds.
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const unsigned lo = __float_as_uint(kbl[2 * w]), hi = __float_as_uint(kbl[2 * w + 1]);
+                const bool rep = ((lo | hi) & 0xFFFFu) == 0;
+                kbw[w] = rep ? (lo >> 16) | hi : 0x7FC07FC0u;
+                kmw[w] = ((lo & 0x7FFFFFFFu) == 0 ? 0x7FFFu : 0xFFFFu) |
+                         ((hi & 0x7FFFFFFFu) == 0 ? 0x7FFF0000u : 0xFFFF0000u);
             }
             P = 0.f;
 #pragma unroll
@@ -239,28 +333,42 @@ __global__ __launch_bounds__(256, 2) void k_probe_mfma(
                 S[i] = 0.f;
             }
         }
-        // per-key value terms and the equal-to-centroid flag, from the LDS rows
+        // Per-key coefficients from the LDS rows, delta = vbar - v_j:
+        //   R = ||delta||^2, beta0 = 2 vbar.delta, alpha0 = ||vbar||^2,
+        //   beta1 = 2 (R - vbar.delta) = -2 delta.v_j, alpha1 = ||v_j||^2 = alpha0 - beta0 + R;
+        // a key equal to its centroid keeps only R (its D is exactly zero), and
+        // rows past the chunk's keys are all zero.
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = srow + 16 * i;
             const u32x4_t kw = *(const u32x4_t*)(b + r * 256 + pr_pos(r, sch) * 16);
             const u32x4_t vw = *(const u32x4_t*)(b + PR_T + r * 256 + pr_pos(r, sch) * 16);
-            float qd = 0.f, rr = 0.f, ne = 0.f;
+            float qd = 0.f, rr = 0.f;
+            unsigned ne = 0;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) ne |= (kw[w] ^ kbw[w]) & kmw[w];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const unsigned kb = (e & 1) ? (kw[e >> 1] & 0xFFFF0000u) : (kw[e >> 1] << 16);
                 const unsigned vb = (e & 1) ? (vw[e >> 1] & 0xFFFF0000u) : (vw[e >> 1] << 16);
-                ne += __uint_as_float(kb) != kb8[e] ? 1.f : 0.f;
-                const float dl = logit_only ? 0.f : vb8[e] - __uint_as_float(vb);
+                const float dl = vb8[e] - __uint_as_float(vb);
                 qd = fmaf(vb8[e], dl, qd);
                 rr = fmaf(dl, dl, rr);
             }
+            // (the logit-only estimate loads no values: vbar = e_1 and delta = 0)
             qd = sum16(qd);
             rr = sum16(rr);
-            ne = sum16(ne);
-            if (sch == 0) s_ks[r] = make_float4(2.f * qd, rr, ne == 0.f ? 0.f : 1.f, 0.f);
+            ne = or16(ne);
+            if (logit_only) qd = rr = 0.f;
+            if (sch == 0) {
+                const bool live = r < nv, moved = ne != 0;
+                const float b0 = 2.f * qd;
+                s_ks[r] = live ? make_float4(moved ? fmaxf(P - b0 + rr, 0.f) : 0.f, moved ? b0 : 0.f,
+                                             moved ? 2.f * rr - b0 : 0.f, rr)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+                s_ka[r] = live && moved ? P : 0.f;
+            }
         }
-        __syncthreads();
+        lds_barrier();
 
         const int ntile = (nv + 15) / 16;
         for (int kt = 0; kt < ntile; ++kt) {
@@ -271,8 +379,12 @@ __global__ __launch_bounds__(256, 2) void k_probe_mfma(
                 ak[ks] = pr_as_bf16x8(*(const u32x4_t*)(b + arow * 256 + pr_pos(arow, 4 * ks + grp) * 16));
             const int kr0 = kt * 16 + 4 * grp;   // this lane's rows kr0 .. kr0 + 3
             float4 kq[4];
+            float ka[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) kq[r] = s_ks[kr0 + r];
+            for (int r = 0; r < 4; ++r) {
+                kq[r] = s_ks[kr0 + r];
+                ka[r] = s_ka[kr0 + r];
+            }
 #pragma unroll
             for (int i = 0; i < NCBW; ++i) {
                 if (cbw + 4 * i >= ncb) continue;   // wave-uniform
@@ -286,26 +398,25 @@ __global__ __launch_bounds__(256, 2) void k_probe_mfma(
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks)
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[ks], bl[i][ks], acc, 0, 0, 0);
-                // Per pair, with D = sbar - s (exactly 0 for a key equal to its
-                // centroid), w = e^{-|D|}, em = w - 1 and sigma = -w if D > 0
-                // else 1:  e = e^{2 sbar} e^{2 max(-D, 0)} f with
-                //   f = em^2 P + 2 em sigma vbar.delta + sigma^2 ||delta||^2,
-                // the bracket with the larger exponential factored out (no
-                // intermediate overflows however far the key lies from its
-                // centroid).  S sums f e^{u'} with u' = log2 e^{2 max(-D, 0)} - sh.
-                const bool tail = kt * 16 + 16 > nv;   // wave-uniform
+                // Per pair, D = sbar - s and em = expm1(-|D|):
+                //   D <= 0:  e = e^{2 s}    ||delta + em vbar||^2  = e^{2 sbar} e^{-2D} f,
+                //   D > 0:   e = e^{2 sbar} ||delta - em v_j||^2   = e^{2 sbar} f,
+                // f = (alpha em + beta) em + R with (alpha, beta) = (alpha0, beta0)
+                // or (alpha1, beta1): the larger exponential is factored out, so
+                // nothing overflows however far the key lies from its centroid.
+                // S sums f e^{u} with u = log2 e^{2 max(-D, 0)} - sh.
                 float f[4], u[4];
                 float umax = -__builtin_inff();
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float D = kq[r].z * fmaf(-tau, acc[r], sb[i]);
+                    const float D = fmaf(-tau, acc[r], sb[i]);
                     const float ad = fabsf(D);
                     const float w = __builtin_amdgcn_exp2f(-ad * kLog2e);   // e^{-|D|}
-                    const float em = expm1_nonpos(-ad, w);
-                    const float sg = D > 0.f ? -w : 1.f;
-                    const float sr = sg * kq[r].y;
-                    const float fr = fmaxf(fmaf(em, fmaf(em, P, sg * kq[r].x), sg * sr), 0.f);
-                    f[r] = (tail && kr0 + r >= nv) ? 0.f : fr;
+                    const float em = expm1_nonpos(ad, w);
+                    const bool pos = D > 0.f;
+                    const float al = pos ? kq[r].x : ka[r];
+                    const float be = pos ? kq[r].z : kq[r].y;
+                    f[r] = fmaxf(fmaf(fmaf(al, em, be), em, kq[r].w), 0.f);
                     u[r] = fmaf(2.f * kLog2e, fmaxf(-D, 0.f), -sh[i]);
                     umax = fmaxf(umax, u[r]);
                 }
@@ -344,12 +455,14 @@ __global__ __launch_bounds__(256, 2) void k_probe_mfma(
                 const int c = (cbw + 4 * i) * 16 + col;
                 if (grp == 0 && c < Cq) {
                     float lr = -__builtin_inff();
-                    if (counts_q[(size_t)h * Cq + c] > 0 && s2 > 0.f)
+                    if (qlive[i] && s2 > 0.f)
                         lr = 2.f * sb[i] + kLn2 * (m + __log2f(s2)) - logf((float)mg);
                     log_ratio[((size_t)h * Cq + c) * Ck + cur.g] = lr;
                 }
             }
         }
+        if (took && tid == 0)   // read by every thread before the barrier above
+            s_item[1] = pr_resolve(pend, hh, left, ctr_s, offsets_k, H, Cq, Ck, c_lo, c_hi, log_ratio);
         cur = nxt;
         bsel ^= 1;
     }
@@ -366,25 +479,30 @@ SVG_HIDDEN hipError_t launch_probe_mfma(const ProbeArgs& a, const float* sbar, h
     const int ncb = (a.Cq + 15) / 16;
     const int ncbw = ncb > 4 ? 2 : 1;                  // column blocks per wave
     const int slices = (ncb + 4 * ncbw - 1) / (4 * ncbw);
-    // about 1536 workgroups in all: two rounds of three per CU (measured best of
-    // 768 to 2304 at the Wan and HunyuanVideo shapes)
-    int gx = (1536 + a.H * slices - 1) / (a.H * slices);
-    if (gx > a.Ck) gx = a.Ck;
+    // one resident round: two workgroups per CU over the slices
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
+        ncu = 256;
+    long long gx = (2LL * ncu + slices - 1) / slices;
+    if (gx > (long long)a.H * a.Ck) gx = (long long)a.H * a.Ck;
+    int* ctr = (int*)(a.scratch + a.L->pr_ctr);
+    zero_words(ctr, (size_t)slices * a.H * 4, st);
     float* eps = (a.flags & SVGEAR_DEBUG_EPS) ? a.log_eps2 : nullptr;
     const int logit_only = (a.flags & SVGEAR_PROBE_LOGIT) ? 1 : 0;
     const float tau = 1.0f / sqrtf((float)PR_D);
 #define SVG_PROBE_CASE(n)                                                                          \
     case n:                                                                                        \
         if (eps)                                                                                   \
-            hipLaunchKernelGGL((k_probe_mfma<n, true>), dim3(gx, a.H, slices), dim3(256), PR_LDS2, st, \
+            hipLaunchKernelGGL((k_probe_mfma<n, true>), dim3((int)gx, slices), dim3(256), PR_LDS2, st,  \
                                a.qbar, a.counts_q, (const bf16*)a.Kp, (const bf16*)a.Vp, a.kbar,   \
-                               a.vbar, sbar, a.offsets_k, a.Nk, a.Cq, a.Ck, tau, logit_only,       \
-                               a.log_ratio, eps);                                                  \
+                               a.vbar, sbar, a.offsets_k, a.H, a.Nk, a.Cq, a.Ck, tau, logit_only,  \
+                               ctr, a.log_ratio, eps);                                                  \
         else                                                                                       \
-            hipLaunchKernelGGL((k_probe_mfma<n, false>), dim3(gx, a.H, slices), dim3(256), PR_LDS2, st, \
+            hipLaunchKernelGGL((k_probe_mfma<n, false>), dim3((int)gx, slices), dim3(256), PR_LDS2, st,  \
                                a.qbar, a.counts_q, (const bf16*)a.Kp, (const bf16*)a.Vp, a.kbar,   \
-                               a.vbar, sbar, a.offsets_k, a.Nk, a.Cq, a.Ck, tau, logit_only,       \
-                               a.log_ratio, eps);                                                  \
+                               a.vbar, sbar, a.offsets_k, a.H, a.Nk, a.Cq, a.Ck, tau, logit_only,  \
+                               ctr, a.log_ratio, eps);                                                  \
         break;
     switch (ncbw) {
         SVG_PROBE_CASE(1) SVG_PROBE_CASE(2)
