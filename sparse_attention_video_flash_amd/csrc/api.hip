@@ -82,6 +82,12 @@ SVG_HIDDEN Layout make_layout(const svgear_shape& s)
     L.pr_end = off;
 
     off = 0;
+    L.rt_hist = take(H * 4096 * 8);
+    L.rt_state = take(H * 24);
+    L.rt_part = take(H * 32 * 8);
+    L.rt_end = off;
+
+    off = 0;
     L.at_kvplanes = take(4 * H * Ck * d * 2);
     L.at_logm = take(H * Ck * 4);
     L.at_tiles = take(H * (Cq + 1) * 4 + 256);
@@ -96,6 +102,7 @@ SVG_HIDDEN Layout make_layout(const svgear_shape& s)
 
     size_t sc = L.cl_end;
     if (L.pr_end > sc) sc = L.pr_end;
+    if (L.rt_end > sc) sc = L.rt_end;
     if (L.at_end > sc) sc = L.at_end;
     L.scratch2 = L.scratch + align256(sc);
     L.total = L.scratch2 + L.cl_end;
@@ -427,6 +434,8 @@ SVG_API int svgear_route(const svgear_shape* shape, double rho, const float* log
     a.counts_k = counts_k;
     a.mask = mask;
     a.sel_cost = sel_cost;
+    a.scratch = (char*)ws + L.scratch;
+    a.L = &L;
     return finish(launch_route(a, (hipStream_t)stream), 0, (hipStream_t)stream, nullptr);
 }
 
@@ -584,6 +593,8 @@ SVG_API int svgear_forward(const svgear_shape* shape, double rho, const void* Q,
     ra.counts_k = counts_k;
     ra.mask = mask;
     ra.sel_cost = sel_cost;
+    ra.scratch = w + L.scratch;
+    ra.L = &L;
     if (launch_route(ra, st) != hipSuccess) return SVGEAR_E_HIP;
     rc = attention_impl(shape, Qp, offsets_q, perm_q, Kp, Vp, kbar, vbar, counts_k, offsets_k, mask,
                         O, ws, L, 0, st);

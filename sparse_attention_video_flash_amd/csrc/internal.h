@@ -241,6 +241,7 @@ struct Layout {
     // probe scratch (relative to scratch)
     size_t pr_sbar, pr_keys, pr_pg, pr_ctr;
     size_t pr_end;
+    size_t rt_hist, rt_state, rt_part, rt_end;   // route
     // attention scratch (relative to scratch)
     size_t at_kvplanes, at_logm, at_tiles, at_segs, at_cinfo, at_comp, at_rows, at_queue;
     size_t at_end;
@@ -323,8 +324,11 @@ struct RouteArgs {
     const int32_t* counts_k;
     uint8_t* mask;
     int64_t* sel_cost;
+    char* scratch;   // per-stage scratch (histograms and per-head states)
+    const Layout* L;
 };
 SVG_HIDDEN hipError_t launch_route(const RouteArgs& a, hipStream_t st);
+SVG_HIDDEN int route_slices(int H);
 SVG_HIDDEN hipError_t launch_route_rows(const RouteArgs& a, double rho, int Nk, hipStream_t st);
 SVG_HIDDEN void zero_words(void* p, size_t bytes, hipStream_t st);
 
