@@ -414,15 +414,18 @@ __device__ __forceinline__ void tile_pv(Softmax& st, const char* vbuf, const bf1
     __builtin_amdgcn_s_setprio(0);
 }
 
-// Tile rows past nvalid get -inf.
+// Tile rows past nvalid get -inf.  Row kb 32 + 8 (i / 4) + 4 half + i % 4 is
+// compared as the constant kb 32 + 8 (i / 4) + i % 4 against nvalid - 4 half
+// (no per-row index registers).
 __device__ __forceinline__ void mask_rows(f32x16_t x[2], int nvalid, int half)
 {
+    const int lim = nvalid - 4 * half;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int kt = kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-            x[kb][i] = kt < nvalid ? x[kb][i] : -__builtin_inff();
+            const int kt = kb * 32 + (i >> 2) * 8 + (i & 3);
+            x[kb][i] = kt < lim ? x[kb][i] : -__builtin_inff();
         }
 }
 

@@ -156,6 +156,30 @@ def test_probe_ratios_and_eps_match_oracle(case):
         log("  head %d: max ratio dev %.2e, max eps dev %.2e" % (h, float(dev.max()), float(devj.max())))
 
 
+@pytest.mark.parametrize("case", ["ragged", "small"])
+def test_probe_repeats_bit_for_bit(case):
+    """The probe hands key clusters to workgroups at run time (per-head claim
+    counters); a cluster's estimate must not depend on which workgroup took it
+    or when: repeated calls agree bit for bit."""
+    torch = torch_gpu()
+    w = CASES[case]
+    log("probe repeatability %s" % case)
+    data = upload(w)
+    refs = _oracle_all(w, data, w.rhos[0])
+    H = len(refs)
+    shape = shape_of(w, H)
+    ws = sv.alloc_workspace(shape)
+    P = _probe_inputs(w, data, refs)
+    outs = []
+    for rep in range(8):
+        lr = torch.empty(H, w.Cq, w.Ck, device="cuda")
+        sv.probe(shape, P["qbar"], P["counts_q"], P["Kp"], P["Vp"], P["kbar"], P["vbar"], P["counts_k"],
+                 P["offsets_k"], lr, ws)
+        outs.append(lr.cpu())
+    for rep in range(1, 8):
+        assert torch.equal(outs[rep], outs[0]), "call %d differs from call 0" % rep
+
+
 @pytest.mark.parametrize("case", ["tiny", "ragged", "small"])
 def test_probe_logit_only_matches_oracle(case):
     """The logit-only estimate (SVGEAR_PROBE_LOGIT) against the oracle's, with the
