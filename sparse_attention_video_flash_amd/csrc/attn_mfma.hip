@@ -472,23 +472,15 @@ __device__ __forceinline__ void tile_fill(char* b, __amdgpu_buffer_rsrc_t rk, __
 // position -> reordered key row, written by the whole workgroup into its own
 // slot of device memory from the segment table tab (in LDS, ns entries
 // (end_s, delta_s): positions end_{s-1} .. end_s - 1 hold rows position +
-// delta_s).  Thread t fills a run of consecutive positions: a binary search
-// finds the segment of its first position, then it walks forward.
-__device__ __forceinline__ void row_list(int* __restrict__ w, const int2* __restrict__ tab, int ns, int nk)
+// delta_s).  Wave w writes segments w, w + 8, ..., its lanes consecutive
+// positions of the segment, so every store is coalesced.
+__device__ __forceinline__ void row_list(int* __restrict__ w, const int2* __restrict__ tab, int ns)
 {
-    const int per = (nk + AT_THREADS - 1) / AT_THREADS;
-    const int q0 = (int)threadIdx.x * per;
-    const int q1 = min(q0 + per, nk);
-    if (q0 >= q1) return;
-    int lo = 0, hi = ns - 1;   // first segment whose end exceeds q0
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (tab[mid].x > q0) hi = mid; else lo = mid + 1;
-    }
-    int2 e = tab[lo];
-    for (int q = q0; q < q1; ++q) {
-        while (e.x <= q) e = tab[++lo];
-        w[q] = q + e.y;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int s = wave; s < ns; s += AT_WAVES) {
+        const int2 e = tab[s];
+        const int begin = s > 0 ? tab[s - 1].x : 0;
+        for (int q = begin + lane; q < e.x; q += 64) w[q] = q + e.y;
     }
 }
 
@@ -713,7 +705,7 @@ __device__ __forceinline__ void attn_tile(
         const int2* sgh = segs + hc * Ck;
         for (int k = tid; k < ns; k += AT_THREADS) tab[k] = sgh[k];
         __syncthreads();
-        row_list(rows, tab, ns, nk);
+        row_list(rows, tab, ns);
         __syncthreads();   // the slot's rows are visible to every wave of the workgroup
         exact_tiles(KBUF(0), KBUF(1), st, qf, rk, rv, rows, nk, wave, lane, wact, scale2);
     }
