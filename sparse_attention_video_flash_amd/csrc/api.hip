@@ -88,7 +88,7 @@ SVG_HIDDEN Layout make_layout(const svgear_shape& s)
     L.rt_end = off;
 
     off = 0;
-    L.at_kvplanes = take(4 * H * Ck * d * 2);
+    L.at_kvplanes = take(3 * H * Ck * d * 2);
     L.at_logm = take(H * Ck * 4);
     L.at_tiles = take(H * (Cq + 1) * 4 + 256);
     L.at_segs = take(H * Cq * Ck * 8);

@@ -15,8 +15,9 @@
 // Key tiles of BN = 64 rows, packed: a tile takes the next 64 entries of the
 // cluster's key list, so no tile is padded at a key-cluster boundary.
 //   1. compensation tiles: the centroids of the key clusters that are skipped
-//      for c and non-empty, split into bf16 hi + lo planes (k-bar and v-bar are
-//      fp32), with logit tau q.kbar_g + ln m_g;
+//      for c and non-empty, with logit tau q.kbar_g + ln m_g: k-bar (fp32) split
+//      into bf16 hi + lo planes, since the logit enters an exponential; v-bar
+//      rounded once to bf16, as every value and weight of the PV product is;
 //   2. exact tiles: the keys of every routed key cluster.
 // Both kinds are gathered by row index straight from global memory into LDS
 // (buffer loads with the lds flag), two buffers deep, the next tile's loads in
@@ -52,9 +53,9 @@ constexpr int ROW_B = AT_D * 2;          // 256
 constexpr int T_BUF = AT_BN * ROW_B;     // 16384
 constexpr int AT_NBUF = 2;
 constexpr int K_PITCH = AT_D * 2 + 16;   // output staging rows (272 B)
-// Compensation tiles: k-bar hi, k-bar lo, v-bar hi, v-bar lo planes of 64
+// Compensation tiles: k-bar hi, k-bar lo and v-bar (bf16) planes of 64
 // centroids per buffer, two buffers, then the two buffers' biases.
-constexpr int C_BUF = 4 * T_BUF;
+constexpr int C_BUF = 3 * T_BUF;
 constexpr int C_AREA = 2 * C_BUF + 2 * AT_BN * 4;
 constexpr int at_max(int a, int b) { return a > b ? a : b; }
 constexpr int AT_AREA = at_max(C_AREA, at_max(AT_NBUF * 2 * T_BUF, AT_BM * K_PITCH));
@@ -76,20 +77,19 @@ __device__ __forceinline__ int v_pos(int r, int c) { return c ^ ((r & 3) << 2); 
 
 // ----------------------------------------------------------------------------- prep kernels
 
-// Split centroids into bf16 hi/lo planes; ln m_g in base-2 units (-inf if empty).
+// k-bar split into bf16 hi/lo planes, v-bar rounded to bf16; ln m_g in base-2
+// units (-inf if empty).
 __global__ void k_comp_planes(const float* __restrict__ kbar, const float* __restrict__ vbar,
                               const int32_t* __restrict__ counts_k, int Ck, bf16* __restrict__ kbh,
-                              bf16* __restrict__ kbl, bf16* __restrict__ vbh, bf16* __restrict__ vbl,
-                              float* __restrict__ logm2)
+                              bf16* __restrict__ kbl, bf16* __restrict__ vbh, float* __restrict__ logm2)
 {
     const int g = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
     const size_t i = ((size_t)h * Ck + g) * AT_D + t;
     const float k = kbar[i], v = vbar[i];
-    const bf16 kh = f32_to_bf16(k), vh = f32_to_bf16(v);
+    const bf16 kh = f32_to_bf16(k);
     kbh[i] = kh;
     kbl[i] = f32_to_bf16(k - bf16_to_f32(kh));
-    vbh[i] = vh;
-    vbl[i] = f32_to_bf16(v - bf16_to_f32(vh));
+    vbh[i] = f32_to_bf16(v);
     if (t == 0) {
         const int m = counts_k[(size_t)h * Ck + g];
         logm2[(size_t)h * Ck + g] = m > 0 ? log2f((float)m) : -__builtin_inff();
@@ -544,13 +544,13 @@ __device__ __forceinline__ void exact_tiles(char* __restrict__ b0, char* __restr
 
 // The compensation tiles of one query tile: the key clusters skipped for this
 // query cluster and non-empty (packed list cl, nc entries), 64 per tile.  A
-// tile holds the bf16 hi and lo planes of k-bar and v-bar of its centroids and
-// their biases log2 m_g; like the exact tiles, its rows are gathered by index
+// tile holds the bf16 hi and lo planes of k-bar, v-bar in bf16, and the
+// biases log2 m_g of its centroids; like the exact tiles, its rows are gathered by index
 // straight into LDS (the bias with one dword load per lane, by wave 0), two
 // buffers deep, the next tile's loads in flight during the current tile's math.
 __device__ __forceinline__ void comp_fill(char* b, float* bias, __amdgpu_buffer_rsrc_t rkh,
                                           __amdgpu_buffer_rsrc_t rkl, __amdgpu_buffer_rsrc_t rvh,
-                                          __amdgpu_buffer_rsrc_t rvl, __amdgpu_buffer_rsrc_t rlm, int wv,
+                                          __amdgpu_buffer_rsrc_t rlm, int wv,
                                           const int r[FILL_N], int br, const int kx[FILL_N], int vx)
 {
     char* kh = b + FILL_ROWS * wv * ROW_B;
@@ -562,7 +562,6 @@ __device__ __forceinline__ void comp_fill(char* b, float* bias, __amdgpu_buffer_
 #pragma unroll
     for (int i = 0; i < FILL_N; ++i) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rvh, (lds_ptr)(kh + 2 * T_BUF + 4 * i * ROW_B), 16, r[i] * ROW_B + vx, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rvl, (lds_ptr)(kh + 3 * T_BUF + 4 * i * ROW_B), 16, r[i] * ROW_B + vx, 0, 0, 0);
     }
     if (wv == 0) __builtin_amdgcn_raw_ptr_buffer_load_lds(rlm, (lds_ptr)bias, 4, br * 4, 0, 0, 0);
 }
@@ -570,7 +569,7 @@ __device__ __forceinline__ void comp_fill(char* b, float* bias, __amdgpu_buffer_
 __device__ __forceinline__ void comp_tiles(char* __restrict__ c0, char* __restrict__ c1, float* __restrict__ bias0,
                                            float* __restrict__ bias1, Softmax& st, const bf16x8_t qf[8],
                                            __amdgpu_buffer_rsrc_t rkh, __amdgpu_buffer_rsrc_t rkl,
-                                           __amdgpu_buffer_rsrc_t rvh, __amdgpu_buffer_rsrc_t rvl,
+                                           __amdgpu_buffer_rsrc_t rvh,
                                            __amdgpu_buffer_rsrc_t rlm, const int* __restrict__ cl, int nc,
                                            int wave, int lane, bool wact, float scale2)
 {
@@ -589,13 +588,13 @@ __device__ __forceinline__ void comp_tiles(char* __restrict__ c0, char* __restri
     B = cl[min((T) * AT_BN + lane, nc - 1)];
     CROWS(ra, ba, 0)
     CROWS(rb, bb, 1)
-    comp_fill(c0, bias0, rkh, rkl, rvh, rvl, rlm, wv, ra, ba, kx, vx);
+    comp_fill(c0, bias0, rkh, rkl, rvh, rlm, wv, ra, ba, kx, vx);
     __builtin_amdgcn_s_waitcnt(0x0F70 | 0);
     tile_barrier();
 #define COMP_STEP(T, CUR, NXT, BCUR, BNXT, RT, BT, RN, BN)                                    \
     {                                                                                         \
         CROWS(RT, BT, (T) + 2)           /* rows of tile T + 2 (set of tile T, now free) */   \
-        comp_fill(NXT, BNXT, rkh, rkl, rvh, rvl, rlm, wv, RN, BN, kx, vx);   /* tile T + 1 */ \
+        comp_fill(NXT, BNXT, rkh, rkl, rvh, rlm, wv, RN, BN, kx, vx);   /* tile T + 1 */      \
         if (wact && (T) < ntiles) {                                                           \
             f32x16_t acc[2] = {f32x16_t{0}, f32x16_t{0}};                                     \
             tile_scores(acc, CUR, qf, lane);                                                  \
@@ -611,7 +610,6 @@ __device__ __forceinline__ void comp_tiles(char* __restrict__ c0, char* __restri
             bf16x8_t pf[4];                                                                   \
             softmax_update(st, acc, scale2, pf);                                              \
             tile_pv(st, CUR + 2 * T_BUF, pf, lane);                                           \
-            tile_pv(st, CUR + 3 * T_BUF, pf, lane);                                           \
         }                                                                                     \
         __builtin_amdgcn_s_waitcnt(0x0F70 | 0);   /* tile T + 1 and rows of T + 2 landed */   \
         tile_barrier();                                                                       \
@@ -634,7 +632,7 @@ __device__ __forceinline__ void attn_tile(
     int logical, char* smem, const bf16* __restrict__ Qp,
     const int32_t* __restrict__ offsets_q, const int32_t* __restrict__ perm_q,
     const bf16* __restrict__ Kp, const bf16* __restrict__ Vp, const bf16* __restrict__ kbh,
-    const bf16* __restrict__ kbl, const bf16* __restrict__ vbh, const bf16* __restrict__ vbl,
+    const bf16* __restrict__ kbl, const bf16* __restrict__ vbh,
     const float* __restrict__ logm2, const int2* __restrict__ segs, const int4* __restrict__ cinfo,
     const int* __restrict__ comp, const int* __restrict__ tstart, int* __restrict__ rows, int Nq,
     int Nk, int Cq, int Ck, int tiles_per_head, float scale2, bf16* __restrict__ O)
@@ -683,10 +681,9 @@ __device__ __forceinline__ void attn_tile(
         const __amdgpu_buffer_rsrc_t rkh = __builtin_amdgcn_make_buffer_rsrc((void*)(kbh + pb), (short)0, plane_bytes, 0x00020000);
         const __amdgpu_buffer_rsrc_t rkl = __builtin_amdgcn_make_buffer_rsrc((void*)(kbl + pb), (short)0, plane_bytes, 0x00020000);
         const __amdgpu_buffer_rsrc_t rvh = __builtin_amdgcn_make_buffer_rsrc((void*)(vbh + pb), (short)0, plane_bytes, 0x00020000);
-        const __amdgpu_buffer_rsrc_t rvl = __builtin_amdgcn_make_buffer_rsrc((void*)(vbl + pb), (short)0, plane_bytes, 0x00020000);
         const __amdgpu_buffer_rsrc_t rlm = __builtin_amdgcn_make_buffer_rsrc((void*)lm, (short)0, Ck * 4, 0x00020000);
         float* const cb = (float*)(smem + 2 * C_BUF);
-        comp_tiles(smem, smem + C_BUF, cb, cb + AT_BN, st, qf, rkh, rkl, rvh, rvl, rlm, comp + hc * Ck, nc, wave,
+        comp_tiles(smem, smem + C_BUF, cb, cb + AT_BN, st, qf, rkh, rkl, rvh, rlm, comp + hc * Ck, nc, wave,
                    lane, wact, scale2);
     }
 
@@ -742,7 +739,7 @@ __device__ __forceinline__ void attn_tile(
     }
 }
 
-// planes: the k-bar hi, k-bar lo, v-bar hi and v-bar lo planes, [H, Ck, d] each,
+// planes: the k-bar hi, k-bar lo and v-bar planes, [H, Ck, d] bf16 each,
 // one after another; qmeta: the work-queue region (lengths, starts, counters,
 // per-head counts and prefixes, then the queue itself).
 __global__ __launch_bounds__(AT_THREADS, 2) void k_attn_mfma(
@@ -759,7 +756,6 @@ __global__ __launch_bounds__(AT_THREADS, 2) void k_attn_mfma(
     const bf16* const kbh = planes;
     const bf16* const kbl = planes + plane;
     const bf16* const vbh = planes + 2 * plane;
-    const bf16* const vbl = planes + 3 * plane;
     int* const qctr = qmeta + 2 * AT_XCD;
     const int* const qlist = qmeta + 3 * AT_XCD + (size_t)H * AT_XCD + (size_t)H * Cq;
 
@@ -774,7 +770,7 @@ __global__ __launch_bounds__(AT_THREADS, 2) void k_attn_mfma(
             const int j = *s_job;
             if (j >= qlen) break;
             attn_tile(qlist[qstart + j], smem, Qp, offsets_q, perm_q, Kp, Vp, kbh, kbl,
-                      vbh, vbl, logm2, segs, cinfo, comp, tstart, rowbuf + (size_t)blockIdx.x * Nk, Nq,
+                      vbh, logm2, segs, cinfo, comp, tstart, rowbuf + (size_t)blockIdx.x * Nk, Nq,
                       Nk, Cq, Ck, tiles_per_head, scale2, O);
         }
     }
@@ -797,14 +793,13 @@ SVG_HIDDEN hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t st)
     bf16* kbh = (bf16*)(s + L.at_kvplanes);
     bf16* kbl = kbh + plane;
     bf16* vbh = kbl + plane;
-    bf16* vbl = vbh + plane;
     float* logm2 = (float*)(s + L.at_logm);
     int* tstart = (int*)(s + L.at_tiles);
     int2* segs = (int2*)(s + L.at_segs);
     int4* cinfo = (int4*)(s + L.at_cinfo);
     int* comp = (int*)(s + L.at_comp);
     hipLaunchKernelGGL(k_comp_planes, dim3(a.Ck, a.H), dim3(AT_D), 0, st, a.kbar, a.vbar, a.counts_k,
-                       a.Ck, kbh, kbl, vbh, vbl, logm2);
+                       a.Ck, kbh, kbl, vbh, logm2);
     hipLaunchKernelGGL(k_seg_list, dim3(a.Cq, a.H), dim3(256), (2 * a.Ck + 1) * 4, st, a.mask, a.offsets_k, a.Cq,
                        a.Ck, segs, cinfo, comp);
     hipLaunchKernelGGL(k_tile_prefix, dim3(a.H), dim3(1024), 0, st, a.offsets_q, a.Cq, tstart);
