@@ -249,13 +249,14 @@ __global__ __launch_bounds__(256) void k_bucket(const int32_t* __restrict__ labe
 constexpr int MC_ROWS = 512;
 
 enum : int { CH_ONE = 0, CH_ONE_COLLECT = 1, CH_TWO = 2 };
-template <typename T, int D, int MODE>
+template <typename T, int D, int MODE, bool GATHER>
 __global__ __launch_bounds__(256) void k_cluster_chunks(const T* __restrict__ X,
                                                         const int32_t* __restrict__ perm,
                                                         const int32_t* __restrict__ offsets, int N,
                                                         int C, unsigned* __restrict__ range,
                                                         unsigned long long* __restrict__ sums,
-                                                        const int* __restrict__ changed, int rev)
+                                                        const int* __restrict__ changed, int rev,
+                                                        uint4* __restrict__ Xp)
 {
     constexpr bool TWO = MODE == CH_TWO, COLLECT = MODE == CH_ONE_COLLECT;
     constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
@@ -304,15 +305,23 @@ __global__ __launch_bounds__(256) void k_cluster_chunks(const T* __restrict__ X,
             }
             if (COLLECT) { rgx.add_min(w.x); rgx.add_min(w.y); rgx.add_min(w.z); rgx.add_min(w.w); }
         };
+        // GATHER (the final pass): the rows are also written out in bucket order
+        auto put = [&](int jj, const uint4 w) {
+            if (GATHER) Xp[((size_t)h * N + p0 + jj) * CPR + ch] = w;
+        };
         int j = a0 + rg;
         for (; j + 3 * RPP < a1; j += 4 * RPP) {
             uint4 w[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) w[u] = *(const uint4*)(Xh + (size_t)s_idx[j + u * RPP] * D);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) add_row(w[u]);
+            for (int u = 0; u < 4; ++u) { put(j + u * RPP, w[u]); add_row(w[u]); }
         }
-        for (; j < a1; j += RPP) add_row(*(const uint4*)(Xh + (size_t)s_idx[j] * D));
+        for (; j < a1; j += RPP) {
+            const uint4 w = *(const uint4*)(Xh + (size_t)s_idx[j] * D);
+            put(j, w);
+            add_row(w);
+        }
         // remove the offset carried by every accumulated image; reduce the
         // first word's row groups, then (if summed) the second word's
         const unsigned long long rows = (unsigned long long)((a1 - a0 - rg + RPP - 1) / RPP);
@@ -572,7 +581,7 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ lab
     }
     s_pos[threadIdx.x] = pos;
     __syncthreads();
-    if (!X) return;
+    if (!X && !V) return;
     const int rows = min(kTile, N - tile * kTile);
     using R = typename RangeOf<T>::type;
     R rx, rv;
@@ -582,16 +591,18 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ lab
         if (p < 0) continue;
         const size_t src = ((size_t)h * N + tile * kTile + r) * row_chunks + ch;
         const size_t dst = ((size_t)h * N + p) * row_chunks + ch;
-        const uint4 xw = X[src];
-        Xp[dst] = xw;
-        if (range_x) { rx.add_max(xw.x); rx.add_max(xw.y); rx.add_max(xw.z); rx.add_max(xw.w); }
+        if (X) {
+            const uint4 xw = X[src];
+            Xp[dst] = xw;
+            if (range_x) { rx.add_max(xw.x); rx.add_max(xw.y); rx.add_max(xw.z); rx.add_max(xw.w); }
+        }
         if (V) {
             const uint4 vw = V[src];
             Vp[dst] = vw;
             rv.add_max(vw.x); rv.add_max(vw.y); rv.add_max(vw.z); rv.add_max(vw.w);
         }
     }
-    if (range_x) range_commit(rx.max_word(), 0u, range_x + kRangeStride * h, false);
+    if (X && range_x) range_commit(rx.max_word(), 0u, range_x + kRangeStride * h, false);
     if (V) range_commit(rv.max_word(), 0u, range_v + kRangeStride * h, false);
 }
 
@@ -632,23 +643,31 @@ static hipError_t run_cluster(const ClusterArgs& a, hipStream_t st)
     // means forward), so each starts on the heads the previous one just read,
     // which the last-level cache still holds.
     auto chunk_pass = [&](const T* src, unsigned* rg, const int32_t* order, const int* chg, int collect,
-                          int rev) {
+                          int rev, uint4* xp) {
+        // (a collecting pass runs only while the range is unknown, before any gather)
         if (collect) {
-            hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_ONE_COLLECT>), gchunks, dim3(256), 0, st, src, order,
-                               a.offsets, N, C, rg, sums, chg, rev);
+            hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_ONE_COLLECT, false>), gchunks, dim3(256), 0, st, src,
+                               order, a.offsets, N, C, rg, sums, chg, rev, (uint4*)nullptr);
             hipLaunchKernelGGL(k_clear_two_word_heads, dim3(16, H), dim3(256), 0, st, rg, N, kPrec,
                                (size_t)C * D, sums);
+        } else if (xp) {
+            hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_ONE, true>), gchunks, dim3(256), 0, st, src, order,
+                               a.offsets, N, C, rg, sums, chg, rev, xp);
         } else {
-            hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_ONE>), gchunks, dim3(256), 0, st, src, order,
-                               a.offsets, N, C, rg, sums, chg, rev);
+            hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_ONE, false>), gchunks, dim3(256), 0, st, src, order,
+                               a.offsets, N, C, rg, sums, chg, rev, xp);
         }
-        hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_TWO>), gchunks, dim3(256), 0, st, src, order,
-                           a.offsets, N, C, rg, sums, chg, rev);
+        if (xp)
+            hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_TWO, true>), gchunks, dim3(256), 0, st, src, order,
+                               a.offsets, N, C, rg, sums, chg, rev, xp);
+        else
+            hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_TWO, false>), gchunks, dim3(256), 0, st, src, order,
+                               a.offsets, N, C, rg, sums, chg, rev, xp);
     };
     // plain mean pass (no planes); checks the range
     auto mean_pass = [&](const T* src, unsigned* rg, const int32_t* order, int collect, int zero_empty,
-                         float* out, int rev) {
-        chunk_pass(src, rg, order, (const int*)nullptr, collect, rev);
+                         float* out, int rev, uint4* xp) {
+        chunk_pass(src, rg, order, (const int*)nullptr, collect, rev, xp);
         hipLaunchKernelGGL((k_cluster_finalize<D, false>), gfin, dim3(256), 0, st, a.counts, C, N,
                            rg, kPrec, collect, err, zero_empty, sums, cent64, out, (bf16*)nullptr,
                            (bf16*)nullptr, (float*)nullptr, (double*)nullptr, (float*)nullptr,
@@ -703,7 +722,7 @@ static hipError_t run_cluster(const ClusterArgs& a, hipStream_t st)
             if (mfma && D == 128) {
                 const int* chg = it > 0 ? changed : nullptr;
                 // the first update reads every row: it also records the smallest magnitude
-                chunk_pass(X, range_x, pwork, chg, it == 0 ? 1 : 0, 1);
+                chunk_pass(X, range_x, pwork, chg, it == 0 ? 1 : 0, 1, nullptr);
                 hipLaunchKernelGGL((k_cluster_finalize<D, D == 128>), gfin, dim3(256), 0, st, a.counts,
                                    C, N, range_x, kPrec, it == 0 ? 1 : 0, it == 0 ? err : nullptr, 0, sums,
                                    cent64, (float*)nullptr, P.hi, P.lo, P.cn32, P.cn64, resid, chg, moved);
@@ -713,7 +732,7 @@ static hipError_t run_cluster(const ClusterArgs& a, hipStream_t st)
                                    P.mlist, P.mpos, P.mcount);
             } else {
                 // the first update reads every row: it also records the smallest magnitude
-                mean_pass(X, range_x, pwork, it == 0 ? 1 : 0, 0, (float*)nullptr, 1);
+                mean_pass(X, range_x, pwork, it == 0 ? 1 : 0, 0, (float*)nullptr, 1, nullptr);
             }
         }
     }
@@ -726,13 +745,17 @@ static hipError_t run_cluster(const ClusterArgs& a, hipStream_t st)
     const int row_chunks = (int)(D * sizeof(T) / 16);
     const bool given = (a.flags & SVGEAR_LABELS_GIVEN) != 0;
     const bool x_known = !given && a.iters >= 2;
+    // With the range of X known, the final mean pass gathers the rows of X
+    // itself (they are read there anyway); otherwise the scatter does, since
+    // the mean pass needs the largest magnitude first.
     hipLaunchKernelGGL((k_scatter<T>), gtiles, dim3(256), 0, st, a.labels, N, C, ntiles, hist, a.offsets,
-                       a.perm, a.inv_perm, (const uint4*)a.X, (uint4*)a.Xp, (const uint4*)a.V,
-                       (uint4*)a.Vp, row_chunks, x_known ? nullptr : range_x, range_v, 1);
-    mean_pass(X, range_x, a.perm, x_known ? 0 : 1, given ? 1 : 0, a.cent, 0);
+                       a.perm, a.inv_perm, x_known ? nullptr : (const uint4*)a.X, (uint4*)a.Xp,
+                       (const uint4*)a.V, (uint4*)a.Vp, row_chunks, x_known ? nullptr : range_x, range_v, 1);
+    mean_pass(X, range_x, a.perm, x_known ? 0 : 1, given ? 1 : 0, a.cent, 0,
+              x_known ? (uint4*)a.Xp : nullptr);
     // V-bar: mean of V over the key clusters (zero for an empty cluster).  cent64
     // is no longer needed and serves as scratch.
-    if (a.side == 1) mean_pass((const T*)a.V, range_v, a.perm, 1, 1, a.vbar, 0);
+    if (a.side == 1) mean_pass((const T*)a.V, range_v, a.perm, 1, 1, a.vbar, 0, nullptr);
     return hipGetLastError();
 }
 

@@ -105,6 +105,12 @@ def test_kmeans_labels_and_centroids_match_oracle(case):
             np.testing.assert_array_equal(out["labels"][hi].cpu().numpy(), lab)
             np.testing.assert_array_equal(out["counts"][hi].cpu().numpy(), counts)
             np.testing.assert_array_equal(out["cent"][hi].cpu().numpy(), cent.astype(np.float32))
+            # the reorder: a stable sort by label, rows gathered in that order
+            perm = oracle.permutation(lab, C)[2]
+            np.testing.assert_array_equal(out["perm"][hi].cpu().numpy(), perm)
+            np.testing.assert_array_equal(out["Xp"][hi].float().cpu().numpy(), Xh[hi][perm])
+            if side == 1:
+                np.testing.assert_array_equal(out["Vp"][hi].float().cpu().numpy(), v[hi][perm])
 
 
 # ----------------------------------------------------------------------------- steps 2-3
