@@ -414,6 +414,79 @@ __device__ __forceinline__ void tile_pv(Softmax& st, const char* vbuf, const bf1
     __builtin_amdgcn_s_setprio(0);
 }
 
+// softmax_update and tile_pv fused, with the same arithmetic in the same
+// order: the weights of keys 16 kk .. 16 kk + 15 are formed while the MFMAs
+// of the previous 16 keys run, and the transpose reads of each k-step are
+// issued one step ahead, so the exponentials overlap the matrix work of the
+// same wave instead of preceding it.
+__device__ __forceinline__ void softmax_pv(Softmax& st, const f32x16_t x[2], float scale2, const char* vbuf,
+                                           int lane)
+{
+    float mloc = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, x[kb][i]);
+    mloc = pair_max(mloc) * scale2;
+    if (__any(mloc > st.m + kLazy)) {
+        const float mnew = fmaxf(st.m, mloc);
+        const float alpha = __builtin_amdgcn_exp2f(st.m - mnew);   // 0 while st.m = -inf
+        st.l *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) st.o[db] *= alpha;
+        st.m = mnew;
+    }
+    const float muse = st.m == -__builtin_inff() ? 0.f : st.m;
+    const bf16x2_t one = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
+    float sum = st.l;
+    // the V^T fragments as in tile_pv
+    const int j = lane & 15, grp = lane >> 4;
+    const int half = grp >> 1;
+    const int jr = (j >> 2) & 3;
+    const char* base = vbuf + (4 * half + (j >> 2)) * ROW_B + (2 * (grp & 1) + ((j >> 1) & 1)) * 16 + (j & 1) * 8;
+    auto vfrag = [&](int kk, int db) {
+        const char* a = base + (16 * kk) * ROW_B + (db ^ jr) * 64;
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a);
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a + 8 * ROW_B));
+        const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+        return as_bf16x8(u32x4_t{l2[0], l2[1], h2[0], h2[1]});
+    };
+    // weights of keys 16 kk + 2 pr, + 1 (pr = 0..3), packed into f
+    auto weights2 = [&](int kk, int pr, bf16x8_t& f) {
+        const int kb = kk >> 1, ks = kk & 1;
+#pragma unroll
+        for (int i = 2 * pr; i < 2 * pr + 2; ++i)
+            f[i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(x[kb][8 * ks + i], scale2, -muse));
+        sum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{f[2 * pr], f[2 * pr + 1]}, one, sum, false);
+        asm volatile("" : "+v"(sum));   // keeps the sum's step in its slot of the schedule
+    };
+    __builtin_amdgcn_s_setprio(1);
+    bf16x8_t vf[2][4];
+    bf16x8_t pf[2];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) vf[0][db] = vfrag(0, db);
+#pragma unroll
+    for (int pr = 0; pr < 4; ++pr) weights2(0, pr, pf[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    // step kk: each MFMA is followed by the reads of one fragment of step
+    // kk + 1 and a quarter of its weights; the order is pinned so that the
+    // exponentials issue while the MFMA before them runs
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+            st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kk & 1][db], pf[kk & 1], st.o[db], 0, 0, 0);
+            if (kk + 1 < 4) {
+                vf[(kk + 1) & 1][db] = vfrag(kk + 1, db);
+                weights2(kk + 1, db, pf[(kk + 1) & 1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    st.l = sum;
+    __builtin_amdgcn_s_setprio(0);
+}
+
 // Tile rows past nvalid get -inf.  Row kb 32 + 8 (i / 4) + 4 half + i % 4 is
 // compared as the constant kb 32 + 8 (i / 4) + i % 4 against nvalid - 4 half
 // (no per-row index registers).
@@ -525,9 +598,7 @@ __device__ __forceinline__ void exact_tiles(char* __restrict__ b0, char* __restr
             tile_scores(acc, CUR, qf, lane);                                                  \
             const int nvalid = nk - (T) * AT_BN;                                              \
             if (nvalid < AT_BN) mask_rows(acc, nvalid, half);                                 \
-            bf16x8_t pf[4];                                                                   \
-            softmax_update(st, acc, scale2, pf);                                              \
-            tile_pv(st, CUR + T_BUF, pf, lane);                                               \
+            softmax_pv(st, acc, scale2, CUR + T_BUF, lane);                                   \
         }                                                                                     \
         __builtin_amdgcn_s_waitcnt(0x0F70 | 0);   /* tile T + 1 landed */                     \
         tile_barrier();                                                                       \
@@ -607,9 +678,7 @@ __device__ __forceinline__ void comp_tiles(char* __restrict__ c0, char* __restri
                 }                                                                             \
             const int nvalid = nc - (T) * AT_BN;                                              \
             if (nvalid < AT_BN) mask_rows(acc, nvalid, half);                                 \
-            bf16x8_t pf[4];                                                                   \
-            softmax_update(st, acc, scale2, pf);                                              \
-            tile_pv(st, CUR + 2 * T_BUF, pf, lane);                                           \
+            softmax_pv(st, acc, scale2, CUR + 2 * T_BUF, lane);                               \
         }                                                                                     \
         __builtin_amdgcn_s_waitcnt(0x0F70 | 0);   /* tile T + 1 and rows of T + 2 landed */   \
         tile_barrier();                                                                       \
