@@ -338,24 +338,39 @@ __global__ __launch_bounds__(256, 3) void k_assign_mfma(
 }
 
 // The moved centroids (list mlist[h, 0 .. mcount)) staged like km_load; rows
-// past the list get ||c||^2 = +inf.
+// past the list get ||c||^2 = +inf.  In two parts, so that the list entries
+// can be requested before the token rows and the centroid rows after them.
 template <int CB>
-__device__ __forceinline__ void km_load_list(KmStage<KmChunk<CB, true>::NV>& s,
-                                             const bf16* __restrict__ hi, const bf16* __restrict__ lo,
-                                             const float* __restrict__ cn,
-                                             const int* __restrict__ ml, int k0, int cnt, int tid)
+struct KmListIdx {
+    int m[CB / 16];   // list entries of rows r, r + 16, ...
+    int mc;           // list entry of centroid tid (the ||c||^2 lane)
+};
+template <int CB>
+__device__ __forceinline__ void km_list_idx(KmListIdx<CB>& ix, const int* __restrict__ ml, int k0, int cnt,
+                                            int tid)
 {
-    const int ch = tid & 15, r = tid >> 4;
+    const int r = tid >> 4;
 #pragma unroll
     for (int i = 0; i < CB / 16; ++i) {
         const int k = k0 + r + 16 * i;
-        const bool ok = k < cnt;
-        const int m = ok ? ml[k] : 0;
+        ix.m[i] = k < cnt ? ml[k] : -1;
+    }
+    ix.mc = (tid < CB && k0 + tid < cnt) ? ml[k0 + tid] : -1;
+}
+template <int CB>
+__device__ __forceinline__ void km_list_rows(KmStage<KmChunk<CB, true>::NV>& s, const KmListIdx<CB>& ix,
+                                             const bf16* __restrict__ hi, const bf16* __restrict__ lo,
+                                             const float* __restrict__ cn, int tid)
+{
+    const int ch = tid & 15;
+#pragma unroll
+    for (int i = 0; i < CB / 16; ++i) {
+        const int m = ix.m[i];
+        const bool ok = m >= 0;
         s.v[i] = ok ? *(const u32x4_t*)(hi + (size_t)m * KM_D + ch * 8) : u32x4_t{0, 0, 0, 0};
         s.v[CB / 16 + i] = ok ? *(const u32x4_t*)(lo + (size_t)m * KM_D + ch * 8) : u32x4_t{0, 0, 0, 0};
     }
-    const bool okc = tid < CB && k0 + tid < cnt;
-    s.cn = okc ? cn[ml[k0 + tid]] : __builtin_inff();
+    s.cn = ix.mc >= 0 ? cn[ix.mc] : __builtin_inff();
 }
 
 // Iterations after the first: screen against the moved centroids only and
@@ -381,24 +396,40 @@ __global__ __launch_bounds__(256, 3) void k_assign_partial(
     const int cnt = mcount[h];
     if (!km_partial_pays(cnt, C)) return;   // k_assign_mfma takes this head
 
-    bf16x8_t xf[2][8];
-    float nx[2];
-    int tok[2], own[2];
-    float pub[2], plb[2], plr[2];   // stored bounds, fetched before the screen so their latency overlaps it
+    // Requests in dependency order: the first chunk's list entries and the
+    // labels, then the token rows, then what depends on the first two (the
+    // chunk's centroid rows, the labels' list positions), so that the chains
+    // of dependent loads overlap the token rows instead of following them.
+    using K = KmPartialChunk;
+    constexpr int CB = 32;
+    const int nchunk = (cnt + CB - 1) / CB;
+    KmListIdx<CB> ix;
+    km_list_idx<CB>(ix, ml, 0, cnt, tid);
+    int tok[2], lab[2], own[2];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
         tok[tb] = blockIdx.x * KM_TOK + wave * 64 + tb * 32 + tcol;
+        lab[tb] = labels[(size_t)h * N + (tok[tb] < N ? tok[tb] : N - 1)];
+    }
+    bf16x8_t xf[2][8];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
         const int row = tok[tb] < N ? tok[tb] : N - 1;
-        own[tb] = mpos[(size_t)h * C + labels[(size_t)h * N + row]];   // list position or -1
-        pub[tb] = ub_own[(size_t)h * N + row];
-        plb[tb] = lb_own[(size_t)h * N + row];
-        plr[tb] = lb_rest[(size_t)h * N + row];
         const bf16* xp = Xh + (size_t)row * KM_D + half * 8;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) xf[tb][s] = as_bf16x8(*(const u32x4_t*)(xp + 16 * s));
+    }
+    KmStage<K::NV> stg;
+    km_list_rows<CB>(stg, ix, hih, loh, cnh, tid);
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) own[tb] = mpos[(size_t)h * C + lab[tb]];   // list position or -1
+    float nx[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
         float ss = 0.f;
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-            const u32x4_t w = *(const u32x4_t*)(xp + 16 * s);
-            xf[tb][s] = as_bf16x8(w);
+            const u32x4_t w = __builtin_bit_cast(u32x4_t, xf[tb][s]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float a = __uint_as_float(w[e] << 16), b = __uint_as_float(w[e] & 0xFFFF0000u);
@@ -421,15 +452,15 @@ __global__ __launch_bounds__(256, 3) void k_assign_partial(
     }
 
     // Single-buffered chunks (the moved list is short after the first few
-    // iterations; it keeps the registers within the three-workgroup limit).
-    using K = KmPartialChunk;
-    constexpr int CB = 32;
-    const int nchunk = (cnt + CB - 1) / CB;
+    // iterations; it keeps the registers within the three-workgroup limit);
+    // the first chunk's rows were requested with the token rows.
     for (int k = 0; k < nchunk; ++k) {
         char* const buf = smem;
         {
-            KmStage<K::NV> stg;
-            km_load_list<CB>(stg, hih, loh, cnh, ml, k * CB, cnt, tid);
+            if (k > 0) {
+                km_list_idx<CB>(ix, ml, k * CB, cnt, tid);
+                km_list_rows<CB>(stg, ix, hih, loh, cnh, tid);
+            }
             __syncthreads();   // the previous chunk's readers are done
             km_store<CB, true>(stg, buf, tid);
             __syncthreads();
@@ -463,6 +494,16 @@ __global__ __launch_bounds__(256, 3) void k_assign_partial(
 
     const float R = __uint_as_float(stats[4 * h + 0]);
     const float cmax = __uint_as_float(stats[4 * h + 1]);
+    // the stored bounds, fetched only now (held through the screen they would
+    // be spilled, and each spill would wait for its load)
+    float pub[2], plb[2], plr[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+        const size_t t = (size_t)h * N + (tok[tb] < N ? tok[tb] : N - 1);
+        pub[tb] = ub_own[t];
+        plb[tb] = lb_own[t];
+        plr[tb] = lb_rest[t];
+    }
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
         const float pb1 = __shfl_xor(b1[tb], 32), pb2 = __shfl_xor(b2[tb], 32);
