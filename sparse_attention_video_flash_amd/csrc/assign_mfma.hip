@@ -227,6 +227,13 @@ __global__ __launch_bounds__(256, 3) void k_assign_mfma(
     const bf16* loh = lo + (size_t)h * C * KM_D;
     const float* cnh = cn32 + (size_t)h * C;
 
+    constexpr int CB = KmScreen<LO>::CB;
+    using K = typename KmScreen<LO>::Chunk;
+    const int nchunk = (C + CB - 1) / CB;
+    KmStage<K::NV> stg;
+    // the first chunk is requested together with the token rows
+    km_load<CB, LO>(stg, hih, loh, cnh, 0, C, tid);
+
     // Token fragments (B operand): token tok[tb], dims 16 s + 8 half + 0..7.
     bf16x8_t xf[2][8];
     float nx[2];
@@ -236,11 +243,15 @@ __global__ __launch_bounds__(256, 3) void k_assign_mfma(
         tok[tb] = blockIdx.x * KM_TOK + wave * 64 + tb * 32 + tcol;
         const int row = tok[tb] < N ? tok[tb] : N - 1;
         const bf16* xp = Xh + (size_t)row * KM_D + half * 8;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) xf[tb][s] = as_bf16x8(*(const u32x4_t*)(xp + 16 * s));
+    }
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
         float ss = 0.f;
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-            const u32x4_t w = *(const u32x4_t*)(xp + 16 * s);
-            xf[tb][s] = as_bf16x8(w);
+            const u32x4_t w = __builtin_bit_cast(u32x4_t, xf[tb][s]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float a = __uint_as_float(w[e] << 16), b = __uint_as_float(w[e] & 0xFFFF0000u);
@@ -273,11 +284,6 @@ __global__ __launch_bounds__(256, 3) void k_assign_mfma(
         i1[tb] = 0;
     }
 
-    constexpr int CB = KmScreen<LO>::CB;
-    using K = typename KmScreen<LO>::Chunk;
-    const int nchunk = (C + CB - 1) / CB;
-    KmStage<K::NV> stg;
-    km_load<CB, LO>(stg, hih, loh, cnh, 0, C, tid);
     km_store<CB, LO>(stg, smem, tid);
     __syncthreads();
     for (int k = 0; k < nchunk; ++k) {

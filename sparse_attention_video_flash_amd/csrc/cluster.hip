@@ -270,82 +270,90 @@ __global__ __launch_bounds__(256) void k_cluster_chunks(const T* __restrict__ X,
     unsigned* rg4 = range + kRangeStride * h;
     if (TWO ? !fix_need_lo(rg4, base, PREC) : (!COLLECT && fix_need_lo(rg4, base, PREC)))
         return;   // a head the other instantiation serves
-    const int p0 = blockIdx.x * MC_ROWS;
-    if (p0 >= N) return;
-    const int p1 = min(N, p0 + MC_ROWS);
     const int32_t* oh = offsets + (size_t)h * (C + 1);
     const int ch = threadIdx.x % CPR, rg = threadIdx.x / CPR;
     const T* Xh = X + (size_t)h * N * D + ch * EPC;
     const double sc = ldexp(1.0, base - fix_exp(rg4[0])), tc = ldexp(1.0, base);
     unsigned long long* sums_lo = sums + (size_t)gridDim.y * C * D;
+    const int* chh = changed ? changed + (size_t)h * C : nullptr;
     using R = typename RangeOf<T>::type;
     R rgx;
-    for (int k = threadIdx.x; k < p1 - p0; k += 256) s_idx[k] = perm[(size_t)h * N + p0 + k];
-    // first cluster whose range ends after p0
-    int lo_c = 0, hi_c = C - 1;
-    while (lo_c < hi_c) {
-        const int mid = (lo_c + hi_c) >> 1;
-        if (oh[mid + 1] > p0) hi_c = mid; else lo_c = mid + 1;
-    }
-    __syncthreads();
-    const int* chh = changed ? changed + (size_t)h * C : nullptr;
-    for (int m = lo_c; m < C && oh[m] < p1; ++m) {
-        const int a0 = max(oh[m], p0) - p0, a1 = min(oh[m + 1], p1) - p0;
-        if (a1 <= a0) continue;
-        if (chh && !chh[m]) continue;   // membership unchanged: its mean is unchanged
-        unsigned long long ah[EPC], al[EPC];
+    // chunks of MC_ROWS positions, gridDim.x apart (the two-word kernel, which
+    // serves few heads if any, runs on a smaller grid)
+    for (int p0 = blockIdx.x * MC_ROWS; p0 < N; p0 += (int)gridDim.x * MC_ROWS) {
+        const int p1 = min(N, p0 + MC_ROWS);
+        // first cluster whose range ends after p0
+        int lo_c = 0, hi_c = C - 1;
+        while (lo_c < hi_c) {
+            const int mid = (lo_c + hi_c) >> 1;
+            if (oh[mid + 1] > p0) hi_c = mid; else lo_c = mid + 1;
+        }
+        if (chh) {   // no changed cluster in the chunk: nothing to sum
+            bool any = false;
+            for (int m = lo_c; m < C && oh[m] < p1 && !any; ++m) any = chh[m] != 0 && oh[m + 1] > oh[m];
+            if (!any) continue;
+        }
+        __syncthreads();   // the previous chunk's readers of s_idx are done
+        for (int k = threadIdx.x; k < p1 - p0; k += 256) s_idx[k] = perm[(size_t)h * N + p0 + k];
+        __syncthreads();
+        for (int m = lo_c; m < C && oh[m] < p1; ++m) {
+            const int a0 = max(oh[m], p0) - p0, a1 = min(oh[m + 1], p1) - p0;
+            if (a1 <= a0) continue;
+            if (chh && !chh[m]) continue;   // membership unchanged: its mean is unchanged
+            unsigned long long ah[EPC], al[EPC];
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) ah[e] = al[e] = 0;
-        auto add_row = [&](const uint4 w) {
-            const T* v = (const T*)&w;
+            for (int e = 0; e < EPC; ++e) ah[e] = al[e] = 0;
+            auto add_row = [&](const uint4 w) {
+                const T* v = (const T*)&w;
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) {
-                if (TWO) fix_add<T>(v[e], sc, tc, ah[e], al[e]);
-                else ah[e] += fix_hi<T>(v[e], sc);
+                for (int e = 0; e < EPC; ++e) {
+                    if (TWO) fix_add<T>(v[e], sc, tc, ah[e], al[e]);
+                    else ah[e] += fix_hi<T>(v[e], sc);
+                }
+                if (COLLECT) { rgx.add_min(w.x); rgx.add_min(w.y); rgx.add_min(w.z); rgx.add_min(w.w); }
+            };
+            // GATHER (the final pass): the rows are also written out in bucket order
+            auto put = [&](int jj, const uint4 w) {
+                if (GATHER) Xp[((size_t)h * N + p0 + jj) * CPR + ch] = w;
+            };
+            int j = a0 + rg;
+            for (; j + 3 * RPP < a1; j += 4 * RPP) {
+                uint4 w[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) w[u] = *(const uint4*)(Xh + (size_t)s_idx[j + u * RPP] * D);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) { put(j + u * RPP, w[u]); add_row(w[u]); }
             }
-            if (COLLECT) { rgx.add_min(w.x); rgx.add_min(w.y); rgx.add_min(w.z); rgx.add_min(w.w); }
-        };
-        // GATHER (the final pass): the rows are also written out in bucket order
-        auto put = [&](int jj, const uint4 w) {
-            if (GATHER) Xp[((size_t)h * N + p0 + jj) * CPR + ch] = w;
-        };
-        int j = a0 + rg;
-        for (; j + 3 * RPP < a1; j += 4 * RPP) {
-            uint4 w[4];
+            for (; j < a1; j += RPP) {
+                const uint4 w = *(const uint4*)(Xh + (size_t)s_idx[j] * D);
+                put(j, w);
+                add_row(w);
+            }
+            // remove the offset carried by every accumulated image; reduce the
+            // first word's row groups, then (if summed) the second word's
+            const unsigned long long rows = (unsigned long long)((a1 - a0 - rg + RPP - 1) / RPP);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) w[u] = *(const uint4*)(Xh + (size_t)s_idx[j + u * RPP] * D);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) { put(j + u * RPP, w[u]); add_row(w[u]); }
-        }
-        for (; j < a1; j += RPP) {
-            const uint4 w = *(const uint4*)(Xh + (size_t)s_idx[j] * D);
-            put(j, w);
-            add_row(w);
-        }
-        // remove the offset carried by every accumulated image; reduce the
-        // first word's row groups, then (if summed) the second word's
-        const unsigned long long rows = (unsigned long long)((a1 - a0 - rg + RPP - 1) / RPP);
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) s_sum[rg][ch * EPC + e] = (long long)(ah[e] - rows * kFixMagicBits);
-        __syncthreads();
-        if ((int)threadIdx.x < D) {
-            long long tot = 0;
-#pragma unroll
-            for (int g = 0; g < RPP; ++g) tot += s_sum[g][threadIdx.x];
-            atomicAdd(sums + ((size_t)h * C + m) * D + threadIdx.x, (unsigned long long)tot);
-        }
-        __syncthreads();
-        if (TWO) {
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) s_sum[rg][ch * EPC + e] = (long long)(al[e] - rows * kFixMagicBits);
+            for (int e = 0; e < EPC; ++e) s_sum[rg][ch * EPC + e] = (long long)(ah[e] - rows * kFixMagicBits);
             __syncthreads();
             if ((int)threadIdx.x < D) {
                 long long tot = 0;
 #pragma unroll
                 for (int g = 0; g < RPP; ++g) tot += s_sum[g][threadIdx.x];
-                atomicAdd(sums_lo + ((size_t)h * C + m) * D + threadIdx.x, (unsigned long long)tot);
+                atomicAdd(sums + ((size_t)h * C + m) * D + threadIdx.x, (unsigned long long)tot);
             }
             __syncthreads();
+            if (TWO) {
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) s_sum[rg][ch * EPC + e] = (long long)(al[e] - rows * kFixMagicBits);
+                __syncthreads();
+                if ((int)threadIdx.x < D) {
+                    long long tot = 0;
+#pragma unroll
+                    for (int g = 0; g < RPP; ++g) tot += s_sum[g][threadIdx.x];
+                    atomicAdd(sums_lo + ((size_t)h * C + m) * D + threadIdx.x, (unsigned long long)tot);
+                }
+                __syncthreads();
+            }
         }
     }
     if (COLLECT) range_commit(0u, rgx.min_word(), rg4, true);
@@ -630,7 +638,8 @@ static hipError_t run_cluster(const ClusterArgs& a, hipStream_t st)
     unsigned* range = (unsigned*)(s + L.cl_range);
     unsigned* range_x = range;
     unsigned* range_v = range + 2;
-    const dim3 gchunks((N + MC_ROWS - 1) / MC_ROWS, H), gfin((C + 3) / 4 < 64 ? (C + 3) / 4 : 64, H);
+    const int nchunks = (N + MC_ROWS - 1) / MC_ROWS;
+    const dim3 gchunks(nchunks, H), gtwo(nchunks < 16 ? nchunks : 16, H), gfin((C + 3) / 4 < 64 ? (C + 3) / 4 : 64, H);
     zero_words(sums, (size_t)2 * H * C * D * 8, st);
     zero_words(range, (size_t)H * kRangeStride * 4, st);
     // plain mean pass (no planes)
@@ -658,10 +667,10 @@ static hipError_t run_cluster(const ClusterArgs& a, hipStream_t st)
                                a.offsets, N, C, rg, sums, chg, rev, xp);
         }
         if (xp)
-            hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_TWO, true>), gchunks, dim3(256), 0, st, src, order,
+            hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_TWO, true>), gtwo, dim3(256), 0, st, src, order,
                                a.offsets, N, C, rg, sums, chg, rev, xp);
         else
-            hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_TWO, false>), gchunks, dim3(256), 0, st, src, order,
+            hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_TWO, false>), gtwo, dim3(256), 0, st, src, order,
                                a.offsets, N, C, rg, sums, chg, rev, xp);
     };
     // plain mean pass (no planes); checks the range
