@@ -72,6 +72,11 @@ SVG_HIDDEN Layout make_layout(const svgear_shape& s)
     L.cl_mlist = take(H * C * 4);
     L.cl_mpos = take(H * C * 4);
     L.cl_mcount = take(H * 4);
+    L.cl_perm2 = take(H * N * 4);            // the previous update's bucket order
+    L.cl_offs = take(2 * H * (C + 1) * 4);   // bucket offsets, current and previous
+    L.cl_tokflag = take(H * N);              // per token: label changed in the last assignment
+    L.cl_ipos = take(2 * H * N * 4);         // per token: its position in the current / previous bucket order
+    L.cl_fpos = take(2 * H * N);             // the token flags by position in those orders
     L.cl_end = off;
 
     off = 0;

@@ -209,10 +209,14 @@ __global__ __launch_bounds__(1024) void k_count_scan(const int32_t* __restrict__
 // Unstable bucket fill: every token goes to its cluster's range (order within a
 // cluster does not matter to the exact sums).  Ranks inside a tile come from
 // LDS atomics.
+// With tokflag (the delta updates of the k-means): also each token's position
+// (ipos) and its flag by position (fpos).
 __global__ __launch_bounds__(256) void k_bucket(const int32_t* __restrict__ labels, int N, int C,
                                                 int ntiles, const int* __restrict__ hist,
                                                 const int32_t* __restrict__ offsets,
-                                                int32_t* __restrict__ perm)
+                                                int32_t* __restrict__ perm,
+                                                const uint8_t* __restrict__ tokflag,
+                                                int32_t* __restrict__ ipos, uint8_t* __restrict__ fpos)
 {
     extern __shared__ int s_r[];
     const int tile = blockIdx.x, h = blockIdx.y;
@@ -226,6 +230,10 @@ __global__ __launch_bounds__(256) void k_bucket(const int32_t* __restrict__ labe
             const int pos =
                 offsets[(size_t)h * (C + 1) + l] + hist[((size_t)h * ntiles + tile) * C + l] + rank;
             perm[(size_t)h * N + pos] = i;
+            if (tokflag) {
+                ipos[(size_t)h * N + i] = pos;
+                fpos[(size_t)h * N + pos] = tokflag[(size_t)h * N + i];
+            }
         }
     }
 }
@@ -246,25 +254,49 @@ __global__ __launch_bounds__(256) void k_bucket(const int32_t* __restrict__ labe
 // head and records the smallest non-zero magnitude; a head that then turns out
 // to need the second word has its sums cleared (k_clear_two_word_heads) and
 // redone by the two-word kernel.
+//
+// DELTA: an update after the first, which adds to the running sums (kept from
+// the previous update) only the rows of the tokens whose label changed:
+// blockIdx.z = 0 walks the current bucket order (perm1, offsets1, flags1: each
+// such token joins its new cluster), blockIdx.z = 1 the previous iteration's
+// bucket order (perm2, offsets2, flags2: it leaves its old one, its image
+// negated, which is exact).  The flags are stored by bucket position.  The
+// sums are integers, so the result equals a full re-summation bit for bit.  A
+// chunk packs its flagged rows' token indices to the front of s_idx and cuts
+// the cluster segments at the prefix sums of the flags.
 constexpr int MC_ROWS = 512;
 
 enum : int { CH_ONE = 0, CH_ONE_COLLECT = 1, CH_TWO = 2 };
-template <typename T, int D, int MODE, bool GATHER>
+template <typename T, int D, int MODE, bool GATHER, bool DELTA>
 __global__ __launch_bounds__(256) void k_cluster_chunks(const T* __restrict__ X,
-                                                        const int32_t* __restrict__ perm,
-                                                        const int32_t* __restrict__ offsets, int N,
+                                                        const int32_t* __restrict__ perm1,
+                                                        const int32_t* __restrict__ offsets1, int N,
                                                         int C, unsigned* __restrict__ range,
                                                         unsigned long long* __restrict__ sums,
                                                         const int* __restrict__ changed, int rev,
-                                                        uint4* __restrict__ Xp)
+                                                        uint4* __restrict__ Xp,
+                                                        const uint8_t* __restrict__ flags1,
+                                                        const int32_t* __restrict__ perm2,
+                                                        const int32_t* __restrict__ offsets2,
+                                                        const uint8_t* __restrict__ flags2)
 {
+    static_assert(!DELTA || (MODE != CH_ONE_COLLECT && !GATHER), "delta passes neither collect nor gather");
     constexpr bool TWO = MODE == CH_TWO, COLLECT = MODE == CH_ONE_COLLECT;
+    constexpr unsigned kSign = sizeof(T) == 2 ? 0x80008000u : 0x80000000u;   // negates every element of a word
     constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
     constexpr int CPR = D / EPC;               // chunks per row
     constexpr int RPP = 256 / CPR;             // rows per pass
     constexpr int PREC = sizeof(T) == 2 ? 8 : 24;
     __shared__ long long s_sum[RPP][D];
-    __shared__ int s_idx[MC_ROWS];
+    // delta passes touch few rows per position: longer chunks, fewer workgroups
+    constexpr int ROWS = DELTA ? 4 * MC_ROWS : MC_ROWS;
+    constexpr int PPT = ROWS / 256;   // positions per thread in the flag scan
+    __shared__ int s_idx[ROWS];
+    __shared__ int s_pre[DELTA ? ROWS + 1 : 1];   // exclusive prefix sums of the chunk's flags
+    __shared__ int s_first, s_wsum[4];
+    const bool neg = DELTA && blockIdx.z == 1;
+    const int32_t* const perm = neg ? perm2 : perm1;
+    const int32_t* const offsets = neg ? offsets2 : offsets1;
     const int h = rev ? (int)gridDim.y - 1 - (int)blockIdx.y : (int)blockIdx.y;
     const int base = fix_base(N);
     unsigned* rg4 = range + kRangeStride * h;
@@ -278,32 +310,80 @@ __global__ __launch_bounds__(256) void k_cluster_chunks(const T* __restrict__ X,
     const int* chh = changed ? changed + (size_t)h * C : nullptr;
     using R = typename RangeOf<T>::type;
     R rgx;
-    // chunks of MC_ROWS positions, gridDim.x apart (the two-word kernel, which
+    // chunks of ROWS positions, gridDim.x apart (the two-word kernel, which
     // serves few heads if any, runs on a smaller grid)
-    for (int p0 = blockIdx.x * MC_ROWS; p0 < N; p0 += (int)gridDim.x * MC_ROWS) {
-        const int p1 = min(N, p0 + MC_ROWS);
-        // first cluster whose range ends after p0
-        int lo_c = 0, hi_c = C - 1;
-        while (lo_c < hi_c) {
-            const int mid = (lo_c + hi_c) >> 1;
-            if (oh[mid + 1] > p0) hi_c = mid; else lo_c = mid + 1;
+    for (int p0 = blockIdx.x * ROWS; p0 < N; p0 += (int)gridDim.x * ROWS) {
+        const int p1 = min(N, p0 + ROWS);
+        // first cluster whose range ends after p0: the number of clusters that
+        // end at or before it (the offsets do not decrease), counted in parallel
+        __syncthreads();   // the previous chunk is done with s_idx, s_first and s_wsum
+        if (threadIdx.x == 0) s_first = 0;
+        __syncthreads();
+        {
+            int n_before = 0;
+            for (int m = threadIdx.x; m < C; m += 256) n_before += oh[m + 1] <= p0;
+            if (n_before) atomicAdd(&s_first, n_before);
         }
+        __syncthreads();
+        const int lo_c = s_first;
         if (chh) {   // no changed cluster in the chunk: nothing to sum
             bool any = false;
-            for (int m = lo_c; m < C && oh[m] < p1 && !any; ++m) any = chh[m] != 0 && oh[m + 1] > oh[m];
-            if (!any) continue;
+            for (int m = lo_c + (int)threadIdx.x; m < C && oh[m] < p1; m += 256)
+                any |= chh[m] != 0 && oh[m + 1] > oh[m];
+            if (__syncthreads_or(any) == 0) continue;
         }
-        __syncthreads();   // the previous chunk's readers of s_idx are done
-        for (int k = threadIdx.x; k < p1 - p0; k += 256) s_idx[k] = perm[(size_t)h * N + p0 + k];
-        __syncthreads();
+        if (!DELTA) {
+            for (int k = threadIdx.x; k < p1 - p0; k += 256) s_idx[k] = perm[(size_t)h * N + p0 + k];
+            __syncthreads();
+        } else {
+            // PPT consecutive positions per thread: flags (stored in bucket
+            // order), block-wide exclusive scan, then the flagged rows' token
+            // indices packed to the front in order
+            const uint8_t* const fl = (neg ? flags2 : flags1) + (size_t)h * N + p0;
+            const int n = p1 - p0, k0 = PPT * (int)threadIdx.x;
+            int fk[PPT];
+            int cnt = 0;
+#pragma unroll
+            for (int i = 0; i < PPT; ++i) {
+                fk[i] = k0 + i < n ? fl[k0 + i] : 0;
+                cnt += fk[i];
+            }
+            // inclusive scan within each wave, then across the four waves
+            const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+            int incl = cnt;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int v = __shfl_up(incl, o);
+                if (lane >= o) incl += v;
+            }
+            if (lane == 63) s_wsum[wave] = incl;
+            __syncthreads();
+#pragma unroll
+            for (int w = 0; w < 3; ++w) incl += w < wave ? s_wsum[w] : 0;
+            int ex = incl - cnt;
+            if (k0 < n && k0 + PPT >= n) s_pre[n] = incl;   // the thread holding the last position
+#pragma unroll
+            for (int i = 0; i < PPT; ++i) {
+                if (k0 + i < n) s_pre[k0 + i] = ex;
+                if (fk[i]) s_idx[ex] = perm[(size_t)h * N + p0 + k0 + i];
+                ex += fk[i];
+            }
+            __syncthreads();
+            if (s_pre[n] == 0) continue;   // no flagged row in the chunk (uniform)
+        }
         for (int m = lo_c; m < C && oh[m] < p1; ++m) {
-            const int a0 = max(oh[m], p0) - p0, a1 = min(oh[m + 1], p1) - p0;
+            int a0 = max(oh[m], p0) - p0, a1 = min(oh[m + 1], p1) - p0;
+            if (DELTA && a1 > a0) {   // the segment's flagged rows, packed
+                a0 = s_pre[a0];
+                a1 = s_pre[a1];
+            }
             if (a1 <= a0) continue;
             if (chh && !chh[m]) continue;   // membership unchanged: its mean is unchanged
             unsigned long long ah[EPC], al[EPC];
 #pragma unroll
             for (int e = 0; e < EPC; ++e) ah[e] = al[e] = 0;
-            auto add_row = [&](const uint4 w) {
+            auto add_row = [&](uint4 w) {
+                if (neg) { w.x ^= kSign; w.y ^= kSign; w.z ^= kSign; w.w ^= kSign; }
                 const T* v = (const T*)&w;
 #pragma unroll
                 for (int e = 0; e < EPC; ++e) {
@@ -400,7 +480,7 @@ __global__ __launch_bounds__(256) void k_cluster_finalize(
     float* __restrict__ cent_out,
     bf16* __restrict__ hi, bf16* __restrict__ lo, float* __restrict__ cn32,
     double* __restrict__ cn64, float* __restrict__ resid, const int* __restrict__ changed,
-    int* __restrict__ moved)
+    int* __restrict__ moved, int keep)
 {
     constexpr int EPL = D / 64;
     const int h = blockIdx.y;
@@ -426,8 +506,10 @@ __global__ __launch_bounds__(256) void k_cluster_finalize(
                 c = fix_value(sums[i], need_lo ? sums_lo[i] : 0ull, inv_s, inv_t) / (double)n;
                 mv |= c != cent64[i];
                 cent64[i] = c;
-                sums[i] = 0ull;
-                if (need_lo) sums_lo[i] = 0ull;
+                if (!keep) {   // the next pass sums from zero (keep: the next update adds to them)
+                    sums[i] = 0ull;
+                    if (need_lo) sums_lo[i] = 0ull;
+                }
             } else if (zero_empty) {
                 c = 0.0;
                 cent64[i] = c;
@@ -467,23 +549,36 @@ __global__ __launch_bounds__(256) void k_cluster_finalize(
 // Label changes of one assignment: both clusters of every token whose label
 // changed are marked (their members, hence their means, changed); the labels are
 // then kept for the next comparison.  With mark == 0 only the copy is made.
+// tokflag: per token, whether its label changed (all set with mark == 0).
 __global__ __launch_bounds__(256) void k_label_diff(const int32_t* __restrict__ labels,
                                                     int32_t* __restrict__ prev, int N, int C,
-                                                    int mark, int* __restrict__ changed)
+                                                    int mark, int* __restrict__ changed,
+                                                    uint8_t* __restrict__ tokflag,
+                                                    const int32_t* __restrict__ ipos_prev,
+                                                    uint8_t* __restrict__ fpos_prev)
 {
     const int h = blockIdx.y;
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= N) return;
     const size_t t = (size_t)h * N + i;
     const int now = labels[t];
+    bool moved = true;
     if (mark) {
         const int was = prev[t];
-        if (now != was) {
+        moved = now != was;
+        if (moved) {
             if (was >= 0 && was < C) changed[(size_t)h * C + was] = 1;
             if (now >= 0 && now < C) changed[(size_t)h * C + now] = 1;
         }
     }
     prev[t] = now;
+    if (tokflag) tokflag[t] = moved ? 1 : 0;
+    // the flag also by the token's position in the previous bucket order (every
+    // token with a valid label had one)
+    if (mark && fpos_prev) {
+        const int ip = ipos_prev[t];
+        if (ip >= 0 && ip < N) fpos_prev[(size_t)h * N + ip] = moved ? 1 : 0;
+    }
 }
 
 // Per head: the ascending list of moved centroids (the only ones the next
@@ -652,43 +747,55 @@ static hipError_t run_cluster(const ClusterArgs& a, hipStream_t st)
     // means forward), so each starts on the heads the previous one just read,
     // which the last-level cache still holds.
     auto chunk_pass = [&](const T* src, unsigned* rg, const int32_t* order, const int* chg, int collect,
-                          int rev, uint4* xp) {
+                          int rev, uint4* xp, const int32_t* offs) {
+        const uint8_t* nf = nullptr;
         // (a collecting pass runs only while the range is unknown, before any gather)
         if (collect) {
-            hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_ONE_COLLECT, false>), gchunks, dim3(256), 0, st, src,
-                               order, a.offsets, N, C, rg, sums, chg, rev, (uint4*)nullptr);
+            hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_ONE_COLLECT, false, false>), gchunks, dim3(256), 0, st,
+                               src, order, offs, N, C, rg, sums, chg, rev, (uint4*)nullptr, nf, order, offs, nf);
             hipLaunchKernelGGL(k_clear_two_word_heads, dim3(16, H), dim3(256), 0, st, rg, N, kPrec,
                                (size_t)C * D, sums);
         } else if (xp) {
-            hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_ONE, true>), gchunks, dim3(256), 0, st, src, order,
-                               a.offsets, N, C, rg, sums, chg, rev, xp);
+            hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_ONE, true, false>), gchunks, dim3(256), 0, st, src, order,
+                               offs, N, C, rg, sums, chg, rev, xp, nf, order, offs, nf);
         } else {
-            hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_ONE, false>), gchunks, dim3(256), 0, st, src, order,
-                               a.offsets, N, C, rg, sums, chg, rev, xp);
+            hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_ONE, false, false>), gchunks, dim3(256), 0, st, src, order,
+                               offs, N, C, rg, sums, chg, rev, xp, nf, order, offs, nf);
         }
         if (xp)
-            hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_TWO, true>), gtwo, dim3(256), 0, st, src, order,
-                               a.offsets, N, C, rg, sums, chg, rev, xp);
+            hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_TWO, true, false>), gtwo, dim3(256), 0, st, src, order,
+                               offs, N, C, rg, sums, chg, rev, xp, nf, order, offs, nf);
         else
-            hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_TWO, false>), gtwo, dim3(256), 0, st, src, order,
-                               a.offsets, N, C, rg, sums, chg, rev, xp);
+            hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_TWO, false, false>), gtwo, dim3(256), 0, st, src, order,
+                               offs, N, C, rg, sums, chg, rev, xp, nf, order, offs, nf);
+    };
+    // an update after the first: the flagged tokens join their clusters (current
+    // bucket order) and leave their previous ones (previous bucket order)
+    auto delta_pass = [&](const int32_t* order, const int32_t* offs, const uint8_t* flags,
+                          const int32_t* order_prev, const int32_t* offs_prev, const uint8_t* flags_prev,
+                          const int* chg) {
+        const int nd = (N + 4 * MC_ROWS - 1) / (4 * MC_ROWS);   // the delta passes' longer chunks
+        hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_ONE, false, true>), dim3(nd, H, 2), dim3(256), 0, st, X,
+                           order, offs, N, C, range_x, sums, chg, 1, (uint4*)nullptr, flags, order_prev, offs_prev, flags_prev);
+        hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_TWO, false, true>), dim3(nd < 16 ? nd : 16, H, 2), dim3(256), 0, st, X,
+                           order, offs, N, C, range_x, sums, chg, 1, (uint4*)nullptr, flags, order_prev, offs_prev, flags_prev);
     };
     // plain mean pass (no planes); checks the range
     auto mean_pass = [&](const T* src, unsigned* rg, const int32_t* order, int collect, int zero_empty,
                          float* out, int rev, uint4* xp) {
-        chunk_pass(src, rg, order, (const int*)nullptr, collect, rev, xp);
+        chunk_pass(src, rg, order, (const int*)nullptr, collect, rev, xp, a.offsets);
         hipLaunchKernelGGL((k_cluster_finalize<D, false>), gfin, dim3(256), 0, st, a.counts, C, N,
                            rg, kPrec, collect, err, zero_empty, sums, cent64, out, (bf16*)nullptr,
                            (bf16*)nullptr, (float*)nullptr, (double*)nullptr, (float*)nullptr,
-                           (const int*)nullptr, (int*)nullptr);
+                           (const int*)nullptr, (int*)nullptr, 0);
     };
 
     // counting-sort front half: tile histograms, per-label tile prefixes, counts, offsets
-    auto sort_front = [&](unsigned* stats, int* nflag) {
+    auto sort_front = [&](unsigned* stats, int* nflag, int32_t* offs) {
         hipLaunchKernelGGL(k_tile_hist, gtiles, dim3(256), (size_t)C * 4, st, a.labels, N, C,
                            ntiles, hist, err);
         hipLaunchKernelGGL(k_hist_cols, gcols, dim3(256), 0, st, hist, C, ntiles, a.counts);
-        hipLaunchKernelGGL(k_count_scan, dim3(H), dim3(1024), 0, st, a.counts, C, a.offsets, stats,
+        hipLaunchKernelGGL(k_count_scan, dim3(H), dim3(1024), 0, st, a.counts, C, offs, stats,
                            nflag);
     };
 
@@ -708,6 +815,15 @@ static hipError_t run_cluster(const ClusterArgs& a, hipStream_t st)
         int* changed = (int*)(s + L.cl_changed);
         int* moved = (int*)(s + L.cl_moved);
         int32_t* labprev = (int32_t*)(s + L.cl_labprev);
+        // With the MFMA path the running sums persist from update to update
+        // (delta passes); the bucket orders and offsets alternate between two
+        // buffers so that the previous ones are at hand.
+        const bool delta = mfma && D == 128;
+        uint8_t* tokflag = (uint8_t*)(s + L.cl_tokflag);
+        int32_t* const order2[2] = {pwork, (int32_t*)(s + L.cl_perm2)};
+        int32_t* const offs2[2] = {(int32_t*)(s + L.cl_offs), (int32_t*)(s + L.cl_offs) + (size_t)H * (C + 1)};
+        int32_t* const ipos2[2] = {(int32_t*)(s + L.cl_ipos), (int32_t*)(s + L.cl_ipos) + (size_t)H * N};
+        uint8_t* const fpos2[2] = {(uint8_t*)(s + L.cl_fpos), (uint8_t*)(s + L.cl_fpos) + (size_t)H * N};
         if (mfma) {
             zero_words(changed, (size_t)H * C * 4, st);
             zero_words(moved, (size_t)H * C * 4, st);
@@ -724,17 +840,23 @@ static hipError_t run_cluster(const ClusterArgs& a, hipStream_t st)
             // update: unstable bucket order + exact per-cluster means (and next planes)
             if (mfma)
                 hipLaunchKernelGGL(k_label_diff, dim3((N + 255) / 256, H), dim3(256), 0, st, a.labels,
-                                   labprev, N, C, it > 0 ? 1 : 0, changed);
-            sort_front(nullptr, mfma ? P.nflag : nullptr);
+                                   labprev, N, C, it > 0 ? 1 : 0, changed, delta ? tokflag : nullptr,
+                                   delta ? ipos2[(it + 1) & 1] : nullptr, delta ? fpos2[(it + 1) & 1] : nullptr);
+            int32_t* const order = delta ? order2[it & 1] : pwork;
+            int32_t* const offs = delta ? offs2[it & 1] : a.offsets;
+            sort_front(nullptr, mfma ? P.nflag : nullptr, offs);
             hipLaunchKernelGGL(k_bucket, gtiles, dim3(256), (size_t)C * 4, st, a.labels, N, C,
-                               ntiles, hist, a.offsets, pwork);
-            if (mfma && D == 128) {
+                               ntiles, hist, offs, order, delta ? tokflag : nullptr, ipos2[it & 1], fpos2[it & 1]);
+            if (delta) {
                 const int* chg = it > 0 ? changed : nullptr;
-                // the first update reads every row: it also records the smallest magnitude
-                chunk_pass(X, range_x, pwork, chg, it == 0 ? 1 : 0, 1, nullptr);
+                if (it == 0)   // the first update reads every row: it also records the smallest magnitude
+                    chunk_pass(X, range_x, order, nullptr, 1, 1, nullptr, offs);
+                else
+                    delta_pass(order, offs, fpos2[it & 1], order2[(it - 1) & 1], offs2[(it - 1) & 1],
+                               fpos2[(it - 1) & 1], chg);
                 hipLaunchKernelGGL((k_cluster_finalize<D, D == 128>), gfin, dim3(256), 0, st, a.counts,
                                    C, N, range_x, kPrec, it == 0 ? 1 : 0, it == 0 ? err : nullptr, 0, sums,
-                                   cent64, (float*)nullptr, P.hi, P.lo, P.cn32, P.cn64, resid, chg, moved);
+                                   cent64, (float*)nullptr, P.hi, P.lo, P.cn32, P.cn64, resid, chg, moved, 1);
                 hipLaunchKernelGGL(k_plane_stats, dim3(H), dim3(256), 0, st, C, P.cn64, resid,
                                    P.stats);
                 hipLaunchKernelGGL(k_moved_list, dim3(H), dim3(1024), 0, st, C, changed, moved,
@@ -744,10 +866,11 @@ static hipError_t run_cluster(const ClusterArgs& a, hipStream_t st)
                 mean_pass(X, range_x, pwork, it == 0 ? 1 : 0, 0, (float*)nullptr, 1, nullptr);
             }
         }
+        if (delta && a.iters >= 2) zero_words(sums, (size_t)2 * H * C * D * 8, st);   // the final pass sums from zero
     }
 
     // Final reorder (stable counting sort), rows gathered, means of the final labels.
-    sort_front(nullptr, nullptr);
+    sort_front(nullptr, nullptr, a.offsets);
     // The scatter records the largest magnitude of V, and of X unless the k-means
     // has its range (its first assignment the largest, its first update the
     // smallest magnitude); a mean pass that collects records the smallest.

@@ -236,7 +236,7 @@ struct Layout {
     // cluster scratch (relative to scratch)
     size_t cl_cent64, cl_hi, cl_lo, cl_cnorm, cl_cn64, cl_stats, cl_flag, cl_nflag,
         cl_hist, cl_perm, cl_sums, cl_range, cl_resid, cl_labprev, cl_bounds, cl_changed, cl_moved,
-        cl_mlist, cl_mpos, cl_mcount;
+        cl_mlist, cl_mpos, cl_mcount, cl_perm2, cl_offs, cl_tokflag, cl_ipos, cl_fpos;
     size_t cl_end;
     // probe scratch (relative to scratch)
     size_t pr_sbar, pr_keys, pr_pg, pr_ctr;
