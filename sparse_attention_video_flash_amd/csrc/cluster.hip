@@ -468,10 +468,11 @@ __device__ __forceinline__ double fix_value(unsigned long long hi, unsigned long
 // (ERR_RANGE: values the exact sums cannot capture, or out of range); an empty cluster keeps its centroid (k-means) or becomes
 // zero (plain means).  Optionally writes an fp32 copy; with PLANES also the
 // bf16 hi/lo planes, ||c||^2 (fp32, fp64) and the split residual norm that the
-// MFMA screen of the next assignment needs.  Clears the sums for the next pass.
-// With `changed`, only clusters whose membership changed are recomputed (the
-// others' sums are zero and their centroids stand); `moved` records whether
-// a recomputed centroid differs from its previous value in any bit.
+// MFMA screen of the next assignment needs.  Clears the sums for the next pass,
+// unless keep (the k-means delta updates add to them).  With `changed`, only
+// clusters whose membership changed are recomputed (the others' centroids
+// stand); `moved` records whether a recomputed centroid differs from its
+// previous value in any bit.
 template <int D, bool PLANES>
 __global__ __launch_bounds__(256) void k_cluster_finalize(
     const int32_t* __restrict__ counts, int C, int N, const unsigned* __restrict__ range, int prec,

@@ -104,6 +104,79 @@ def test_small_n_clustering_bit_exact(case):
     _cluster_and_check(w, q, k, v, iq, ik)
 
 
+def _exact_means(X, labels, C):
+    """Means of the rows of X (bf16 values as float32) per label, each the exact
+    rational mean rounded once to fp64: the values are scaled by 2^150 to
+    integers, summed exactly, and divided as fractions."""
+    from fractions import Fraction
+    X = np.asarray(X, np.float64)
+    out = np.zeros((C, X.shape[1]))
+    for m in range(C):
+        rows = X[labels == m]
+        if len(rows) == 0:
+            continue
+        for t in range(X.shape[1]):
+            tot = sum(int(v * 2.0 ** 150) for v in rows[:, t])
+            out[m, t] = float(Fraction(tot, len(rows) * 2 ** 150))
+    return out
+
+
+def test_two_word_sums_through_the_delta_updates():
+    """A head whose values span more than one 64-bit word of the fixed-point
+    sums (values near 10^-13 next to values in the hundreds) is summed with two
+    words: in the first update, in every later update (which adds only the
+    tokens that changed cluster), and in the final means.  Its labels and
+    permutation equal the oracle's; its centroids are within one fp32 ulp of
+    the exact means of the final labels (the oracle's plain fp64 sums round at
+    this span, the device's integer sums do not).  The other heads stay on one
+    word and are bit-exact."""
+    torch = torch_gpu()
+    w = RAGGED
+    log("two-word heads through the k-means updates")
+    q, k, v, iq, ik = _data(w, 613.0)
+    # head 0: coordinate 5 of every token near 10^-13, so that its centroid
+    # coordinates are of that size too and show any value the sums dropped
+    rng = np.random.default_rng(11)
+    for X in (q, k):
+        X[0, :, 5] = round_to_bf16((3e-13 * rng.standard_normal(X.shape[1])).astype(np.float32))
+    et = torch.bfloat16
+    H = q.shape[0]
+    shape = shape_of(w, H)
+    ws = sv.alloc_workspace(shape)
+    for side, Xh, C, init in ((0, q, w.Cq, iq), (1, k, w.Ck, ik)):
+        N = Xh.shape[1]
+        X = _dev(Xh, et)
+        out = dict(labels=torch.empty(H, N, dtype=torch.int32, device="cuda"),
+                   cent=torch.empty(H, C, w.d, device="cuda"),
+                   counts=torch.empty(H, C, dtype=torch.int32, device="cuda"),
+                   offsets=torch.empty(H, C + 1, dtype=torch.int32, device="cuda"),
+                   perm=torch.empty(H, N, dtype=torch.int32, device="cuda"),
+                   inv_perm=torch.empty(H, N, dtype=torch.int32, device="cuda"), Xp=torch.empty_like(X))
+        V = None
+        if side == 1:
+            V = _dev(v, et)
+            out["vbar"] = torch.empty(H, C, w.d, device="cuda")
+            out["Vp"] = torch.empty_like(V)
+        sv.cluster(shape, side, X, _dev(init, torch.int32), out, ws, V=V, flags=sv.DEBUG_SYNC)
+        for hi in range(H):
+            lab, cent, counts = oracle.kmeans(Xh[hi], C, init[hi], iters=w.iters)
+            np.testing.assert_array_equal(out["labels"][hi].cpu().numpy(), lab)
+            np.testing.assert_array_equal(out["counts"][hi].cpu().numpy(), counts)
+            perm = oracle.permutation(lab, C)[2]
+            np.testing.assert_array_equal(out["perm"][hi].cpu().numpy(), perm)
+            np.testing.assert_array_equal(out["Xp"][hi].float().cpu().numpy(), Xh[hi][perm])
+            got = out["cent"][hi].cpu().numpy()
+            if hi == 0:   # non-empty clusters (an empty one keeps its centroid of an earlier iteration)
+                ref = _exact_means(Xh[hi], lab, C).astype(np.float32)
+                ulp = np.spacing(np.abs(ref))
+                ne = counts > 0
+                assert ne.sum() > C // 2
+                assert (np.abs(got - ref)[ne] <= ulp[ne]).all(), float((np.abs(got - ref) / ulp)[ne].max())
+            else:
+                np.testing.assert_array_equal(got, cent.astype(np.float32))
+        log("  side %d: labels and permutation exact, two-word head within one ulp" % side)
+
+
 def test_wide_range_forward_matches_oracle():
     """End to end at values in the thousands (logits in the millions: the
     softmax picks single keys); the output bar scales with the output."""
