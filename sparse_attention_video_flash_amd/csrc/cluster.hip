@@ -278,7 +278,7 @@ __global__ __launch_bounds__(256) void k_cluster_chunks(const T* __restrict__ X,
                                                         const uint8_t* __restrict__ flags1,
                                                         const int32_t* __restrict__ perm2,
                                                         const int32_t* __restrict__ offsets2,
-                                                        const uint8_t* __restrict__ flags2)
+                                                        const uint8_t* __restrict__ flags2, int drows)
 {
     static_assert(!DELTA || (MODE != CH_ONE_COLLECT && !GATHER), "delta passes neither collect nor gather");
     constexpr bool TWO = MODE == CH_TWO, COLLECT = MODE == CH_ONE_COLLECT;
@@ -288,9 +288,12 @@ __global__ __launch_bounds__(256) void k_cluster_chunks(const T* __restrict__ X,
     constexpr int RPP = 256 / CPR;             // rows per pass
     constexpr int PREC = sizeof(T) == 2 ? 8 : 24;
     __shared__ long long s_sum[RPP][D];
-    // delta passes touch few rows per position: longer chunks, fewer workgroups
+    // delta passes touch few rows per position: longer chunks (drows positions,
+    // at most ROWS, a multiple of 256), fewer workgroups
     constexpr int ROWS = DELTA ? 4 * MC_ROWS : MC_ROWS;
-    constexpr int PPT = ROWS / 256;   // positions per thread in the flag scan
+    constexpr int PPT = ROWS / 256;   // most positions per thread in the flag scan
+    const int rows_c = DELTA ? drows : MC_ROWS;
+    const int ppt = rows_c / 256;
     __shared__ int s_idx[ROWS];
     __shared__ int s_pre[DELTA ? ROWS + 1 : 1];   // exclusive prefix sums of the chunk's flags
     __shared__ int s_first, s_wsum[4];
@@ -312,8 +315,8 @@ __global__ __launch_bounds__(256) void k_cluster_chunks(const T* __restrict__ X,
     R rgx;
     // chunks of ROWS positions, gridDim.x apart (the two-word kernel, which
     // serves few heads if any, runs on a smaller grid)
-    for (int p0 = blockIdx.x * ROWS; p0 < N; p0 += (int)gridDim.x * ROWS) {
-        const int p1 = min(N, p0 + ROWS);
+    for (int p0 = blockIdx.x * rows_c; p0 < N; p0 += (int)gridDim.x * rows_c) {
+        const int p1 = min(N, p0 + rows_c);
         // first cluster whose range ends after p0: the number of clusters that
         // end at or before it (the offsets do not decrease), counted in parallel
         __syncthreads();   // the previous chunk is done with s_idx, s_first and s_wsum
@@ -340,12 +343,12 @@ __global__ __launch_bounds__(256) void k_cluster_chunks(const T* __restrict__ X,
             // order), block-wide exclusive scan, then the flagged rows' token
             // indices packed to the front in order
             const uint8_t* const fl = (neg ? flags2 : flags1) + (size_t)h * N + p0;
-            const int n = p1 - p0, k0 = PPT * (int)threadIdx.x;
+            const int n = p1 - p0, k0 = ppt * (int)threadIdx.x;
             int fk[PPT];
             int cnt = 0;
 #pragma unroll
             for (int i = 0; i < PPT; ++i) {
-                fk[i] = k0 + i < n ? fl[k0 + i] : 0;
+                fk[i] = i < ppt && k0 + i < n ? fl[k0 + i] : 0;
                 cnt += fk[i];
             }
             // inclusive scan within each wave, then across the four waves
@@ -361,10 +364,10 @@ __global__ __launch_bounds__(256) void k_cluster_chunks(const T* __restrict__ X,
 #pragma unroll
             for (int w = 0; w < 3; ++w) incl += w < wave ? s_wsum[w] : 0;
             int ex = incl - cnt;
-            if (k0 < n && k0 + PPT >= n) s_pre[n] = incl;   // the thread holding the last position
+            if (k0 < n && k0 + ppt >= n) s_pre[n] = incl;   // the thread holding the last position
 #pragma unroll
             for (int i = 0; i < PPT; ++i) {
-                if (k0 + i < n) s_pre[k0 + i] = ex;
+                if (i < ppt && k0 + i < n) s_pre[k0 + i] = ex;
                 if (fk[i]) s_idx[ex] = perm[(size_t)h * N + p0 + k0 + i];
                 ex += fk[i];
             }
@@ -753,33 +756,37 @@ static hipError_t run_cluster(const ClusterArgs& a, hipStream_t st)
         // (a collecting pass runs only while the range is unknown, before any gather)
         if (collect) {
             hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_ONE_COLLECT, false, false>), gchunks, dim3(256), 0, st,
-                               src, order, offs, N, C, rg, sums, chg, rev, (uint4*)nullptr, nf, order, offs, nf);
+                               src, order, offs, N, C, rg, sums, chg, rev, (uint4*)nullptr, nf, order, offs, nf, MC_ROWS);
             hipLaunchKernelGGL(k_clear_two_word_heads, dim3(16, H), dim3(256), 0, st, rg, N, kPrec,
                                (size_t)C * D, sums);
         } else if (xp) {
             hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_ONE, true, false>), gchunks, dim3(256), 0, st, src, order,
-                               offs, N, C, rg, sums, chg, rev, xp, nf, order, offs, nf);
+                               offs, N, C, rg, sums, chg, rev, xp, nf, order, offs, nf, MC_ROWS);
         } else {
             hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_ONE, false, false>), gchunks, dim3(256), 0, st, src, order,
-                               offs, N, C, rg, sums, chg, rev, xp, nf, order, offs, nf);
+                               offs, N, C, rg, sums, chg, rev, xp, nf, order, offs, nf, MC_ROWS);
         }
         if (xp)
             hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_TWO, true, false>), gtwo, dim3(256), 0, st, src, order,
-                               offs, N, C, rg, sums, chg, rev, xp, nf, order, offs, nf);
+                               offs, N, C, rg, sums, chg, rev, xp, nf, order, offs, nf, MC_ROWS);
         else
             hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_TWO, false, false>), gtwo, dim3(256), 0, st, src, order,
-                               offs, N, C, rg, sums, chg, rev, xp, nf, order, offs, nf);
+                               offs, N, C, rg, sums, chg, rev, xp, nf, order, offs, nf, MC_ROWS);
     };
     // an update after the first: the flagged tokens join their clusters (current
     // bucket order) and leave their previous ones (previous bucket order)
     auto delta_pass = [&](const int32_t* order, const int32_t* offs, const uint8_t* flags,
                           const int32_t* order_prev, const int32_t* offs_prev, const uint8_t* flags_prev,
                           const int* chg) {
-        const int nd = (N + 4 * MC_ROWS - 1) / (4 * MC_ROWS);   // the delta passes' longer chunks
+        // the delta passes' chunk: the longest (up to 2,048 positions) that still
+        // gives about four workgroups per CU
+        int dr = 4 * MC_ROWS;
+        while (dr > MC_ROWS && (size_t)((N + dr - 1) / dr) * H < 1024) dr /= 2;
+        const int nd = (N + dr - 1) / dr;
         hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_ONE, false, true>), dim3(nd, H, 2), dim3(256), 0, st, X,
-                           order, offs, N, C, range_x, sums, chg, 1, (uint4*)nullptr, flags, order_prev, offs_prev, flags_prev);
+                           order, offs, N, C, range_x, sums, chg, 1, (uint4*)nullptr, flags, order_prev, offs_prev, flags_prev, dr);
         hipLaunchKernelGGL((k_cluster_chunks<T, D, CH_TWO, false, true>), dim3(nd < 16 ? nd : 16, H, 2), dim3(256), 0, st, X,
-                           order, offs, N, C, range_x, sums, chg, 1, (uint4*)nullptr, flags, order_prev, offs_prev, flags_prev);
+                           order, offs, N, C, range_x, sums, chg, 1, (uint4*)nullptr, flags, order_prev, offs_prev, flags_prev, dr);
     };
     // plain mean pass (no planes); checks the range
     auto mean_pass = [&](const T* src, unsigned* rg, const int32_t* order, int collect, int zero_empty,
