@@ -302,11 +302,12 @@ __global__ __launch_bounds__(256, 3) void k_assign_mfma(
                 const int m = k * CB + r;
 #pragma unroll
                 for (int tb = 0; tb < 2; ++tb) {
+                    // the two smallest so far (b1 <= b2): the new second is the
+                    // middle of (b1, b2, d), one v_med3 for max-then-min
                     const float d = fmaf(-2.f, acc[tb][i], cnv);
-                    const float u = fmaxf(b1[tb], d);
                     i1[tb] = d < b1[tb] ? m : i1[tb];
+                    b2[tb] = __builtin_amdgcn_fmed3f(b1[tb], b2[tb], d);
                     b1[tb] = fminf(b1[tb], d);
-                    b2[tb] = fminf(b2[tb], u);
                 }
             }
         }
@@ -488,10 +489,9 @@ __global__ __launch_bounds__(256, 3) void k_assign_partial(
                         const bool is_own = m == own[tb];
                         od[tb] = is_own ? d : od[tb];
                         const float dd = is_own ? __builtin_inff() : d;
-                        const float u = fmaxf(b1[tb], dd);
                         i1[tb] = dd < b1[tb] ? m : i1[tb];
+                        b2[tb] = __builtin_amdgcn_fmed3f(b1[tb], b2[tb], dd);   // as in the full screen
                         b1[tb] = fminf(b1[tb], dd);
-                        b2[tb] = fminf(b2[tb], u);
                     }
                 }
             }
