@@ -104,22 +104,57 @@ __global__ __launch_bounds__(256) void k_assign_exact(const T* __restrict__ X,
 
 // ----------------------------------------------------------------------------- counting sort
 
-// Per-tile label histogram (tiles of kTile consecutive tokens).
+// The label comparison of one k-means assignment, fused into the histogram
+// pass that reads the labels anyway: both clusters of every token whose label
+// changed are marked (their members, hence their means, changed); the labels
+// are kept for the next comparison (with mark == 0 only the copy is made);
+// tokflag records per token whether its label changed (all set with mark ==
+// 0), and fpos_prev the same flag at the token's position in the previous
+// bucket order (ipos_prev; the delta updates).  prev == nullptr: no comparison.
+struct LabelDiff {
+    int32_t* prev;
+    int mark;
+    int* changed;
+    uint8_t* tokflag;
+    const int32_t* ipos_prev;
+    uint8_t* fpos_prev;
+};
+
+// Per-tile label histogram (tiles of tt consecutive tokens, tt a multiple of
+// 256), with the optional label comparison.
 __global__ __launch_bounds__(256) void k_tile_hist(const int32_t* __restrict__ labels, int N, int C,
-                                                   int ntiles, int* __restrict__ hist,
-                                                   int* __restrict__ err)
+                                                   int ntiles, int tt, int* __restrict__ hist,
+                                                   int* __restrict__ err, LabelDiff ld)
 {
     extern __shared__ int s_h[];
     const int tile = blockIdx.x, h = blockIdx.y;
     for (int c = threadIdx.x; c < C; c += 256) s_h[c] = 0;
     __syncthreads();
-    const int i = tile * kTile + threadIdx.x;
-    if (i < N) {
-        int l = labels[(size_t)h * N + i];
+    const int i1 = min(N, (tile + 1) * tt);
+    for (int i = tile * tt + (int)threadIdx.x; i < i1; i += 256) {
+        const size_t t = (size_t)h * N + i;
+        const int l = labels[t];
         if (l < 0 || l >= C) {
             atomicOr(err, ERR_LABEL);
         } else {
             atomicAdd(&s_h[l], 1);
+        }
+        if (ld.prev) {
+            bool moved = true;
+            if (ld.mark) {
+                const int was = ld.prev[t];
+                moved = l != was;
+                if (moved) {
+                    if (was >= 0 && was < C) ld.changed[(size_t)h * C + was] = 1;
+                    if (l >= 0 && l < C) ld.changed[(size_t)h * C + l] = 1;
+                }
+                if (ld.fpos_prev) {   // every token with a valid label had a position
+                    const int ip = ld.ipos_prev[t];
+                    if (ip >= 0 && ip < N) ld.fpos_prev[(size_t)h * N + ip] = moved ? 1 : 0;
+                }
+            }
+            ld.prev[t] = l;
+            if (ld.tokflag) ld.tokflag[t] = moved ? 1 : 0;
         }
     }
     __syncthreads();
@@ -207,12 +242,11 @@ __global__ __launch_bounds__(1024) void k_count_scan(const int32_t* __restrict__
 }
 
 // Unstable bucket fill: every token goes to its cluster's range (order within a
-// cluster does not matter to the exact sums).  Ranks inside a tile come from
-// LDS atomics.
-// With tokflag (the delta updates of the k-means): also each token's position
-// (ipos) and its flag by position (fpos).
+// cluster does not matter to the exact sums).  Ranks inside a tile (tt tokens)
+// come from LDS atomics.  With tokflag (the delta updates of the k-means): also
+// each token's position (ipos) and its flag by position (fpos).
 __global__ __launch_bounds__(256) void k_bucket(const int32_t* __restrict__ labels, int N, int C,
-                                                int ntiles, const int* __restrict__ hist,
+                                                int ntiles, int tt, const int* __restrict__ hist,
                                                 const int32_t* __restrict__ offsets,
                                                 int32_t* __restrict__ perm,
                                                 const uint8_t* __restrict__ tokflag,
@@ -222,8 +256,8 @@ __global__ __launch_bounds__(256) void k_bucket(const int32_t* __restrict__ labe
     const int tile = blockIdx.x, h = blockIdx.y;
     for (int c = threadIdx.x; c < C; c += 256) s_r[c] = 0;
     __syncthreads();
-    const int i = tile * kTile + threadIdx.x;
-    if (i < N) {
+    const int i1 = min(N, (tile + 1) * tt);
+    for (int i = tile * tt + (int)threadIdx.x; i < i1; i += 256) {
         const int l = labels[(size_t)h * N + i];
         if (l >= 0 && l < C) {
             const int rank = atomicAdd(&s_r[l], 1);
@@ -550,41 +584,6 @@ __global__ __launch_bounds__(256) void k_cluster_finalize(
     }
 }
 
-// Label changes of one assignment: both clusters of every token whose label
-// changed are marked (their members, hence their means, changed); the labels are
-// then kept for the next comparison.  With mark == 0 only the copy is made.
-// tokflag: per token, whether its label changed (all set with mark == 0).
-__global__ __launch_bounds__(256) void k_label_diff(const int32_t* __restrict__ labels,
-                                                    int32_t* __restrict__ prev, int N, int C,
-                                                    int mark, int* __restrict__ changed,
-                                                    uint8_t* __restrict__ tokflag,
-                                                    const int32_t* __restrict__ ipos_prev,
-                                                    uint8_t* __restrict__ fpos_prev)
-{
-    const int h = blockIdx.y;
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i >= N) return;
-    const size_t t = (size_t)h * N + i;
-    const int now = labels[t];
-    bool moved = true;
-    if (mark) {
-        const int was = prev[t];
-        moved = now != was;
-        if (moved) {
-            if (was >= 0 && was < C) changed[(size_t)h * C + was] = 1;
-            if (now >= 0 && now < C) changed[(size_t)h * C + now] = 1;
-        }
-    }
-    prev[t] = now;
-    if (tokflag) tokflag[t] = moved ? 1 : 0;
-    // the flag also by the token's position in the previous bucket order (every
-    // token with a valid label had one)
-    if (mark && fpos_prev) {
-        const int ip = ipos_prev[t];
-        if (ip >= 0 && ip < N) fpos_prev[(size_t)h * N + ip] = moved ? 1 : 0;
-    }
-}
-
 // Per head: the ascending list of moved centroids (the only ones the next
 // assignment has to evaluate) and each centroid's position in it (-1 if it did
 // not move); both flag arrays are then cleared for the next round.
@@ -798,14 +797,20 @@ static hipError_t run_cluster(const ClusterArgs& a, hipStream_t st)
                            (const int*)nullptr, (int*)nullptr, 0);
     };
 
-    // counting-sort front half: tile histograms, per-label tile prefixes, counts, offsets
-    auto sort_front = [&](unsigned* stats, int* nflag, int32_t* offs) {
-        hipLaunchKernelGGL(k_tile_hist, gtiles, dim3(256), (size_t)C * 4, st, a.labels, N, C,
-                           ntiles, hist, err);
-        hipLaunchKernelGGL(k_hist_cols, gcols, dim3(256), 0, st, hist, C, ntiles, a.counts);
+    // counting-sort front half: tile histograms (tiles of tt tokens; with ld, the
+    // label comparison of the k-means as well), per-label tile prefixes, counts,
+    // offsets.  The stable final sort uses kTile-token tiles (the scatter ranks
+    // within a tile by scanning it); the unstable sorts of the k-means updates
+    // use tiles of kTileU tokens, which keeps the tile histograms small.
+    auto sort_front = [&](unsigned* stats, int* nflag, int32_t* offs, int tt, const LabelDiff& ld) {
+        const int nt = (N + tt - 1) / tt;
+        hipLaunchKernelGGL(k_tile_hist, dim3(nt, H), dim3(256), (size_t)C * 4, st, a.labels, N, C,
+                           nt, tt, hist, err, ld);
+        hipLaunchKernelGGL(k_hist_cols, gcols, dim3(256), 0, st, hist, C, nt, a.counts);
         hipLaunchKernelGGL(k_count_scan, dim3(H), dim3(1024), 0, st, a.counts, C, offs, stats,
                            nflag);
     };
+    const LabelDiff no_diff = {nullptr, 0, nullptr, nullptr, nullptr, nullptr};
 
     if (!(a.flags & SVGEAR_LABELS_GIVEN)) {
         hipLaunchKernelGGL((k_init_centroids<T>), gcent, dim3(D), 0, st, X, a.init, N, D, C, cent64,
@@ -846,15 +851,21 @@ static hipError_t run_cluster(const ClusterArgs& a, hipStream_t st)
             }
             if (it == a.iters - 1) break;
             // update: unstable bucket order + exact per-cluster means (and next planes)
-            if (mfma)
-                hipLaunchKernelGGL(k_label_diff, dim3((N + 255) / 256, H), dim3(256), 0, st, a.labels,
-                                   labprev, N, C, it > 0 ? 1 : 0, changed, delta ? tokflag : nullptr,
-                                   delta ? ipos2[(it + 1) & 1] : nullptr, delta ? fpos2[(it + 1) & 1] : nullptr);
+            LabelDiff ld = no_diff;
+            if (mfma) {
+                ld.prev = labprev;
+                ld.mark = it > 0 ? 1 : 0;
+                ld.changed = changed;
+                ld.tokflag = delta ? tokflag : nullptr;
+                ld.ipos_prev = delta ? ipos2[(it + 1) & 1] : nullptr;
+                ld.fpos_prev = delta ? fpos2[(it + 1) & 1] : nullptr;
+            }
             int32_t* const order = delta ? order2[it & 1] : pwork;
             int32_t* const offs = delta ? offs2[it & 1] : a.offsets;
-            sort_front(nullptr, mfma ? P.nflag : nullptr, offs);
-            hipLaunchKernelGGL(k_bucket, gtiles, dim3(256), (size_t)C * 4, st, a.labels, N, C,
-                               ntiles, hist, offs, order, delta ? tokflag : nullptr, ipos2[it & 1], fpos2[it & 1]);
+            sort_front(nullptr, mfma ? P.nflag : nullptr, offs, kTileU, ld);
+            hipLaunchKernelGGL(k_bucket, dim3((N + kTileU - 1) / kTileU, H), dim3(256), (size_t)C * 4, st,
+                               a.labels, N, C, (N + kTileU - 1) / kTileU, kTileU, hist, offs, order,
+                               delta ? tokflag : nullptr, ipos2[it & 1], fpos2[it & 1]);
             if (delta) {
                 const int* chg = it > 0 ? changed : nullptr;
                 if (it == 0)   // the first update reads every row: it also records the smallest magnitude
@@ -878,7 +889,7 @@ static hipError_t run_cluster(const ClusterArgs& a, hipStream_t st)
     }
 
     // Final reorder (stable counting sort), rows gathered, means of the final labels.
-    sort_front(nullptr, nullptr, a.offsets);
+    sort_front(nullptr, nullptr, a.offsets, kTile, no_diff);
     // The scatter records the largest magnitude of V, and of X unless the k-means
     // has its range (its first assignment the largest, its first update the
     // smallest magnitude); a mean pass that collects records the smallest.

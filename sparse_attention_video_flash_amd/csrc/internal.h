@@ -213,6 +213,7 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return f32
 // ----------------------------------------------------------------------------- sizes
 
 constexpr int kTile = 256;          // tokens per counting-sort / run-length tile
+constexpr int kTileU = 2048;        // tokens per tile of the k-means' unstable bucket sorts
 constexpr int kMaxC = 4096;         // largest cluster count
 constexpr int kAttnRows = 256;      // query rows per attention tile (bf16, d = 128 kernel)
 constexpr int kXcd = 8;             // XCDs per device: attention work queues
