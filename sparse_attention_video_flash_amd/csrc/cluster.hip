@@ -824,7 +824,9 @@ static hipError_t run_cluster(const ClusterArgs& a, hipStream_t st)
         // With the MFMA screen, iteration 0 evaluates every centroid; later
         // iterations only the centroids that moved in the last update, against
         // per-token bounds on the distances to all others (see assign_mfma.hip).
-        // Updates recompute only the clusters whose membership changed.
+        // The first update sums every token; later ones (MFMA path) add only the
+        // tokens whose label changed to the kept sums, and the means of only the
+        // clusters whose membership changed are recomputed.
         int* changed = (int*)(s + L.cl_changed);
         int* moved = (int*)(s + L.cl_moved);
         int32_t* labprev = (int32_t*)(s + L.cl_labprev);
