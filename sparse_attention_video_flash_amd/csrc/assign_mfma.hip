@@ -545,13 +545,14 @@ __global__ __launch_bounds__(256, 3) void k_assign_partial(
     }
 }
 
-// Exact settlement of queued tokens (few per head), one workgroup per token.
+// Exact settlement of queued tokens (few per head), one workgroup per token at a
+// time (the queues of all heads dealt to the whole grid).
 // Pass 1: every centroid's ||c||^2 - 2 x.c in fp64, each thread owning whole
 // centroid rows (16-byte loads, x broadcast from LDS).  Pass 2: for every
 // centroid within a tolerance of the minimum, the distance exactly as the
 // oracle evaluates it (sum of (x_t - c_t)^2 in coordinate order, no fusion),
 // rows staged in LDS; the smallest wins, lowest index first.
-constexpr int RC_ROWS = 8, RC_MAXCAND = 64;
+constexpr int RC_ROWS = 8, RC_MAXCAND = 64, RC_HEADS = 1024;
 __global__ __launch_bounds__(256) void k_recheck(const bf16* __restrict__ X,
                                                  const double* __restrict__ cent64,
                                                  const double* __restrict__ cn64,
@@ -571,14 +572,58 @@ __global__ __launch_bounds__(256) void k_recheck(const bf16* __restrict__ X,
     __shared__ double s_c[RC_ROWS][KM_D];
     __shared__ int s_cand[RC_MAXCAND];
     __shared__ int s_nc, s_win;
-    const int h = blockIdx.y;
+    __shared__ int s_hp[RC_HEADS + 1], s_ws[4];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int cnt = nflag[h];
-    const double* ch = cent64 + (size_t)h * C * KM_D;
-    const double* cnh = cn64 + (size_t)h * C;
-    const double cmax = (double)__uint_as_float(stats[4 * h + 1]);
-    for (int e = blockIdx.x; e < cnt; e += gridDim.x) {
-        const int token = flags[(size_t)h * N + e];
+    // The queued tokens of all heads form one list (heads in order), dealt to
+    // every workgroup of the grid, so a head with many queued tokens does not
+    // wait on its own share of workgroups.  Heads in segments of RC_HEADS: the
+    // exclusive prefix of their queue lengths in s_hp.
+    const int H = (int)gridDim.y;
+    const int wg = (int)(blockIdx.y * gridDim.x + blockIdx.x), nwg = (int)(gridDim.x * gridDim.y);
+    for (int h0 = 0; h0 < H; h0 += RC_HEADS) {
+    const int hn = min(RC_HEADS, H - h0);
+    {
+        constexpr int PER = RC_HEADS / 256;
+        int v[PER], loc = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int j = tid * PER + i;
+            v[i] = j < hn ? nflag[h0 + j] : 0;
+            loc += v[i];
+        }
+        int incl = loc;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int t = __shfl_up(incl, o);
+            if (lane >= o) incl += t;
+        }
+        __syncthreads();   // the previous segment's readers of s_hp and s_ws are done
+        if (lane == 63) s_ws[wave] = incl;
+        __syncthreads();
+        int ex = incl - loc;
+#pragma unroll
+        for (int w = 0; w < 3; ++w) ex += w < wave ? s_ws[w] : 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int j = tid * PER + i;
+            if (j < hn) s_hp[j] = ex;
+            ex += v[i];
+        }
+        if (tid == 255) s_hp[hn] = ex;   // the segment's total
+        __syncthreads();
+    }
+    const int total = s_hp[hn];
+    for (int e = wg; e < total; e += nwg) {
+        int lo = 0, hi = hn - 1;   // the head: last j with s_hp[j] <= e
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_hp[mid] <= e) lo = mid; else hi = mid - 1;
+        }
+        const int h = h0 + lo;
+        const double* ch = cent64 + (size_t)h * C * KM_D;
+        const double* cnh = cn64 + (size_t)h * C;
+        const double cmax = (double)__uint_as_float(stats[4 * h + 1]);
+        const int token = flags[(size_t)h * N + (e - s_hp[lo])];
         __syncthreads();
         if (tid < KM_D) s_x[tid] = (double)bf16_to_f32(X[((size_t)h * N + token) * KM_D + tid]);
         __syncthreads();
@@ -685,6 +730,7 @@ __global__ __launch_bounds__(256) void k_recheck(const bf16* __restrict__ X,
             lb_own[t] = __double2float_rd(own - tol);
             lb_rest[t] = __double2float_rd(second - tol);
         }
+    }
     }
 }
 
