@@ -566,7 +566,7 @@ __global__ __launch_bounds__(256) void k_recheck(const bf16* __restrict__ X,
 {
 #pragma clang fp contract(off)
     __shared__ double s_x[KM_D];
-    __shared__ double s_d[kMaxC];
+    extern __shared__ double s_d[];   // [C], sized at launch
     __shared__ double s_rb[4];
     __shared__ int s_ri[4];
     __shared__ double s_c[RC_ROWS][KM_D];
@@ -653,17 +653,13 @@ __global__ __launch_bounds__(256) void k_recheck(const bf16* __restrict__ X,
         // so the exact minimiser lies within twice that of the dot-form minimum.
         const double nxc = sqrt(xx) + cmax;
         const double tol = 0x1p-42 * nxc * nxc;
-        // candidates (usually one or two): compacted per block of RC_MAXCAND centroids,
-        // their rows staged in LDS for the sequential exact sums
+        // candidates (usually one or two): collected in one pass (their order
+        // does not matter: the smallest distance wins, the lowest index on
+        // ties), their rows staged in LDS RC_ROWS at a time for the sequential
+        // exact sums; more than RC_MAXCAND of them are taken block by block
         double best = __builtin_inf();
         int bi = 0x7fffffff;
-        for (int m0 = 0; m0 < C; m0 += RC_MAXCAND) {
-            if (tid == 0) s_nc = 0;
-            __syncthreads();
-            if (tid < RC_MAXCAND && m0 + tid < C && s_d[m0 + tid] <= dmin + tol)
-                s_cand[atomicAdd(&s_nc, 1)] = m0 + tid;
-            __syncthreads();
-            const int nc = s_nc;
+        auto settle = [&](int nc) {
             for (int k0 = 0; k0 < nc; k0 += RC_ROWS) {
                 const int kn = min(RC_ROWS, nc - k0);
                 for (int k = tid; k < kn * KM_D; k += 256)
@@ -682,6 +678,28 @@ __global__ __launch_bounds__(256) void k_recheck(const bf16* __restrict__ X,
                     }
                 }
                 __syncthreads();
+            }
+        };
+        if (tid == 0) s_nc = 0;
+        __syncthreads();
+        for (int m = tid; m < C; m += 256)
+            if (s_d[m] <= dmin + tol) {
+                const int k = atomicAdd(&s_nc, 1);
+                if (k < RC_MAXCAND) s_cand[k] = m;
+            }
+        __syncthreads();
+        const int ntot = s_nc;
+        if (ntot <= RC_MAXCAND) {
+            settle(ntot);
+        } else {
+            for (int m0 = 0; m0 < C; m0 += RC_MAXCAND) {
+                __syncthreads();   // every thread has read s_nc
+                if (tid == 0) s_nc = 0;
+                __syncthreads();
+                if (tid < RC_MAXCAND && m0 + tid < C && s_d[m0 + tid] <= dmin + tol)
+                    s_cand[atomicAdd(&s_nc, 1)] = m0 + tid;
+                __syncthreads();
+                settle(s_nc);
             }
         }
         for (int o = 32; o >= 1; o >>= 1) {
@@ -790,7 +808,7 @@ SVG_HIDDEN hipError_t launch_assign_mfma(const ClusterArgs& a, const double* cen
         hipLaunchKernelGGL(k_assign_partial, grid, dim3(256), KmPartialChunk::BYTES, st, (const bf16*)a.X, P.hi,
                            P.lo, P.cn32, P.stats, P.mlist, P.mpos, P.mcount, a.N, a.C, a.labels,
                            P.flags, P.nflag, P.ub_own, P.lb_own, P.lb_rest);
-    hipLaunchKernelGGL(k_recheck, dim3(256, a.H), dim3(256), 0, st, (const bf16*)a.X, cent64, P.cn64,
+    hipLaunchKernelGGL(k_recheck, dim3(256, a.H), dim3(256), (size_t)a.C * 8, st, (const bf16*)a.X, cent64, P.cn64,
                        P.stats, a.N, a.C, P.flags, P.nflag, a.labels, P.ub_own, P.lb_own, P.lb_rest);
     return hipGetLastError();
 }
