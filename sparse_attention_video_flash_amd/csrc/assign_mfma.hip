@@ -88,44 +88,43 @@ __device__ __forceinline__ float screen_error(float nx, float R, float cmax)
     return 1.01f * (2.f * xn * R + 64.f * u * xn * cmax + 2.f * u * (cmax * cmax + 2.f * xn * cmax));
 }
 
-// Per centroid: bf16 hi/lo planes, ||c||^2 (fp32 and fp64); per head: R and ||c||max
-// (as float bits, via integer max of non-negative floats).
-__global__ __launch_bounds__(KM_D) void k_km_prep(const double* __restrict__ cent64, int C,
-                                                  bf16* __restrict__ hi, bf16* __restrict__ lo,
-                                                  float* __restrict__ cn32,
-                                                  double* __restrict__ cn64,
-                                                  float* __restrict__ resid,
-                                                  unsigned* __restrict__ stats)
+// Per centroid: bf16 hi/lo planes, ||c||^2 (fp32 and fp64) and the split
+// residual norm; the per-head R and ||c||max follow from k_plane_stats (one
+// workgroup per head: atomics on two words per head from every centroid
+// serialised in L2).
+__global__ __launch_bounds__(256) void k_km_prep(const double* __restrict__ cent64, int C,
+                                                 bf16* __restrict__ hi, bf16* __restrict__ lo,
+                                                 float* __restrict__ cn32,
+                                                 double* __restrict__ cn64,
+                                                 float* __restrict__ resid)
 {
-    __shared__ double s_a[KM_D], s_b[KM_D];
-    const int m = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
-    const size_t i = ((size_t)h * C + m) * KM_D + t;
-    const double c = cent64[i];
-    const bf16 ch = f32_to_bf16((float)c);
-    const double r1 = c - (double)bf16_to_f32(ch);
-    const bf16 cl = f32_to_bf16((float)r1);
-    const double r2 = r1 - (double)bf16_to_f32(cl);
-    hi[i] = ch;
-    lo[i] = cl;
-    s_a[t] = c * c;
-    s_b[t] = r2 * r2;
-    __syncthreads();
-    for (int o = KM_D / 2; o >= 1; o >>= 1) {
-        if (t < o) {
-            s_a[t] += s_a[t + o];
-            s_b[t] += s_b[t + o];
-        }
-        __syncthreads();
+    // one wave per centroid, two coordinates per lane (the layout of the
+    // update's finalize, which prepares the later screens the same way)
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int m = blockIdx.x * 4 + wave, h = blockIdx.y;
+    if (m >= C) return;   // wave-uniform
+    double a2 = 0.0, r2s = 0.0;
+#pragma unroll
+    for (int e = 0; e < KM_D / 64; ++e) {
+        const size_t i = ((size_t)h * C + m) * KM_D + lane * (KM_D / 64) + e;
+        const double c = cent64[i];
+        const bf16 ch = f32_to_bf16((float)c);
+        const double r1 = c - (double)bf16_to_f32(ch);
+        const bf16 cl = f32_to_bf16((float)r1);
+        const double r2 = r1 - (double)bf16_to_f32(cl);
+        hi[i] = ch;
+        lo[i] = cl;
+        a2 = fma(c, c, a2);
+        r2s = fma(r2, r2, r2s);
     }
-    if (t == 0) {
-        const double n2 = s_a[0];
-        cn64[(size_t)h * C + m] = n2;
-        cn32[(size_t)h * C + m] = (float)n2;
-        const float cmax = (float)(sqrt(n2) * (1.0 + 1e-6));
-        const float res = (float)(sqrt(s_b[0]) * (1.0 + 1e-6));
-        resid[(size_t)h * C + m] = res;
-        atomicMax(stats + 4 * h + 0, __float_as_uint(res));
-        atomicMax(stats + 4 * h + 1, __float_as_uint(cmax));
+    for (int o = 32; o >= 1; o >>= 1) {
+        a2 += __shfl_xor(a2, o);
+        r2s += __shfl_xor(r2s, o);
+    }
+    if (lane == 0) {
+        cn64[(size_t)h * C + m] = a2;
+        cn32[(size_t)h * C + m] = (float)a2;
+        resid[(size_t)h * C + m] = (float)(sqrt(r2s) * (1.0 + 1e-6));
     }
 }
 
@@ -782,8 +781,8 @@ SVG_HIDDEN bool assign_mfma_supported(const ClusterArgs& a)
 SVG_HIDDEN hipError_t launch_km_prep(const ClusterArgs& a, const double* cent64, const KmPlanes& P,
                                      hipStream_t st)
 {
-    hipLaunchKernelGGL(k_km_prep, dim3(a.C, a.H), dim3(KM_D), 0, st, cent64, a.C, P.hi, P.lo, P.cn32,
-                       P.cn64, (float*)(a.scratch + a.L->cl_resid), P.stats);
+    hipLaunchKernelGGL(k_km_prep, dim3((a.C + 3) / 4, a.H), dim3(256), 0, st, cent64, a.C, P.hi, P.lo, P.cn32,
+                       P.cn64, (float*)(a.scratch + a.L->cl_resid));
     return hipGetLastError();
 }
 

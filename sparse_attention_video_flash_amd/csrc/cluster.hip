@@ -820,6 +820,7 @@ static hipError_t run_cluster(const ClusterArgs& a, hipStream_t st)
             zero_words(P.nflag, (size_t)H * 4, st);
             hipError_t e = launch_km_prep(a, cent64, P, st);
             if (e != hipSuccess) return e;
+            hipLaunchKernelGGL(k_plane_stats, dim3(H), dim3(256), 0, st, C, P.cn64, resid, P.stats);
         }
         // With the MFMA screen, iteration 0 evaluates every centroid; later
         // iterations only the centroids that moved in the last update, against
