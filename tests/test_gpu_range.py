@@ -177,6 +177,20 @@ def test_two_word_sums_through_the_delta_updates():
         log("  side %d: labels and permutation exact, two-word head within one ulp" % side)
 
 
+def test_many_tied_centroids_take_the_blocked_recheck():
+    """Seventy initial centroids on one token: every token near it has more
+    than RC_MAXCAND = 64 exactly tied candidates, so its exact settlement takes
+    the block-by-block candidate path; labels (lowest index on ties), counts,
+    permutation and centroids stay bit-exact with the oracle."""
+    w = Workload("ties", 2, (3, 20, 23), 128, "bf16", 16, 100, 6, (0.3,), 21,
+                 (Mixture((0, 2), 24, (2, 3, 4), 0.25, "normal", 0.08, 2.0, "add"),))
+    log("clustering with 70 coincident initial centroids")
+    q, k, v, iq, ik = _data(w, 1.0)
+    ik = ik.copy()
+    ik[:, :70] = ik[:, :1]
+    _cluster_and_check(w, q, k, v, iq, ik)
+
+
 def test_wide_range_forward_matches_oracle():
     """End to end at values in the thousands (logits in the millions: the
     softmax picks single keys); the output bar scales with the output."""
