@@ -87,8 +87,12 @@ SVG_HIDDEN Layout make_layout(const svgear_shape& s)
     L.pr_end = off;
 
     off = 0;
-    L.rt_hist = take(H * 4096 * 8);
+    // per-head states and histograms (one launch per pass, cleared together),
+    // then the per-slice top-digit histograms and the digit words of the
+    // two-launch route
     L.rt_state = take(H * 24);
+    L.rt_hist = take(H * 4096 * 8);
+    L.rt_top = take(route_top_bytes((int)H, (int)(s.Cq * s.Ck)));
     L.rt_part = take(H * 32 * 8);
     L.rt_end = off;
 

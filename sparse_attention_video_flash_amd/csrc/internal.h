@@ -242,7 +242,7 @@ struct Layout {
     // probe scratch (relative to scratch)
     size_t pr_sbar, pr_keys, pr_pg, pr_ctr;
     size_t pr_end;
-    size_t rt_hist, rt_state, rt_part, rt_end;   // route
+    size_t rt_state, rt_hist, rt_top, rt_part, rt_end;   // route
     // attention scratch (relative to scratch)
     size_t at_kvplanes, at_logm, at_tiles, at_segs, at_cinfo, at_comp, at_rows, at_queue;
     size_t at_end;
@@ -330,6 +330,7 @@ struct RouteArgs {
 };
 SVG_HIDDEN hipError_t launch_route(const RouteArgs& a, hipStream_t st);
 SVG_HIDDEN int route_slices(int H);
+SVG_HIDDEN size_t route_top_bytes(int H, int nb);
 SVG_HIDDEN hipError_t launch_route_rows(const RouteArgs& a, double rho, int Nk, hipStream_t st);
 SVG_HIDDEN void zero_words(void* p, size_t bytes, hipStream_t st);
 

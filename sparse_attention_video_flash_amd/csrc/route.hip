@@ -12,12 +12,15 @@
 // cost exceeds the budget" (all blocks if none does).  That crossing key is
 // found by a radix select, 12 bits per pass, most significant digit first, with
 // cost-weighted (int64) histograms: the blocks still in play are those whose
-// higher digits equal the digits chosen so far.  Each pass is one launch of
-// several workgroups per head (a slice of the head's blocks each, LDS
-// histogram, then integer atomics into the head's histogram in device memory);
-// the last workgroup of a head to finish scans that histogram and records the
-// chosen digit and the cost before it for the next pass.  A last launch writes
-// the mask and the selected cost.
+// higher digits equal the digits chosen so far.  Heads of up to 2^18 blocks
+// take two launches: per-slice top-digit histograms and the top 24 key bits of
+// every block, then one workgroup per head for every later pass and the mask
+// (k_route_top, k_route_head).  Larger
+// heads take one launch per pass, several workgroups per head (a slice
+// of the head's blocks each, LDS histogram, then integer atomics into the
+// head's histogram in device memory); the last workgroup of a head to finish
+// scans that histogram and records the chosen digit and the cost before it for
+// the next pass, and a last launch writes the mask and the selected cost.
 #include "internal.h"
 
 namespace svg {
@@ -198,6 +201,338 @@ __global__ __launch_bounds__(RT_THREADS) void k_route_mask(
     }
 }
 
+// ----------------------------------------------------------------------------- heads of up to 2^18 blocks
+//
+// Two launches.  Both top digits lie above the index bits, so the top 24 bits
+// of a block's key are the order key of its ratio shifted right (its "word").
+// k_route_top: S workgroups per head, each over a slice of the head's blocks:
+// the LDS histogram of the top digit, written whole to its own slot (no
+// device-memory atomics, nothing to clear), and every block's word (a row of P
+// words per head, P = the block count rounded up to 4).  k_route_head: one
+// workgroup of 1024 threads per head sums the S histograms and scans them; the
+// second pass sweeps the words (four per 16-byte load); the third sweeps them
+// again and only the blocks whose word equals the chosen 24-bit prefix load
+// their ratio: they are kept as composite keys in an LDS list, so that the
+// later passes read no device memory unless more than RH_CAND blocks share the
+// prefix (then they sweep the words again).  A last sweep of the words writes
+// the mask, the blocks of the listed prefix taking theirs from the list.  The
+// selected cost needs no sweep: it is the cost ahead of the crossing key, which
+// the last pass's scan yields (the whole head's cost when nothing crosses).
+constexpr int RH_THREADS = 1024;
+constexpr int RH_CAND = 8192;
+constexpr int RH_MAX_BLOCKS = 1 << 18;
+constexpr int RH_BATCH = 16;        // ratios loaded together per thread of k_route_top
+constexpr int RH_SLICES = 16;       // at most this many slices per head
+constexpr int RH_SLICE_BLOCKS = 8192;   // blocks per slice aimed at
+constexpr int RH_SLICE_LOAD = 8;    // slice histograms loaded together per thread
+constexpr int RH_VEC = 4;           // words per 16-byte load
+
+typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__host__ __device__ inline int route_word_pitch(int nb) { return (nb + RH_VEC - 1) / RH_VEC * RH_VEC; }
+
+SVG_HIDDEN int route_top_slices(int nb)
+{
+    const int s = (nb + RH_SLICE_BLOCKS - 1) / RH_SLICE_BLOCKS;
+    return s < 1 ? 1 : (s > RH_SLICES ? RH_SLICES : s);
+}
+
+SVG_HIDDEN size_t route_top_bytes(int H, int nb)
+{
+    if (nb > RH_MAX_BLOCKS) return 0;
+    return align256((size_t)H * route_top_slices(nb) * RT_BINS * 8) + (size_t)H * route_word_pitch(nb) * 4;
+}
+
+struct RhStep {
+    int c, g, dc, dg, Ck;
+    __device__ void start(int b, int stride, int Ck_)
+    {
+        Ck = Ck_;
+        c = b / Ck;
+        g = b - c * Ck;
+        dc = stride / Ck;
+        dg = stride - dc * Ck;
+    }
+    __device__ void next()
+    {
+        c += dc;
+        g += dg;
+        if (g >= Ck) {
+            g -= Ck;
+            ++c;
+        }
+    }
+};
+
+__global__ __launch_bounds__(RT_THREADS) void k_route_top(
+    const float* __restrict__ log_ratio, const int32_t* __restrict__ counts_q,
+    const int32_t* __restrict__ counts_k, RouteGeom gm, unsigned long long* __restrict__ part,
+    uint32_t* __restrict__ words)
+{
+    extern __shared__ int s_cnt[];   // counts_q of the head, then counts_k
+    __shared__ unsigned long long s_hist[RT_BINS];
+    const int h = blockIdx.y, tid = threadIdx.x;
+    const int Cq = gm.nb / gm.Ck;
+    for (int i = tid; i < RT_BINS; i += RT_THREADS) s_hist[i] = 0ull;
+    for (int i = tid; i < Cq; i += RT_THREADS) s_cnt[i] = counts_q[(size_t)h * Cq + i];
+    for (int i = tid; i < gm.Ck; i += RT_THREADS) s_cnt[Cq + i] = counts_k[(size_t)h * gm.Ck + i];
+    __syncthreads();
+    const float* lr = log_ratio + (size_t)h * gm.nb;
+    uint32_t* wh = words + (size_t)h * route_word_pitch(gm.nb);
+    const int wsh = gm.shift(1) - gm.IB;
+    int b0, b1;
+    route_slice(gm.nb, b0, b1);
+    RhStep cg;
+    cg.start(b0 + tid, RT_THREADS, gm.Ck);
+    for (int bb = b0 + tid; bb < b1; bb += RT_THREADS * RH_BATCH) {
+        float v[RH_BATCH];
+#pragma unroll
+        for (int u = 0; u < RH_BATCH; ++u) {
+            const int b = bb + u * RT_THREADS;
+            v[u] = b < b1 ? lr[b] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < RH_BATCH; ++u, cg.next()) {
+            const int b = bb + u * RT_THREADS;
+            if (b >= b1) continue;
+            const unsigned w24 = order_key(v[u]) >> wsh;
+            wh[b] = w24;
+            const long long w = (long long)s_cnt[cg.c] * (long long)s_cnt[Cq + cg.g];
+            atomicAdd(&s_hist[w24 >> RT_DIGIT], (unsigned long long)w);
+        }
+    }
+    __syncthreads();
+    unsigned long long* out = part + ((size_t)h * gridDim.x + blockIdx.x) * RT_BINS;
+    for (int i = tid; i < RT_BINS; i += RT_THREADS) out[i] = s_hist[i];
+}
+
+// Scan of a histogram from the top digit down, thread t holding digits
+// RT_BINS - 1 - 4t - j in v[j].  When the running cost (from base) first exceeds
+// the budget inside digit dg, the owner records dg and the cost ahead of it in
+// s_dig / s_base; s_dig must be -1 on entry and stays so when everything fits.
+// s_total receives base plus the whole histogram.
+__device__ void rh_scan(const long long (&v)[RT_BINS / RH_THREADS], long long* s_wsum, long long base,
+                        long long budget, int* s_dig, long long* s_base, long long* s_total)
+{
+    constexpr int PER = RT_BINS / RH_THREADS;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    long long sum = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) sum += v[j];
+    long long inc = sum;   // inclusive scan over the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const long long t = __shfl_up(inc, o);
+        if (lane >= o) inc += t;
+    }
+    if (lane == 63) s_wsum[wave] = inc;
+    __syncthreads();
+    long long acc = base + inc - sum;
+    for (int k = 0; k < wave; ++k) acc += s_wsum[k];
+    if (tid == RH_THREADS - 1) *s_total = acc + sum;
+    if (acc <= budget && acc + sum > budget) {   // exactly one thread
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            if (acc + v[j] > budget) {
+                *s_dig = RT_BINS - 1 - PER * tid - j;
+                *s_base = acc;
+                break;
+            }
+            acc += v[j];
+        }
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(RH_THREADS) void k_route_head(
+    const float* __restrict__ log_ratio, const int32_t* __restrict__ counts_q,
+    const int32_t* __restrict__ counts_k, RouteGeom gm, int S, long long budget,
+    const unsigned long long* __restrict__ part, const uint32_t* __restrict__ words,
+    uint8_t* __restrict__ mask, long long* __restrict__ sel_cost)
+{
+    constexpr int PER = RT_BINS / RH_THREADS;
+    extern __shared__ int s_cnt[];   // counts_q of the head, then counts_k
+    __shared__ unsigned long long s_hist[RT_BINS];
+    __shared__ unsigned long long s_cand[RH_CAND];
+    __shared__ long long s_wsum[RH_THREADS / 64];
+    __shared__ long long s_base, s_total;
+    __shared__ int s_dig, s_ncand;
+    const int h = blockIdx.x, tid = threadIdx.x;
+    const int Cq = gm.nb / gm.Ck;
+    int* s_cq = s_cnt;
+    int* s_ck = s_cnt + Cq;
+    for (int i = tid; i < Cq; i += RH_THREADS) s_cq[i] = counts_q[(size_t)h * Cq + i];
+    for (int i = tid; i < gm.Ck; i += RH_THREADS) s_ck[i] = counts_k[(size_t)h * gm.Ck + i];
+    if (tid == 0) {
+        s_ncand = 0;
+        s_dig = -1;
+    }
+    const float* lr = log_ratio + (size_t)h * gm.nb;
+    const int nvec = route_word_pitch(gm.nb) / RH_VEC;
+    const u32x4* wv = (const u32x4*)(words + (size_t)h * route_word_pitch(gm.nb));
+    const unsigned ibm = (1u << gm.IB) - 1u;
+    auto cost = [&](int b) {
+        const int c = b / gm.Ck, g = b - c * gm.Ck;
+        return (unsigned long long)((long long)s_cq[c] * (long long)s_ck[g]);
+    };
+    // the blocks of vector iv: bit e set where the word tests true
+    auto select = [&](const u32x4& w4, int iv, auto pred) {
+        unsigned in = 0;
+#pragma unroll
+        for (int e = 0; e < RH_VEC; ++e) in |= (pred(w4[e]) ? 1u : 0u) << e;
+        const int bb = iv * RH_VEC;
+        if (bb + RH_VEC > gm.nb) in &= (1u << (gm.nb - bb)) - 1u;   // words past the blocks
+        return in;
+    };
+
+    // First pass: the sum of the slices' histograms of the top digit.  This
+    // thread's four digits are adjacent (32 bytes per slice); the slices were
+    // written by other workgroups, so their loads go past this L2 and are all
+    // issued before the first is used.
+    long long v[PER] = {0, 0, 0, 0};
+    {
+        static_assert(PER == 4, "four digits per thread");
+        const u64x2* ph = (const u64x2*)(part + (size_t)h * S * RT_BINS + (RT_BINS - PER * (tid + 1)));
+        for (int k0 = 0; k0 < S; k0 += RH_SLICE_LOAD) {
+            u64x2 x[RH_SLICE_LOAD][2];
+#pragma unroll
+            for (int q = 0; q < RH_SLICE_LOAD; ++q) {
+                if (k0 + q < S) {
+                    x[q][0] = ph[(size_t)(k0 + q) * (RT_BINS / 2)];
+                    x[q][1] = ph[(size_t)(k0 + q) * (RT_BINS / 2) + 1];
+                } else {
+                    x[q][0] = x[q][1] = u64x2{0, 0};
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < RH_SLICE_LOAD; ++q) {   // ascending addresses: digits top - 3 .. top
+                v[3] += (long long)x[q][0][0];
+                v[2] += (long long)x[q][0][1];
+                v[1] += (long long)x[q][1][0];
+                v[0] += (long long)x[q][1][1];
+            }
+        }
+    }
+    __syncthreads();
+    rh_scan(v, s_wsum, 0, budget, &s_dig, &s_base, &s_total);
+    const bool crosses = s_dig >= 0;
+    unsigned long long prefix = crosses ? (unsigned)s_dig : 0u;
+    long long base = s_base;
+    long long used = s_total;
+    unsigned w2 = 0;   // the 24-bit prefix once the second pass has chosen it
+    for (int pass = 1; crosses && pass < gm.npass; ++pass) {
+        const int sh = gm.shift(pass);
+        __syncthreads();   // everyone has read s_dig, s_base and s_total
+        for (int i = tid; i < RT_BINS; i += RH_THREADS) s_hist[i] = 0ull;
+        if (tid == 0) s_dig = -1;
+        __syncthreads();
+        const int nc = s_ncand;
+        if (pass == 1) {
+            // second digit straight from the words; block 4 iv + e is query
+            // cluster c, key cluster g + e (wrapped), (c, g) stepped per vector
+            const unsigned d0 = (unsigned)prefix;
+            RhStep cg;
+            cg.start(tid * RH_VEC, RH_THREADS * RH_VEC, gm.Ck);
+            for (int iv = tid; iv < nvec; iv += RH_THREADS, cg.next()) {
+                const u32x4 w4 = wv[iv];
+                const unsigned in = select(w4, iv, [&](unsigned w) { return (w >> RT_DIGIT) == d0; });
+                if (!in) continue;
+#pragma unroll
+                for (int e = 0; e < RH_VEC; ++e) {
+                    int c = cg.c, g = cg.g + e;
+                    while (g >= gm.Ck) {   // once at most unless C_k < 4
+                        g -= gm.Ck;
+                        ++c;
+                    }
+                    if ((in >> e) & 1u)
+                        atomicAdd(&s_hist[w4[e] & (RT_BINS - 1)],
+                                  (unsigned long long)((long long)s_cq[c] * (long long)s_ck[g]));
+                }
+            }
+        } else if (pass == 2 || nc > RH_CAND) {
+            // the blocks of the 24-bit prefix: their keys (listed by the third
+            // pass; a later pass tests the rest of the prefix on the key)
+            for (int iv = tid; iv < nvec; iv += RH_THREADS) {
+                const u32x4 w4 = wv[iv];
+                unsigned in = select(w4, iv, [&](unsigned w) { return w == w2; });
+                if (!in) continue;
+                float r[RH_VEC];
+#pragma unroll
+                for (int e = 0; e < RH_VEC; ++e) r[e] = ((in >> e) & 1u) ? lr[iv * RH_VEC + e] : 0.f;
+                int pos = 0;
+                if (pass == 2) pos = atomicAdd(&s_ncand, __popc(in));
+#pragma unroll
+                for (int e = 0; e < RH_VEC; ++e) {
+                    if (!((in >> e) & 1u)) continue;
+                    const int b = iv * RH_VEC + e;
+                    const unsigned long long K = gm.key(r[e], b);
+                    if (pass == 2) {
+                        if (pos < RH_CAND) s_cand[pos] = K;
+                        ++pos;
+                    } else if ((K >> (sh + RT_DIGIT)) != prefix) {
+                        continue;
+                    }
+                    atomicAdd(&s_hist[(K >> sh) & (RT_BINS - 1)], cost(b));
+                }
+            }
+        } else {
+            for (int i = tid; i < nc; i += RH_THREADS) {
+                const unsigned long long K = s_cand[i];
+                if ((K >> (sh + RT_DIGIT)) != prefix) continue;
+                atomicAdd(&s_hist[(K >> sh) & (RT_BINS - 1)], cost((int)(ibm - (unsigned)(K & ibm))));
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < PER; ++j) v[j] = (long long)s_hist[RT_BINS - 1 - PER * tid - j];
+        rh_scan(v, s_wsum, base, budget, &s_dig, &s_base, &s_total);
+        prefix = (prefix << RT_DIGIT) | (unsigned long long)s_dig;   // a later digit always crosses
+        base = s_base;
+        if (pass == 1) w2 = (unsigned)prefix;
+    }
+    if (crosses) used = base;   // the cost of every block whose key exceeds the crossing key
+    // Mask: every block whose key exceeds the crossing key (all when none
+    // crosses).  The words above the crossing key's 24-bit prefix are taken, those
+    // below are not; the blocks of the prefix itself take their key from the list.
+    const int nc = s_ncand;
+    const bool listed = nc <= RH_CAND;
+    uint8_t* mk = mask + (size_t)h * gm.nb;
+    // whole vectors whose four words all differ from the prefix write four mask
+    // bytes at once where the row is 4-byte aligned
+    const bool aligned = (((uintptr_t)mk) & 3u) == 0;
+    for (int iv = tid; iv < nvec; iv += RH_THREADS) {
+        const u32x4 w4 = wv[iv];
+        const int bb = iv * RH_VEC;
+        if (aligned && bb + RH_VEC <= gm.nb &&
+            (!crosses || (w4[0] != w2 && w4[1] != w2 && w4[2] != w2 && w4[3] != w2))) {
+            unsigned m4 = 0;
+#pragma unroll
+            for (int e = 0; e < RH_VEC; ++e) m4 |= ((!crosses || w4[e] > w2) ? 1u : 0u) << (8 * e);
+            *(uint32_t*)(mk + bb) = m4;
+            continue;
+        }
+#pragma unroll
+        for (int e = 0; e < RH_VEC; ++e) {
+            const int b = bb + e;
+            if (b >= gm.nb) break;
+            const unsigned w = w4[e];
+            if (!crosses || w != w2) {
+                mk[b] = (!crosses || w > w2) ? 1 : 0;
+            } else if (!listed) {
+                mk[b] = gm.key(lr[b], b) > prefix ? 1 : 0;
+            }
+        }
+    }
+    if (crosses && listed) {
+        for (int i = tid; i < nc; i += RH_THREADS) {
+            const unsigned long long K = s_cand[i];
+            mk[ibm - (unsigned)(K & ibm)] = K > prefix ? 1 : 0;
+        }
+    }
+    if (tid == 0) sel_cost[h] = used;
+}
+
 SVG_HIDDEN int route_slices(int H)
 {
     int s = 480 / (H > 0 ? H : 1);
@@ -210,13 +545,24 @@ SVG_HIDDEN hipError_t launch_route(const RouteArgs& a, hipStream_t st)
     int IB = 1;
     while ((1 << IB) < nb) ++IB;
     RouteGeom gm{nb, IB, (32 + IB + RT_DIGIT - 1) / RT_DIGIT, a.Ck};
-    const int S = route_slices(a.H);
     const Layout& L = *a.L;
+    if (nb <= RH_MAX_BLOCKS) {
+        const int S = route_top_slices(nb);
+        unsigned long long* top = (unsigned long long*)(a.scratch + L.rt_top);
+        uint32_t* words = (uint32_t*)(a.scratch + L.rt_top + align256((size_t)a.H * S * RT_BINS * 8));
+        const size_t lds = (size_t)(a.Cq + a.Ck) * 4;
+        hipLaunchKernelGGL(k_route_top, dim3(S, a.H), dim3(RT_THREADS), lds, st, a.log_ratio, a.counts_q,
+                           a.counts_k, gm, top, words);
+        hipLaunchKernelGGL(k_route_head, dim3(a.H), dim3(RH_THREADS), lds, st, a.log_ratio, a.counts_q,
+                           a.counts_k, gm, S, (long long)a.budget, top, words, a.mask, (long long*)a.sel_cost);
+        return hipGetLastError();
+    }
+    const int S = route_slices(a.H);
     unsigned long long* ghist = (unsigned long long*)(a.scratch + L.rt_hist);
     RouteState* state = (RouteState*)(a.scratch + L.rt_state);
     long long* part = (long long*)(a.scratch + L.rt_part);
-    // the histograms and states are contiguous: one fill clears both
-    zero_words(ghist, L.rt_end - L.rt_hist, st);
+    // the states and histograms are contiguous: one fill clears both
+    zero_words(a.scratch + L.rt_state, L.rt_top - L.rt_state, st);
     const dim3 grid(S, a.H);
     for (int p = 0; p < gm.npass; ++p)
         hipLaunchKernelGGL(k_route_pass, grid, dim3(RT_THREADS), 0, st, a.log_ratio, a.counts_q,

@@ -266,6 +266,44 @@ def test_route_mask_bit_exact_given_ratios(case):
     del Nq, Nk
 
 
+@pytest.mark.parametrize("Cq,Ck,N", [(100, 500, 75600), (200, 1000, 118800), (128, 4096, 65536)])
+def test_route_mask_bit_exact_at_full_block_counts(Cq, Ck, N):
+    """The head-wide route at the block counts of the Wan and HunyuanVideo
+    shapes (one workgroup per head: 50,000 and 200,000 blocks) and beyond 2^18
+    blocks (524,288: one launch per radix pass): mask and selected cost
+    bit-exact against the oracle.  Tied ratios put more blocks under one top
+    digit than the workgroup keeps in LDS, so its later passes read the ratios
+    again; continuous ratios keep the blocks in play in LDS."""
+    torch = torch_gpu()
+    log("route Cq=%d Ck=%d" % (Cq, Ck))
+    rng = np.random.default_rng(Cq + Ck)
+    H = 2
+    cq = rng.integers(0, 2 * N // Cq + 1, (H, Cq)).astype(np.int32)
+    ck = rng.integers(0, 2 * N // Ck + 1, (H, Ck)).astype(np.int32)
+    cq[:, 0] = 0
+    ck[:, 1] = 0
+    variants = {
+        "continuous": rng.standard_normal((H, Cq, Ck)).astype(np.float32) * 5,
+        "ties": rng.integers(-3, 3, (H, Cq, Ck)).astype(np.float32),
+        "with_-inf": np.where(rng.random((H, Cq, Ck)) < 0.2, -np.inf,
+                              rng.standard_normal((H, Cq, Ck))).astype(np.float32),
+    }
+    shape = sv.make_shape(H, N, N, 128, Cq, Ck, 10, sv.BF16)
+    ws = sv.alloc_workspace(shape)
+    mask = torch.empty(H, Cq, Ck, dtype=torch.uint8, device="cuda")
+    sel = torch.empty(H, dtype=torch.int64, device="cuda")
+    for name, lr in variants.items():
+        for rho in (0.0, 0.1, 0.15, 0.5, 1.0):
+            sv.route(shape, rho, _dev(lr, torch.float32), _dev(cq, torch.int32), _dev(ck, torch.int32),
+                     mask, sel, ws)
+            torch.cuda.synchronize()
+            m, st = mask.cpu().numpy(), sel.cpu().numpy()
+            for h in range(H):
+                ref, used = oracle.route(lr[h].astype(np.float64), cq[h], ck[h], rho, N, N)
+                np.testing.assert_array_equal(m[h], ref, err_msg="%s rho=%s head %d" % (name, rho, h))
+                assert st[h] == used, (name, rho, h)
+
+
 @pytest.mark.parametrize("Cq,Ck,N", [(8, 16, 256), (13, 37, 1380), (64, 256, 8192), (3, 4096, 8192)])
 def test_route_rows_bit_exact_given_ratios(Cq, Ck, N):
     """Per-query-cluster budgets: mask and total cost bit-exact against the
