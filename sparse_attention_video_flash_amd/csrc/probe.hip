@@ -80,18 +80,22 @@ __global__ __launch_bounds__(256) void k_key_scalars(const T* __restrict__ Vp,
 }
 
 // sbar[c, g] = tau qbar_c . kbar_g, accumulated in fp64 in dimension order and
-// rounded once to fp32.  A workgroup takes 4 query clusters x 64 key clusters:
-// the 64 kbar rows are staged in LDS (row pitch D + 1 floats, so the 64 lanes
-// of a wave, one row each, read one dimension from distinct banks) and the 4
-// qbar rows as fp64 (one row per wave, broadcast).
+// rounded once to fp32.  A workgroup takes SB_C query clusters x 64 key
+// clusters: the 64 kbar rows are staged in LDS (row pitch D + 1 floats, so the
+// 64 lanes of a wave, one row each, read one dimension from distinct banks) and
+// the SB_C qbar rows as fp64 (broadcast reads); wave w owns query clusters
+// w, w + 4, ..., so each kbar value read from LDS feeds SB_C / 4 products.
+constexpr int SB_C = 32;
+
 template <int D>
 __global__ __launch_bounds__(256) void k_sbar(const float* __restrict__ qbar,
                                               const float* __restrict__ kbar, int Cq, int Ck,
                                               double tau, float* __restrict__ sbar)
 {
+    constexpr int NR = SB_C / 4;   // query clusters per wave
     __shared__ float s_k[64][D + 1];
-    __shared__ double s_q[4][D];
-    const int c0 = blockIdx.x * 4, g0 = blockIdx.y * 64, h = blockIdx.z, tid = threadIdx.x;
+    __shared__ double s_q[SB_C][D];
+    const int c0 = blockIdx.x * SB_C, g0 = blockIdx.y * 64, h = blockIdx.z, tid = threadIdx.x;
     // 64 rows x D floats as float4, all loads of a thread issued together
     constexpr int V4 = 64 * D / 4 / 256;
     float4 kv[V4];
@@ -99,6 +103,21 @@ __global__ __launch_bounds__(256) void k_sbar(const float* __restrict__ qbar,
     for (int u = 0; u < V4; ++u) {
         const int i = tid + 256 * u, r = i / (D / 4), t4 = i - r * (D / 4), g = g0 + r;
         kv[u] = g < Ck ? *(const float4*)(kbar + ((size_t)h * Ck + g) * D + 4 * t4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    constexpr int Q4 = SB_C * D / 4 / 256;   // the qbar rows likewise
+    float4 qv[Q4];
+#pragma unroll
+    for (int u = 0; u < Q4; ++u) {
+        const int i = tid + 256 * u, r = i / (D / 4), t4 = i - r * (D / 4), c = c0 + r;
+        qv[u] = c < Cq ? *(const float4*)(qbar + ((size_t)h * Cq + c) * D + 4 * t4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < Q4; ++u) {
+        const int i = tid + 256 * u, r = i / (D / 4), t4 = i - r * (D / 4);
+        s_q[r][4 * t4] = (double)qv[u].x;
+        s_q[r][4 * t4 + 1] = (double)qv[u].y;
+        s_q[r][4 * t4 + 2] = (double)qv[u].z;
+        s_q[r][4 * t4 + 3] = (double)qv[u].w;
     }
 #pragma unroll
     for (int u = 0; u < V4; ++u) {
@@ -108,17 +127,23 @@ __global__ __launch_bounds__(256) void k_sbar(const float* __restrict__ qbar,
         s_k[r][4 * t4 + 2] = kv[u].z;
         s_k[r][4 * t4 + 3] = kv[u].w;
     }
-    for (int i = tid; i < 4 * D; i += 256) {
-        const int r = i / D, t = i - r * D, c = c0 + r;
-        s_q[r][t] = c < Cq ? (double)qbar[((size_t)h * Cq + c) * D + t] : 0.0;
-    }
     __syncthreads();
-    const int r = tid >> 6, gl = tid & 63, c = c0 + r, g = g0 + gl;
-    if (c >= Cq || g >= Ck) return;
-    double s = 0.0;
-#pragma unroll 8
-    for (int t = 0; t < D; ++t) s = fma(s_q[r][t], (double)s_k[gl][t], s);
-    sbar[((size_t)h * Cq + c) * Ck + g] = (float)(tau * s);
+    const int w = tid >> 6, gl = tid & 63, g = g0 + gl;
+    if (g >= Ck) return;
+    double s[NR];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) s[k] = 0.0;
+#pragma unroll 4
+    for (int t = 0; t < D; ++t) {
+        const double kt = (double)s_k[gl][t];
+#pragma unroll
+        for (int k = 0; k < NR; ++k) s[k] = fma(s_q[w + 4 * k][t], kt, s[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+        const int c = c0 + w + 4 * k;
+        if (c < Cq) sbar[((size_t)h * Cq + c) * Ck + g] = (float)(tau * s[k]);
+    }
 }
 
 // Attention-score comparator: row c of ln r is sbar[c, g] minus the row's
@@ -241,13 +266,13 @@ static hipError_t run_probe(const ProbeArgs& a, hipStream_t st)
     float* pg = (float*)(a.scratch + L.pr_pg);
     const float tau = 1.0f / sqrtf((float)D);
     if (a.flags & SVGEAR_PROBE_SCORE) {
-        hipLaunchKernelGGL((k_sbar<D>), dim3((a.Cq + 3) / 4, (a.Ck + 63) / 64, a.H), dim3(256), 0, st, a.qbar,
+        hipLaunchKernelGGL((k_sbar<D>), dim3((a.Cq + SB_C - 1) / SB_C, (a.Ck + 63) / 64, a.H), dim3(256), 0, st, a.qbar,
                            a.kbar, a.Cq, a.Ck, 1.0 / sqrt((double)D), sbar);
         hipLaunchKernelGGL(k_score_ratio, dim3(a.Cq, a.H), dim3(256), 0, st, sbar, a.counts_q,
                            a.counts_k, a.Cq, a.Ck, a.log_ratio);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((k_sbar<D>), dim3((a.Cq + 3) / 4, (a.Ck + 63) / 64, a.H), dim3(256), 0, st, a.qbar,
+    hipLaunchKernelGGL((k_sbar<D>), dim3((a.Cq + SB_C - 1) / SB_C, (a.Ck + 63) / 64, a.H), dim3(256), 0, st, a.qbar,
                        a.kbar, a.Cq, a.Ck, 1.0 / sqrt((double)D), sbar);
     // the MFMA probe forms its per-key value terms itself (one read of K_p and V_p)
     if (probe_mfma_supported(a)) return launch_probe_mfma(a, sbar, st);
