@@ -266,14 +266,16 @@ def test_route_mask_bit_exact_given_ratios(case):
     del Nq, Nk
 
 
-@pytest.mark.parametrize("Cq,Ck,N", [(100, 500, 75600), (200, 1000, 118800), (128, 4096, 65536)])
+@pytest.mark.parametrize("Cq,Ck,N", [(100, 500, 75600), (200, 1000, 118800), (64, 4096, 65536),
+                                     (128, 4096, 65536)])
 def test_route_mask_bit_exact_at_full_block_counts(Cq, Ck, N):
     """The head-wide route at the block counts of the Wan and HunyuanVideo
-    shapes (one workgroup per head: 50,000 and 200,000 blocks) and beyond 2^18
-    blocks (524,288: one launch per radix pass): mask and selected cost
-    bit-exact against the oracle.  Tied ratios put more blocks under one top
-    digit than the workgroup keeps in LDS, so its later passes read the ratios
-    again; continuous ratios keep the blocks in play in LDS."""
+    shapes (50,000 and 200,000 blocks), at 2^18 blocks (five radix passes, a
+    two-bit top digit), all three in two launches, and beyond 2^18 (524,288:
+    one launch per pass): mask and selected cost bit-exact against the oracle.
+    Tied ratios put more blocks on one 24-bit key prefix than the head
+    workgroup keeps in LDS, so its later passes sweep the words and ratios
+    again; continuous ratios keep those blocks in LDS."""
     torch = torch_gpu()
     log("route Cq=%d Ck=%d" % (Cq, Ck))
     rng = np.random.default_rng(Cq + Ck)
