@@ -306,6 +306,38 @@ def test_route_mask_bit_exact_at_full_block_counts(Cq, Ck, N):
                 assert st[h] == used, (name, rho, h)
 
 
+@pytest.mark.parametrize("Cq,Ck", [(1, 1), (1, 7), (5, 1), (3, 5), (1, 4096), (4096, 1)])
+def test_route_degenerate_block_grids(Cq, Ck):
+    """Single blocks, single rows and columns and odd block counts (words past
+    the last block in the last 16-byte vector, one key cluster per row so that
+    the per-vector cluster stepping wraps several times): mask and selected
+    cost bit-exact against the oracle, from rho = 0 to 1."""
+    torch = torch_gpu()
+    log("route grid %d x %d" % (Cq, Ck))
+    rng = np.random.default_rng(Cq * 7 + Ck)
+    H, N = 3, 4096
+    cq = rng.integers(0, 2 * N // Cq + 2, (H, Cq)).astype(np.int32)
+    ck = rng.integers(0, 2 * N // Ck + 2, (H, Ck)).astype(np.int32)
+    variants = {
+        "continuous": rng.standard_normal((H, Cq, Ck)).astype(np.float32) * 5,
+        "ties": rng.integers(-1, 1, (H, Cq, Ck)).astype(np.float32),
+    }
+    shape = sv.make_shape(H, N, N, 128, Cq, Ck, 10, sv.BF16)
+    ws = sv.alloc_workspace(shape)
+    mask = torch.empty(H, Cq, Ck, dtype=torch.uint8, device="cuda")
+    sel = torch.empty(H, dtype=torch.int64, device="cuda")
+    for name, lr in variants.items():
+        for rho in (0.0, 0.01, 0.3, 0.7, 1.0):
+            sv.route(shape, rho, _dev(lr, torch.float32), _dev(cq, torch.int32), _dev(ck, torch.int32),
+                     mask, sel, ws)
+            torch.cuda.synchronize()
+            m, st = mask.cpu().numpy(), sel.cpu().numpy()
+            for h in range(H):
+                ref, used = oracle.route(lr[h].astype(np.float64), cq[h], ck[h], rho, N, N)
+                np.testing.assert_array_equal(m[h], ref, err_msg="%s rho=%s head %d" % (name, rho, h))
+                assert st[h] == used, (name, rho, h)
+
+
 @pytest.mark.parametrize("Cq,Ck,N", [(8, 16, 256), (13, 37, 1380), (64, 256, 8192), (3, 4096, 8192)])
 def test_route_rows_bit_exact_given_ratios(Cq, Ck, N):
     """Per-query-cluster budgets: mask and total cost bit-exact against the
