@@ -192,8 +192,9 @@ int svgear_probe_noalloc(const svgear_shape* shape, const float* qbar, const int
  * B = floor((rho * Nq) * Nk) (fp64), the longest prefix of that order whose
  * total cost is <= B is selected.  Writes mask [H, Cq, Ck] (1 = exact block)
  * and sel_cost [H] (int64 total cost of the selection).  rho in [0, 1].
- * ws holds the selection's scratch (per-head digit histograms and states);
- * several workgroups share each head, so calls that overlap on one workspace race.
+ * ws holds the selection's scratch (per-slice digit histograms, the top key
+ * bits of every block, per-head states); calls that overlap on one workspace
+ * race.
  * Errors: _NULL, _SHAPE, _RHO, _ALIGN, _WORKSPACE, _HIP. */
 int svgear_route(const svgear_shape* shape, double rho, const float* log_ratio,
                  const int32_t* counts_q, const int32_t* counts_k, uint8_t* mask,
