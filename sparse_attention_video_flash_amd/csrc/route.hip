@@ -15,12 +15,12 @@
 // higher digits equal the digits chosen so far.  Heads of up to 2^18 blocks
 // take two launches: per-slice top-digit histograms and the top 24 key bits of
 // every block, then one workgroup per head for every later pass and the mask
-// (k_route_top, k_route_head).  Larger
-// heads take one launch per pass, several workgroups per head (a slice
-// of the head's blocks each, LDS histogram, then integer atomics into the
-// head's histogram in device memory); the last workgroup of a head to finish
-// scans that histogram and records the chosen digit and the cost before it for
-// the next pass, and a last launch writes the mask and the selected cost.
+// (k_route_top, k_route_head).  Larger heads take one launch per pass, several
+// workgroups per head (a slice of the head's blocks each, LDS histogram, then
+// integer atomics into the head's histogram in device memory); the last
+// workgroup of a head to finish scans that histogram and records the chosen
+// digit and the cost before it for the next pass, and a last launch writes the
+// mask and the selected cost.
 #include "internal.h"
 
 namespace svg {
