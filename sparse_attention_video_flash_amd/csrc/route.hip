@@ -54,7 +54,15 @@ struct RouteGeom {
     {
         return ((unsigned long long)order_key(lr) << IB) | (unsigned long long)(((1u << IB) - 1u) - (unsigned)b);
     }
+    // digits aligned at the bottom of the key (the first may be narrower)
     __device__ int shift(int pass) const { return RT_DIGIT * (npass - 1 - pass); }
+    // digits aligned at the top of the key, so that the first two are bits of
+    // the ratio's order key whatever IB is (the last may be narrower)
+    __device__ int tshift(int pass) const
+    {
+        const int s = 32 + IB - RT_DIGIT * (pass + 1);
+        return s > 0 ? s : 0;
+    }
 };
 
 // This workgroup's slice of the head's blocks.
@@ -203,8 +211,10 @@ __global__ __launch_bounds__(RT_THREADS) void k_route_mask(
 
 // ----------------------------------------------------------------------------- heads of up to 2^18 blocks
 //
-// Two launches.  Both top digits lie above the index bits, so the top 24 bits
-// of a block's key are the order key of its ratio shifted right (its "word").
+// Two launches.  The digits are aligned at the top of the key (the last pass
+// takes what is left), so the first two are the top 24 bits of the order key of
+// a block's ratio (its "word"), whatever the block count: a first digit of
+// the full 12 bits keeps few blocks in play however many index bits follow.
 // k_route_top: S workgroups per head, each over a slice of the head's blocks:
 // the LDS histogram of the top digit, written whole to its own slot (no
 // device-memory atomics, nothing to clear), and every block's word (a row of P
@@ -280,7 +290,7 @@ __global__ __launch_bounds__(RT_THREADS) void k_route_top(
     __syncthreads();
     const float* lr = log_ratio + (size_t)h * gm.nb;
     uint32_t* wh = words + (size_t)h * route_word_pitch(gm.nb);
-    const int wsh = gm.shift(1) - gm.IB;
+    constexpr int wsh = 32 - 2 * RT_DIGIT;   // the word: the top 24 bits of the order key
     int b0, b1;
     route_slice(gm.nb, b0, b1);
     RhStep cg;
@@ -422,7 +432,8 @@ __global__ __launch_bounds__(RH_THREADS) void k_route_head(
     long long used = s_total;
     unsigned w2 = 0;   // the 24-bit prefix once the second pass has chosen it
     for (int pass = 1; crosses && pass < gm.npass; ++pass) {
-        const int sh = gm.shift(pass);
+        const int sh = gm.tshift(pass), hs = gm.tshift(pass - 1);   // this digit: key bits sh .. hs - 1
+        const unsigned long long dm = (1ull << (hs - sh)) - 1ull;
         __syncthreads();   // everyone has read s_dig, s_base and s_total
         for (int i = tid; i < RT_BINS; i += RH_THREADS) s_hist[i] = 0ull;
         if (tid == 0) s_dig = -1;
@@ -470,24 +481,24 @@ __global__ __launch_bounds__(RH_THREADS) void k_route_head(
                     if (pass == 2) {
                         if (pos < RH_CAND) s_cand[pos] = K;
                         ++pos;
-                    } else if ((K >> (sh + RT_DIGIT)) != prefix) {
+                    } else if ((K >> hs) != prefix) {
                         continue;
                     }
-                    atomicAdd(&s_hist[(K >> sh) & (RT_BINS - 1)], cost(b));
+                    atomicAdd(&s_hist[(K >> sh) & dm], cost(b));
                 }
             }
         } else {
             for (int i = tid; i < nc; i += RH_THREADS) {
                 const unsigned long long K = s_cand[i];
-                if ((K >> (sh + RT_DIGIT)) != prefix) continue;
-                atomicAdd(&s_hist[(K >> sh) & (RT_BINS - 1)], cost((int)(ibm - (unsigned)(K & ibm))));
+                if ((K >> hs) != prefix) continue;
+                atomicAdd(&s_hist[(K >> sh) & dm], cost((int)(ibm - (unsigned)(K & ibm))));
             }
         }
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < PER; ++j) v[j] = (long long)s_hist[RT_BINS - 1 - PER * tid - j];
         rh_scan(v, s_wsum, base, budget, &s_dig, &s_base, &s_total);
-        prefix = (prefix << RT_DIGIT) | (unsigned long long)s_dig;   // a later digit always crosses
+        prefix = (prefix << (hs - sh)) | (unsigned long long)s_dig;   // a later digit always crosses
         base = s_base;
         if (pass == 1) w2 = (unsigned)prefix;
     }
